@@ -1,0 +1,288 @@
+"""Pins of the oracle's decoder, attention readers and LSE merge.
+
+Definitions: NanoKV pages, Figure 4(a) (full- or mixed-dimensional reads of
+coefficients plus shared centers), Figure 4(b) (decoder reconstructs the
+coefficients and adds the centers back) and Figure 4(d) (fixed routing,
+query reduction, output restoration, LSE merging).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_history_attention_amd import synth
+
+
+def _sdpa(q, k, v, H, d, tau):
+    """Library routine: torch's scaled_dot_product_attention in float64 on
+    the CPU, plus torch.logsumexp for the LSE."""
+    nq = q.shape[0]
+    qt = torch.from_numpy(q).view(nq, H, d).transpose(0, 1)
+    kt = torch.from_numpy(k).view(-1, H, d).transpose(0, 1)
+    vt = torch.from_numpy(v).view(-1, H, d).transpose(0, 1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=tau)
+    lse = torch.logsumexp(tau * qt @ kt.transpose(1, 2), dim=-1)
+    return o.transpose(0, 1).reshape(nq, H * d).numpy(), lse.transpose(0, 1).numpy()
+
+
+def _brute_attention(q, k, v, H, d, tau):
+    nq = q.shape[0]
+    o = np.zeros((nq, H * d))
+    lse = np.zeros((nq, H))
+    for i in range(nq):
+        for h in range(H):
+            s = [tau * sum(q[i, h * d + j] * k[t, h * d + j] for j in range(d))
+                 for t in range(k.shape[0])]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            tot = sum(e)
+            for j in range(d):
+                o[i, h * d + j] = sum(e[t] * v[t, h * d + j] for t in range(k.shape[0])) / tot
+            lse[i, h] = m + math.log(tot)
+    return o, lse
+
+
+def _tiny(seed=0, H=2, d=4, nq=3, nk=5):
+    rng = np.random.default_rng(seed)
+    W = H * d
+    return (rng.standard_normal((nq, W)), rng.standard_normal((nk, W)),
+            rng.standard_normal((nk, W)), H, d)
+
+
+def test_exact_attention_brute_force():
+    q, k, v, H, d = _tiny()
+    o, l = oracle.exact_attention(q, k, v, H, d, 0.7)
+    ob, lb = _brute_attention(q, k, v, H, d, 0.7)
+    np.testing.assert_allclose(o, ob, atol=1e-13)
+    np.testing.assert_allclose(l, lb, atol=1e-13)
+
+
+def test_exact_attention_matches_sdpa():
+    rng = np.random.default_rng(1)
+    H, d = 3, 16
+    q, k, v = (rng.standard_normal((n, H * d)) for n in (20, 70, 70))
+    o, l = oracle.exact_attention(q, k, v, H, d, 0.25)
+    os_, ls = _sdpa(q, k, v, H, d, 0.25)
+    np.testing.assert_allclose(o, os_, atol=1e-12)
+    np.testing.assert_allclose(l, ls, atol=1e-12)
+
+
+def test_exact_attention_empty_keys():
+    q = np.ones((2, 8))
+    o, l = oracle.exact_attention(q, np.zeros((0, 8)), np.zeros((0, 8)), 2, 4, 0.5)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+def test_shift_invariance():
+    """Adding the same vector c to every key shifts all scores of a (query,
+    head) by tau q.c: O is unchanged and LSE moves by exactly that amount."""
+    q, k, v, H, d = _tiny(3, nk=9)
+    c = np.random.default_rng(4).standard_normal(H * d)
+    o1, l1 = oracle.exact_attention(q, k, v, H, d, 0.3)
+    o2, l2 = oracle.exact_attention(q, k + c, v, H, d, 0.3)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    shift = np.stack([0.3 * q[:, h * d:(h + 1) * d] @ c[h * d:(h + 1) * d] for h in range(H)], 1)
+    np.testing.assert_allclose(l2 - l1, shift, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# LSE merge
+# --------------------------------------------------------------------------
+
+def test_merge_equals_concatenation():
+    q, k, v, H, d = _tiny(5, nk=11)
+    whole = oracle.exact_attention(q, k, v, H, d, 0.4)
+    a = oracle.exact_attention(q, k[:4], v[:4], H, d, 0.4)
+    b = oracle.exact_attention(q, k[4:], v[4:], H, d, 0.4)
+    o, l = oracle.lse_merge([a, b], H, d)
+    np.testing.assert_allclose(o, whole[0], atol=1e-13)
+    np.testing.assert_allclose(l, whole[1], atol=1e-13)
+
+
+def test_merge_identities():
+    q, k, v, H, d = _tiny(6, nk=7)
+    a = oracle.exact_attention(q, k, v, H, d, 0.4)
+    empty = oracle.exact_attention(q, k[:0], v[:0], H, d, 0.4)
+    o, l = oracle.lse_merge([a, empty], H, d)
+    np.testing.assert_allclose(o, a[0], atol=1e-15)
+    np.testing.assert_allclose(l, a[1], atol=1e-15)
+    o, l = oracle.lse_merge([a, a], H, d)
+    np.testing.assert_allclose(o, a[0], atol=1e-14)
+    np.testing.assert_allclose(l, a[1] + math.log(2.0), atol=1e-14)
+    o, l = oracle.lse_merge([empty, empty], H, d)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+# --------------------------------------------------------------------------
+# decoder + full-dimensional read
+# --------------------------------------------------------------------------
+
+def _codec_exact(rng, N, W, r, A, group, D):
+    """Compressed records whose dequantised coefficients are exact multiples
+    of 1/8 (scale 0.125 is an fp16 number), so decoding is exact."""
+    codes = rng.integers(-7, 8, size=(N, r)).astype(np.int8)
+    scales = np.full((N, r // group), np.float16(0.125)).view(np.uint16)
+    idx = rng.integers(0, A, N).astype(np.int32)
+    return idx, oracle.pack_int4(codes), scales, codes.astype(np.float64) / 8.0
+
+
+@pytest.mark.parametrize("identity", [True, False])
+def test_full_read_reduces_to_attention_over_raw_tokens(identity):
+    """r = W with D orthonormal (identity or not) and exact coefficients: the
+    full-dimensional read equals SDPA over x = mu_a + D c built here by hand."""
+    rng = np.random.default_rng(7)
+    H, d = 2, 8
+    W = H * d
+    r, A, N, nq, ncur = W, 3, 40, 6, 5
+    D = np.eye(W) if identity else np.linalg.qr(rng.standard_normal((W, W)))[0]
+    mus = [rng.standard_normal((A, W)).astype(np.float32) for _ in range(2)]
+    recs = []
+    xs = []
+    for b in range(2):
+        Dq = D.astype(np.float32)
+        idx, codes, sc, ch = _codec_exact(rng, N, W, r, A, 8, Dq)
+        recs.append(oracle.Branch(idx, codes, sc, mus[b], Dq, "f32", 8))
+        xs.append(mus[b].astype(np.float64)[idx] + ch @ Dq.astype(np.float64).T)
+    q = rng.standard_normal((nq, W))
+    ck, cv = rng.standard_normal((ncur, W)), rng.standard_normal((ncur, W))
+    o, l = oracle.attend_full(q, recs[0], recs[1], ck, cv, H, d, 0.3)
+    k = np.concatenate([xs[0], ck])
+    v = np.concatenate([xs[1], cv])
+    os_, ls = _sdpa(q, k, v, H, d, 0.3)
+    np.testing.assert_allclose(o, os_, atol=1e-12)
+    np.testing.assert_allclose(l, ls, atol=1e-12)
+
+
+def test_decode_drops_no_term():
+    """decode = center + D c, each term checked on its own."""
+    rng = np.random.default_rng(8)
+    W, r, A, N = 12, 4, 3, 6
+    D = rng.standard_normal((W, r))
+    mu = rng.standard_normal((A, W))
+    idx, codes, sc, ch = _codec_exact(rng, N, W, r, A, 4, D)
+    xh = oracle.decode(idx, codes, sc, mu, D, 4)
+    np.testing.assert_allclose(xh - mu[idx], ch @ D.T, atol=1e-13)
+    zero = oracle.pack_int4(np.zeros((N, r), np.int8))
+    np.testing.assert_allclose(oracle.decode(idx, zero, sc, mu, D, 4), mu[idx], atol=0)
+
+
+# --------------------------------------------------------------------------
+# NanoKV-Fast low-dimensional read
+# --------------------------------------------------------------------------
+
+def _fast_case(seed=9, H=2, d=8, r=8, A=5, N=30, nq=4, ncur=3, group=4):
+    rng = np.random.default_rng(seed)
+    W = H * d
+    DK = np.linalg.qr(rng.standard_normal((W, r)))[0]
+    DV = np.linalg.qr(rng.standard_normal((W, r)))[0]
+    brs = []
+    for D in (DK, DV):
+        codes = rng.integers(-7, 8, size=(N, r)).astype(np.int8)
+        scales = rng.uniform(0.02, 0.3, size=(N, r // group)).astype(np.float16).view(np.uint16)
+        idx = rng.integers(0, A, N).astype(np.int32)
+        mu = rng.standard_normal((A, W))
+        brs.append(oracle.Branch(idx, oracle.pack_int4(codes), scales, mu, D, "f32", group))
+        brs[-1].centers = mu          # keep float64 centers exactly
+        brs[-1].decoder = D
+    q = rng.standard_normal((nq, W))
+    ck, cv = rng.standard_normal((ncur, W)), rng.standard_normal((ncur, W))
+    return q, brs[0], brs[1], ck, cv, H, d
+
+
+def test_fast_with_full_rank_equals_full_read():
+    q, kb, vb, ck, cv, H, d = _fast_case()
+    r = kb.r
+    N = kb.idx.shape[0]
+    segs = [(0, 17, 1), (17, N, 0)]
+    of, lf = oracle.attend_full(q, kb, vb, ck, cv, H, d, 0.35)
+    oq, lq = oracle.attend_fast(q, kb, vb, segs, r, ck, cv, H, d, 0.35)
+    np.testing.assert_allclose(oq, of, atol=1e-12)
+    np.testing.assert_allclose(lq, lf, atol=1e-12)
+    # and a partial r_low really differs
+    o2, _ = oracle.attend_fast(q, kb, vb, segs, 4, ck, cv, H, d, 0.35)
+    assert np.max(np.abs(o2 - of)) > 1e-3
+
+
+def test_low_read_with_zero_rank_is_attention_over_centers():
+    q, kb, vb, _, _, H, d = _fast_case(10)
+    o, l = oracle.low_attention(q, kb, vb, 0, H, d, 0.35)
+    os_, ls = _sdpa(q, kb.centers[kb.idx], vb.centers[vb.idx], H, d, 0.35)
+    np.testing.assert_allclose(o, os_, atol=1e-12)
+    np.testing.assert_allclose(l, ls, atol=1e-12)
+
+
+def _brute_low(q, kb, vb, r_low, H, d, tau):
+    ck, cv = kb.coefficients(), vb.coefficients()
+    nq, N = q.shape[0], ck.shape[0]
+    o = np.zeros((nq, H * d))
+    lse = np.zeros((nq, H))
+    for i in range(nq):
+        for h in range(H):
+            rows = range(h * d, (h + 1) * d)
+            qt = [sum(kb.decoder[w, j] * q[i, w] for w in rows) for j in range(r_low)]
+            s = []
+            for t in range(N):
+                a = kb.idx[t]
+                s.append(tau * (sum(qt[j] * ck[t, j] for j in range(r_low))
+                                + sum(q[i, w] * kb.centers[a, w] for w in rows)))
+            m = max(s)
+            p = [math.exp(x - m) for x in s]
+            tot = sum(p)
+            for jj, w in enumerate(rows):
+                val = 0.0
+                for t in range(N):
+                    coef = sum(vb.decoder[w, j] * cv[t, j] for j in range(r_low))
+                    val += p[t] * (coef + vb.centers[vb.idx[t], w])
+                o[i, w] = val / tot
+            lse[i, h] = m + math.log(tot)
+    return o, lse
+
+
+def test_low_read_brute_force():
+    q, kb, vb, _, _, H, d = _fast_case(11, N=12, nq=2)
+    for r_low in (3, 8):
+        o, l = oracle.low_attention(q, kb, vb, r_low, H, d, 0.35)
+        ob, lb = _brute_low(q, kb, vb, r_low, H, d, 0.35)
+        np.testing.assert_allclose(o, ob, atol=1e-12)
+        np.testing.assert_allclose(l, lb, atol=1e-12)
+
+
+def test_low_read_permutation_invariant():
+    q, kb, vb, _, _, H, d = _fast_case(12)
+    perm = np.random.default_rng(1).permutation(kb.idx.shape[0])
+    o1, l1 = oracle.low_attention(q, kb, vb, 5, H, d, 0.35)
+    o2, l2 = oracle.low_attention(q, kb.rows(perm), vb.rows(perm), 5, H, d, 0.35)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, atol=1e-12)
+
+
+def test_route_indices_validation():
+    f, l = oracle.route_indices([(0, 3, 1), (3, 10, 0)], 10)
+    assert list(l) == [0, 1, 2] and list(f) == list(range(3, 10))
+    with pytest.raises(ValueError):
+        oracle.route_indices([(0, 3, 1), (2, 10, 0)], 10)
+    with pytest.raises(ValueError):
+        oracle.route_indices([(0, 3, 1)], 10)
+
+
+def test_fast_minus_full_gap_on_discriminating_variant():
+    """With centers scaled down the coefficients carry the signal, so the
+    Fast read differs clearly from the full read (used by the D-rule)."""
+    cfg = synth.small_config("C0", center_scale=0.05, mode="fast", r_low=4,
+                             n_full_tail=32)
+    w = synth.workload(cfg)
+    dt = cfg.dtype
+    brs = []
+    for b in range(2):
+        x = w.history_tokens(b)
+        e = oracle.encode(x, w.centers(b), w.encoder(b), cfg.group, dt)
+        brs.append(oracle.Branch(e["idx"], e["codes"], e["scales_bits"], w.centers(b),
+                                 w.decoder(b), dt, cfg.group))
+    q = oracle.as_f64(w.queries(), dt)
+    ck, cv = (oracle.as_f64(w.current(b), dt) for b in range(2))
+    of, _ = oracle.attend_full(q, brs[0], brs[1], ck, cv, cfg.H, cfg.d, cfg.tau)
+    oq, _ = oracle.attend_fast(q, brs[0], brs[1], cfg.segments(), cfg.r_low, ck, cv,
+                               cfg.H, cfg.d, cfg.tau)
+    assert np.max(np.abs(oq - of)) > 0.05 * np.max(np.abs(of))
