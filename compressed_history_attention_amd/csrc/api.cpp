@@ -1,0 +1,321 @@
+// C ABI of libnanokv: validation, workspace layout and dispatch.
+//
+// Every argument is checked on the host before anything is enqueued; the
+// work itself runs in the HIP kernels of this library on the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kernels.hpp"
+#include "tuned.hpp"
+
+namespace nkv {
+
+static thread_local char g_err[512];
+static int g_force_generic = 0;
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+#define NKV_FAIL(code, ...)      \
+  do {                           \
+    ::nkv::set_error(__VA_ARGS__); \
+    return code;                 \
+  } while (0)
+
+static nkv_status check_shape(const nkv_shape* s) {
+  if (!s) NKV_FAIL(NKV_EINVAL, "shape is NULL");
+  if (s->H < 1 || s->d < 1 || s->r < 1 || s->group < 1)
+    NKV_FAIL(NKV_EINVAL, "H, d, r and group must be positive (H=%d d=%d r=%d group=%d)", s->H,
+             s->d, s->r, s->group);
+  if (s->dtype != NKV_F32 && s->dtype != NKV_BF16)
+    NKV_FAIL(NKV_EINVAL, "dtype must be NKV_F32 or NKV_BF16 (got %d)", s->dtype);
+  if (s->d != 16 && s->d != 32 && s->d != 64 && s->d != 128)
+    NKV_FAIL(NKV_EUNSUPPORTED, "head dimension %d not in {16, 32, 64, 128}", s->d);
+  if (s->group != 8 && s->group != 16 && s->group != 32 && s->group != 64)
+    NKV_FAIL(NKV_EUNSUPPORTED, "group %d not in {8, 16, 32, 64}", s->group);
+  if (s->r % 2 || s->r % s->group)
+    NKV_FAIL(NKV_EUNSUPPORTED, "r=%d must be even and a multiple of group=%d", s->r, s->group);
+  if ((int64_t)s->H * s->d > 8192) NKV_FAIL(NKV_EUNSUPPORTED, "H*d above 8192");
+  if (s->r > 4096) NKV_FAIL(NKV_EUNSUPPORTED, "r above 4096");
+  if (!(s->softmax_scale == s->softmax_scale) || isinf(s->softmax_scale))
+    NKV_FAIL(NKV_EINVAL, "softmax_scale is not finite");
+  return NKV_OK;
+}
+
+static float tau_of(const nkv_shape* s) {
+  return s->softmax_scale > 0.f ? s->softmax_scale : 1.0f / sqrtf((float)s->d);
+}
+
+static bool tuned_applies(const nkv_shape* s, int32_t r_low) {
+  if (g_force_generic || !tuned_available()) return false;
+  return s->dtype == NKV_BF16 && s->d == 128 && s->r % 32 == 0 &&
+         (r_low == 0 || (r_low % 16 == 0));
+}
+
+// Build FULL / LOW range tables from a route; adjacent same-mode ranges are
+// joined.  route == NULL means everything FULL.
+static nkv_status build_routes(const nkv_segment* route, int32_t n_seg, int64_t N_hist,
+                               RangeTable* full, RangeTable* low) {
+  memset(full, 0, sizeof(*full));
+  memset(low, 0, sizeof(*low));
+  std::vector<nkv_segment> segs;
+  if (!route || n_seg == 0) {
+    if (n_seg != 0) NKV_FAIL(NKV_EINVAL, "route is NULL but n_seg=%d", n_seg);
+    if (N_hist > 0) segs.push_back({0, N_hist, NKV_FULL});
+  } else {
+    if (n_seg < 0) NKV_FAIL(NKV_EINVAL, "n_seg negative");
+    segs.assign(route, route + n_seg);
+    for (auto& g : segs) {
+      if (g.mode != NKV_FULL && g.mode != NKV_LOW)
+        NKV_FAIL(NKV_EINVAL, "segment mode %d is neither NKV_FULL nor NKV_LOW", g.mode);
+      if (g.begin < 0 || g.end < g.begin || g.end > N_hist)
+        NKV_FAIL(NKV_EINVAL, "segment [%lld, %lld) outside [0, %lld)", (long long)g.begin,
+                 (long long)g.end, (long long)N_hist);
+    }
+    std::sort(segs.begin(), segs.end(),
+              [](const nkv_segment& a, const nkv_segment& b) { return a.begin < b.begin; });
+    int64_t pos = 0;
+    for (auto& g : segs) {
+      if (g.begin != pos)
+        NKV_FAIL(NKV_EINVAL, "segments must be disjoint and cover [0, N_hist) (gap/overlap at %lld)",
+                 (long long)pos);
+      pos = g.end;
+    }
+    if (pos != N_hist) NKV_FAIL(NKV_EINVAL, "segments cover [0, %lld) not [0, %lld)",
+                                (long long)pos, (long long)N_hist);
+  }
+  for (auto& g : segs) {
+    if (g.end == g.begin) continue;
+    RangeTable* t = g.mode == NKV_FULL ? full : low;
+    if (t->n > 0 && t->begin[t->n - 1] + (t->prefix[t->n] - t->prefix[t->n - 1]) == g.begin) {
+      t->prefix[t->n] += g.end - g.begin;  // join with the previous adjacent range
+    } else {
+      if (t->n == NKV_MAX_SEGMENTS)
+        NKV_FAIL(NKV_EUNSUPPORTED, "more than %d ranges of one mode", NKV_MAX_SEGMENTS);
+      t->begin[t->n] = g.begin;
+      t->prefix[t->n + 1] = t->prefix[t->n] + (g.end - g.begin);
+      t->n += 1;
+    }
+    t->total = t->prefix[t->n];
+  }
+  return NKV_OK;
+}
+
+static nkv_status check_branch(const nkv_branch* b, const char* name, int64_t N_hist) {
+  if (!b) NKV_FAIL(NKV_EINVAL, "%s branch is NULL", name);
+  if (b->A < 1) NKV_FAIL(NKV_EINVAL, "%s branch: A=%d must be positive", name, b->A);
+  if (b->A > 4096) NKV_FAIL(NKV_EUNSUPPORTED, "%s branch: A=%d above 4096", name, b->A);
+  if (!b->centers || !b->decoder) NKV_FAIL(NKV_EINVAL, "%s branch: NULL centers/decoder", name);
+  if (N_hist > 0 && (!b->idx || !b->codes || !b->scales))
+    NKV_FAIL(NKV_EINVAL, "%s branch: NULL idx/codes/scales with N_hist>0", name);
+  return NKV_OK;
+}
+
+static BranchArgs to_args(const nkv_branch* b) {
+  return BranchArgs{b->idx, b->codes, b->scales, b->centers, b->decoder, b->A};
+}
+
+// --------------------------------------------------------------------------
+// generic-path workspace
+// --------------------------------------------------------------------------
+struct GenericLayout {
+  size_t k, v, o_full, lse_full, o_low, lse_low, total;
+};
+
+static GenericLayout generic_layout(const nkv_shape* s, int64_t n_full, int64_t n_low, int64_t Nq,
+                                    int64_t N_cur) {
+  GenericLayout L{};
+  const int64_t W = (int64_t)s->H * s->d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const int64_t nk = n_full + N_cur;
+  L.k = take(sizeof(float) * nk * W);
+  L.v = take(sizeof(float) * nk * W);
+  if (n_low > 0) {
+    L.o_full = take(sizeof(float) * Nq * W);
+    L.lse_full = take(sizeof(float) * Nq * s->H);
+    L.o_low = take(sizeof(float) * Nq * W);
+    L.lse_low = take(sizeof(float) * Nq * s->H);
+  }
+  L.total = off;
+  return L;
+}
+
+static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, const nkv_branch* v,
+                                int64_t N_hist, const nkv_segment* route, int32_t n_seg,
+                                int32_t r_low, const void* q, int64_t Nq, const void* cur_k,
+                                const void* cur_v, int64_t N_cur, void* out, float* lse,
+                                void* ws, size_t ws_bytes, void* stream_, bool fast) {
+  nkv_status st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_branch(k, "K", N_hist)) || (st = check_branch(v, "V", N_hist))) return st;
+  if (N_hist < 0 || Nq < 0 || N_cur < 0) NKV_FAIL(NKV_EINVAL, "negative size");
+  if (Nq > (int64_t)1 << 31 || N_hist > (int64_t)1 << 31 || N_cur > (int64_t)1 << 31)
+    NKV_FAIL(NKV_EUNSUPPORTED, "sizes above 2^31");
+  if (Nq > 0 && (!q || !out || !lse)) NKV_FAIL(NKV_EINVAL, "NULL q/out/lse with Nq>0");
+  if (N_cur > 0 && (!cur_k || !cur_v)) NKV_FAIL(NKV_EINVAL, "NULL current chunk with N_cur>0");
+  RangeTable full, low;
+  if (fast) {
+    if (r_low < 1 || r_low > shape->r)
+      NKV_FAIL(NKV_EUNSUPPORTED, "r_low=%d must be in [1, r=%d]", r_low, shape->r);
+    if ((st = build_routes(route, n_seg, N_hist, &full, &low))) return st;
+  } else {
+    if ((st = build_routes(nullptr, 0, N_hist, &full, &low))) return st;
+    r_low = 0;
+  }
+  if (low.total > 0 && r_low > 512 && !tuned_applies(shape, r_low))
+    NKV_FAIL(NKV_EUNSUPPORTED, "generic low-dimensional read supports r_low <= 512");
+  const size_t need = nkv_attend_workspace_size(shape, k->A, v->A, N_hist, fast ? route : nullptr,
+                                                fast ? n_seg : 0, r_low, Nq, N_cur);
+  if (need == SIZE_MAX) return NKV_EINVAL;
+  if (need > 0 && (!ws || ws_bytes < need))
+    NKV_FAIL(NKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (Nq == 0) return NKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream_);
+  const float tau = tau_of(shape);
+  const int dt = shape->dtype, H = shape->H, d = shape->d, r = shape->r, g = shape->group;
+  const BranchArgs kb = to_args(k), vb = to_args(v);
+
+  if (tuned_applies(shape, r_low)) {
+    return tuned_attend(shape, kb, vb, full, low, r_low, tau, q, Nq, cur_k, cur_v, N_cur, out,
+                        lse, static_cast<char*>(ws), ws_bytes, s);
+  }
+
+  const int64_t W = (int64_t)H * d;
+  const GenericLayout L = generic_layout(shape, full.total, low.total, Nq, N_cur);
+  char* base = static_cast<char*>(ws);
+  float* kw = reinterpret_cast<float*>(base + L.k);
+  float* vw = reinterpret_cast<float*>(base + L.v);
+  if ((st = launch_decode_generic(dt, kb, (int)W, r, g, full, kw, s))) return st;
+  if ((st = launch_decode_generic(dt, vb, (int)W, r, g, full, vw, s))) return st;
+  if ((st = launch_rows_to_f32(dt, cur_k, N_cur * W, kw + full.total * W, s))) return st;
+  if ((st = launch_rows_to_f32(dt, cur_v, N_cur * W, vw + full.total * W, s))) return st;
+  const int64_t nk = full.total + N_cur;
+  if (low.total == 0) {
+    return launch_attention_generic(dt, false, q, Nq, H, d, tau, kw, vw, nk, out, lse, s);
+  }
+  float* of = reinterpret_cast<float*>(base + L.o_full);
+  float* lf = reinterpret_cast<float*>(base + L.lse_full);
+  float* ol = reinterpret_cast<float*>(base + L.o_low);
+  float* ll = reinterpret_cast<float*>(base + L.lse_low);
+  if ((st = launch_attention_generic(dt, true, q, Nq, H, d, tau, kw, vw, nk, of, lf, s))) return st;
+  if ((st = launch_low_generic(dt, q, Nq, H, d, r, g, r_low, tau, kb, vb, low, nullptr, nullptr,
+                               Nq * H, ol, ll, s)))
+    return st;
+  return launch_lse_merge(Nq, H, d, of, lf, ol, ll, out, dt, lse, s);
+}
+
+}  // namespace nkv
+
+using namespace nkv;
+
+extern "C" {
+
+int nkv_version(void) { return NKV_VERSION; }
+
+const char* nkv_last_error(void) { return g_err; }
+
+void nkv_force_generic(int on) { g_force_generic = on ? 1 : 0; }
+
+const char* nkv_status_string(nkv_status s) {
+  switch (s) {
+    case NKV_OK: return "ok";
+    case NKV_EINVAL: return "invalid argument";
+    case NKV_EUNSUPPORTED: return "unsupported shape";
+    case NKV_EWORKSPACE: return "workspace too small";
+    case NKV_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t nkv_encode_workspace_size(const nkv_shape* shape, int64_t N, int32_t A) {
+  g_err[0] = 0;
+  if (check_shape(shape) || N < 0 || A < 1) return SIZE_MAX;
+  if (tuned_applies(shape, 0)) return tuned_encode_workspace(shape, N, A);
+  return 0;
+}
+
+nkv_status nkv_encode(const nkv_shape* shape, const void* x, int64_t N, const void* centers,
+                      int32_t A, const void* encoder, int32_t* idx, uint8_t* codes,
+                      uint16_t* scales, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  nkv_status st = check_shape(shape);
+  if (st) return st;
+  if (N < 0) NKV_FAIL(NKV_EINVAL, "N negative");
+  if (N > (int64_t)1 << 31) NKV_FAIL(NKV_EUNSUPPORTED, "N above 2^31");
+  if (A < 1) NKV_FAIL(NKV_EINVAL, "A=%d must be positive", A);
+  if (A > 65536) NKV_FAIL(NKV_EUNSUPPORTED, "A above 65536");
+  if (!centers || !encoder) NKV_FAIL(NKV_EINVAL, "NULL centers/encoder");
+  if (N > 0 && (!x || !idx || !codes || !scales)) NKV_FAIL(NKV_EINVAL, "NULL x/idx/codes/scales with N>0");
+  const size_t need = nkv_encode_workspace_size(shape, N, A);
+  if (need > 0 && (!ws || ws_bytes < need))
+    NKV_FAIL(NKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (N == 0) return NKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int W = shape->H * shape->d;
+  if (tuned_applies(shape, 0))
+    return tuned_encode(shape, x, N, centers, A, encoder, idx, codes, scales,
+                        static_cast<char*>(ws), ws_bytes, s);
+  return launch_encode_generic(shape->dtype, x, N, W, centers, A, encoder, shape->r, shape->group,
+                               idx, codes, scales, s);
+}
+
+size_t nkv_attend_workspace_size(const nkv_shape* shape, int32_t A_k, int32_t A_v, int64_t N_hist,
+                                 const nkv_segment* route, int32_t n_seg, int32_t r_low,
+                                 int64_t Nq, int64_t N_cur) {
+  if (check_shape(shape) || A_k < 1 || A_v < 1 || N_hist < 0 || Nq < 0 || N_cur < 0)
+    return SIZE_MAX;
+  RangeTable full, low;
+  if (build_routes(route, n_seg, N_hist, &full, &low)) return SIZE_MAX;
+  if (low.total == 0) r_low = 0;
+  if (tuned_applies(shape, r_low))
+    return tuned_attend_workspace(shape, A_k, A_v, full, low, r_low, Nq, N_cur);
+  return generic_layout(shape, full.total, low.total, Nq, N_cur).total;
+}
+
+nkv_status nkv_attend_full(const nkv_shape* shape, const nkv_branch* k, const nkv_branch* v,
+                           int64_t N_hist, const void* q, int64_t Nq, const void* cur_k,
+                           const void* cur_v, int64_t N_cur, void* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  return attend_common(shape, k, v, N_hist, nullptr, 0, 0, q, Nq, cur_k, cur_v, N_cur, out, lse,
+                       ws, ws_bytes, stream, false);
+}
+
+nkv_status nkv_attend_fast(const nkv_shape* shape, const nkv_branch* k, const nkv_branch* v,
+                           int64_t N_hist, const nkv_segment* route, int32_t n_seg, int32_t r_low,
+                           const void* q, int64_t Nq, const void* cur_k, const void* cur_v,
+                           int64_t N_cur, void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+  g_err[0] = 0;
+  return attend_common(shape, k, v, N_hist, route, n_seg, r_low, q, Nq, cur_k, cur_v, N_cur, out,
+                       lse, ws, ws_bytes, stream, true);
+}
+
+nkv_status nkv_lse_merge(int64_t Nq, int32_t H, int32_t d, const float* o_a, const float* lse_a,
+                         const float* o_b, const float* lse_b, void* out, int32_t out_dtype,
+                         float* lse_out, void* stream) {
+  g_err[0] = 0;
+  if (Nq < 0 || H < 1 || d < 1) NKV_FAIL(NKV_EINVAL, "bad sizes Nq=%lld H=%d d=%d", (long long)Nq, H, d);
+  if (out_dtype != NKV_F32 && out_dtype != NKV_BF16) NKV_FAIL(NKV_EINVAL, "bad out dtype %d", out_dtype);
+  if (Nq > 0 && (!o_a || !lse_a || !o_b || !lse_b || !out || !lse_out))
+    NKV_FAIL(NKV_EINVAL, "NULL pointer with Nq>0");
+  if ((int64_t)H * d > 16384) NKV_FAIL(NKV_EUNSUPPORTED, "H*d above 16384");
+  return launch_lse_merge(Nq, H, d, o_a, lse_a, o_b, lse_b, out, out_dtype, lse_out,
+                          static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

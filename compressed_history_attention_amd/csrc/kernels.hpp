@@ -1,0 +1,40 @@
+// Internal launcher declarations of libnanokv.
+#pragma once
+
+#include "nkv_common.hpp"
+
+namespace nkv {
+
+// Device view of one compressed branch (mirrors nkv_branch).
+struct BranchArgs {
+  const int32_t* idx;
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const void* centers;
+  const void* decoder;
+  int32_t A;
+};
+
+// generic kernels (generic.hip)
+nkv_status launch_encode_generic(int dt, const void* x, int64_t N, int W, const void* centers,
+                                 int A, const void* enc, int r, int group, int32_t* idx,
+                                 uint8_t* codes, uint16_t* scales, hipStream_t s);
+nkv_status launch_decode_generic(int dt, const BranchArgs& b, int W, int r, int group,
+                                 const RangeTable& rows, float* out, hipStream_t s);
+nkv_status launch_rows_to_f32(int dt, const void* src, int64_t n, float* dst, hipStream_t s);
+nkv_status launch_attention_generic(int dt, bool out_f32, const void* q, int64_t Nq, int H,
+                                    int d, float tau, const float* K, const float* V,
+                                    int64_t Nk, void* out, float* lse, hipStream_t s);
+size_t low_generic_lds_bytes(int A_k, int A_v, int r_low, int d);
+nkv_status launch_low_generic(int dt, const void* q, int64_t Nq, int H, int d, int r, int group,
+                              int r_low, float tau, const BranchArgs& kb, const BranchArgs& vb,
+                              const RangeTable& low, const int32_t* rows,
+                              const int32_t* nrows, int64_t max_rows, float* o_low,
+                              float* lse_low, hipStream_t s);
+
+// LSE merge (merge.hip)
+nkv_status launch_lse_merge(int64_t Nq, int H, int d, const float* o_a, const float* lse_a,
+                            const float* o_b, const float* lse_b, void* out, int out_dt,
+                            float* lse_out, hipStream_t s);
+
+}  // namespace nkv

@@ -1,0 +1,24 @@
+// Tuned (MFMA) path of libnanokv: bf16 tensors, head dimension 128.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace nkv {
+
+size_t tuned_encode_workspace(const nkv_shape* s, int64_t N, int32_t A);
+nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void* centers,
+                        int32_t A, const void* enc, int32_t* idx, uint8_t* codes,
+                        uint16_t* scales, char* ws, size_t ws_bytes, hipStream_t st);
+
+size_t tuned_attend_workspace(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& full,
+                              const RangeTable& low, int32_t r_low, int64_t Nq, int64_t N_cur);
+nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
+                        const RangeTable& full, const RangeTable& low, int32_t r_low, float tau,
+                        const void* q, int64_t Nq, const void* cur_k, const void* cur_v,
+                        int64_t N_cur, void* out, float* lse, char* ws, size_t ws_bytes,
+                        hipStream_t st);
+
+// true once the tuned kernels are compiled in
+bool tuned_available();
+
+}  // namespace nkv

@@ -1,0 +1,281 @@
+"""ctypes binding of libnanokv (argument marshalling only).
+
+The functions named like the C entry points (``nkv_encode``,
+``nkv_attend_full``, ``nkv_attend_fast``, ``nkv_lse_merge`` and the
+workspace-size queries) take torch tensors that already live on the GPU,
+pass their device pointers and the current HIP stream to the library and
+raise ``NkvError`` on a non-zero status.  The helpers ``encode``,
+``attend_full``, ``attend_fast`` and ``lse_merge`` additionally allocate the
+outputs and the workspace with torch.  No computation happens here: every
+step runs in the HIP kernels of ``libnanokv.so``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnanokv.so")
+
+NKV_F32, NKV_BF16 = 0, 1
+NKV_FULL, NKV_LOW = 0, 1
+MAX_SEGMENTS = 64
+SIZE_MAX = ctypes.c_size_t(-1).value
+_DT = {"f32": NKV_F32, "bf16": NKV_BF16}
+_TORCH_DT = {NKV_F32: torch.float32, NKV_BF16: torch.bfloat16}
+
+
+class NkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libnanokv status {status}: {msg}")
+        self.status = status
+
+
+class nkv_shape(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("d", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class nkv_branch(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("centers", ctypes.c_void_p),
+                ("decoder", ctypes.c_void_p), ("A", ctypes.c_int32)]
+
+
+class nkv_segment(ctypes.Structure):
+    _fields_ = [("begin", ctypes.c_int64), ("end", ctypes.c_int64), ("mode", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libnanokv.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "compressed_history_attention_amd/build.py (or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    SH, BR, SG = ctypes.POINTER(nkv_shape), ctypes.POINTER(nkv_branch), ctypes.POINTER(nkv_segment)
+    sig = {
+        "nkv_version": (ctypes.c_int, []),
+        "nkv_last_error": (ctypes.c_char_p, []),
+        "nkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "nkv_force_generic": (None, [ctypes.c_int]),
+        "nkv_encode_workspace_size": (SZ, [SH, I64, I32]),
+        "nkv_encode": (ctypes.c_int, [SH, P, I64, P, I32, P, P, P, P, P, SZ, P]),
+        "nkv_attend_workspace_size": (SZ, [SH, I32, I32, I64, SG, I32, I32, I64, I64]),
+        "nkv_attend_full": (ctypes.c_int, [SH, BR, BR, I64, P, I64, P, P, I64, P, P, P, SZ, P]),
+        "nkv_attend_fast": (ctypes.c_int, [SH, BR, BR, I64, SG, I32, I32, P, I64, P, P, I64, P,
+                                           P, P, SZ, P]),
+        "nkv_lse_merge": (ctypes.c_int, [I64, I32, I32, P, P, P, P, P, I32, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+EXPORTS = ("nkv_version", "nkv_last_error", "nkv_status_string", "nkv_force_generic",
+           "nkv_encode_workspace_size", "nkv_encode", "nkv_attend_workspace_size",
+           "nkv_attend_full", "nkv_attend_fast", "nkv_lse_merge")
+
+
+def _check(status: int):
+    if status != 0:
+        raise NkvError(status, load().nkv_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libnanokv must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ----------------------------------------------------------------------------
+# Python-side descriptions
+# ----------------------------------------------------------------------------
+
+@dataclass
+class Shape:
+    H: int
+    d: int
+    r: int
+    group: int
+    dtype: str = "bf16"
+    softmax_scale: float = 0.0
+
+    def c(self) -> nkv_shape:
+        return nkv_shape(self.H, self.d, self.r, self.group, _DT[self.dtype], self.softmax_scale)
+
+    @property
+    def W(self) -> int:
+        return self.H * self.d
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DT[_DT[self.dtype]]
+
+
+@dataclass
+class Branch:
+    """Compressed history of one branch on the GPU (idx, codes, scales) plus
+    its centers [A, W] and decoder [W, r]."""
+    idx: torch.Tensor
+    codes: torch.Tensor
+    scales: torch.Tensor
+    centers: torch.Tensor
+    decoder: torch.Tensor
+
+    def c(self) -> nkv_branch:
+        return nkv_branch(_ptr(self.idx), _ptr(self.codes), _ptr(self.scales), _ptr(self.centers),
+                          _ptr(self.decoder), int(self.centers.shape[0]))
+
+    @property
+    def A(self) -> int:
+        return int(self.centers.shape[0])
+
+
+def _segments(route: Optional[Sequence[Tuple[int, int, int]]]):
+    if not route:
+        return None, 0
+    arr = (nkv_segment * len(route))(*[nkv_segment(int(b), int(e), int(m)) for b, e, m in route])
+    return arr, len(route)
+
+
+# ----------------------------------------------------------------------------
+# entry points with the C names
+# ----------------------------------------------------------------------------
+
+def nkv_version() -> int:
+    return load().nkv_version()
+
+
+def nkv_force_generic(on: bool) -> None:
+    load().nkv_force_generic(1 if on else 0)
+
+
+def nkv_encode_workspace_size(shape: Shape, N: int, A: int) -> int:
+    n = load().nkv_encode_workspace_size(ctypes.byref(shape.c()), N, A)
+    if n == SIZE_MAX:
+        raise NkvError(1, "invalid encode shape")
+    return n
+
+
+def nkv_encode(shape: Shape, x, centers, encoder, idx, codes, scales, ws=None, stream=None):
+    N = int(x.shape[0]) if x is not None else 0
+    _check(load().nkv_encode(ctypes.byref(shape.c()), _ptr(x), N, _ptr(centers),
+                             int(centers.shape[0]), _ptr(encoder), _ptr(idx), _ptr(codes),
+                             _ptr(scales), _ptr(ws), 0 if ws is None else ws.numel(),
+                             _stream(stream)))
+
+
+def nkv_attend_workspace_size(shape: Shape, A_k: int, A_v: int, N_hist: int, route, r_low: int,
+                              Nq: int, N_cur: int) -> int:
+    segs, n = _segments(route)
+    res = load().nkv_attend_workspace_size(ctypes.byref(shape.c()), A_k, A_v, N_hist, segs, n,
+                                           r_low, Nq, N_cur)
+    if res == SIZE_MAX:
+        raise NkvError(1, load().nkv_last_error().decode() or "invalid attend arguments")
+    return res
+
+
+def nkv_attend_full(shape: Shape, k: Branch, v: Branch, N_hist: int, q, cur_k, cur_v, out, lse,
+                    ws=None, stream=None):
+    N_cur = 0 if cur_k is None else int(cur_k.shape[0])
+    _check(load().nkv_attend_full(ctypes.byref(shape.c()), ctypes.byref(k.c()),
+                                  ctypes.byref(v.c()), N_hist, _ptr(q), int(q.shape[0]),
+                                  _ptr(cur_k), _ptr(cur_v), N_cur, _ptr(out), _ptr(lse),
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def nkv_attend_fast(shape: Shape, k: Branch, v: Branch, N_hist: int, route, r_low: int, q, cur_k,
+                    cur_v, out, lse, ws=None, stream=None):
+    N_cur = 0 if cur_k is None else int(cur_k.shape[0])
+    segs, n = _segments(route)
+    _check(load().nkv_attend_fast(ctypes.byref(shape.c()), ctypes.byref(k.c()),
+                                  ctypes.byref(v.c()), N_hist, segs, n, r_low, _ptr(q),
+                                  int(q.shape[0]), _ptr(cur_k), _ptr(cur_v), N_cur, _ptr(out),
+                                  _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream)))
+
+
+def nkv_lse_merge(H: int, d: int, o_a, lse_a, o_b, lse_b, out, lse_out, stream=None):
+    dt = NKV_F32 if out.dtype == torch.float32 else NKV_BF16
+    _check(load().nkv_lse_merge(int(o_a.shape[0]), H, d, _ptr(o_a), _ptr(lse_a), _ptr(o_b),
+                                _ptr(lse_b), _ptr(out), dt, _ptr(lse_out), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# allocating helpers
+# ----------------------------------------------------------------------------
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def encode(shape: Shape, x, centers, encoder, out=None, stream=None):
+    """Encode tokens x [N, W]; returns (idx int32 [N], codes uint8 [N, r/2],
+    scales int16 [N, r/group] holding fp16 bits).  ``out`` may supply the
+    three output tensors (e.g. views into a preallocated history)."""
+    N = int(x.shape[0])
+    dev = x.device
+    if out is None:
+        out = (torch.empty(N, dtype=torch.int32, device=dev),
+               torch.empty((N, shape.r // 2), dtype=torch.uint8, device=dev),
+               torch.empty((N, shape.r // shape.group), dtype=torch.int16, device=dev))
+    ws = _workspace(nkv_encode_workspace_size(shape, N, int(centers.shape[0])), dev)
+    nkv_encode(shape, x, centers, encoder, *out, ws=ws, stream=stream)
+    return out
+
+
+def attend_full(shape: Shape, k: Branch, v: Branch, N_hist: int, q, cur_k=None, cur_v=None,
+                ws=None, stream=None):
+    Nq = int(q.shape[0])
+    N_cur = 0 if cur_k is None else int(cur_k.shape[0])
+    out = torch.empty((Nq, shape.W), dtype=shape.torch_dtype, device=q.device)
+    lse = torch.empty((Nq, shape.H), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(nkv_attend_workspace_size(shape, k.A, v.A, N_hist, None, 0, Nq, N_cur),
+                        q.device)
+    nkv_attend_full(shape, k, v, N_hist, q, cur_k, cur_v, out, lse, ws=ws, stream=stream)
+    return out, lse
+
+
+def attend_fast(shape: Shape, k: Branch, v: Branch, N_hist: int, route, r_low: int, q,
+                cur_k=None, cur_v=None, ws=None, stream=None):
+    Nq = int(q.shape[0])
+    N_cur = 0 if cur_k is None else int(cur_k.shape[0])
+    out = torch.empty((Nq, shape.W), dtype=shape.torch_dtype, device=q.device)
+    lse = torch.empty((Nq, shape.H), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(nkv_attend_workspace_size(shape, k.A, v.A, N_hist, route, r_low, Nq,
+                                                  N_cur), q.device)
+    nkv_attend_fast(shape, k, v, N_hist, route, r_low, q, cur_k, cur_v, out, lse, ws=ws,
+                    stream=stream)
+    return out, lse
+
+
+def lse_merge(H: int, d: int, o_a, lse_a, o_b, lse_b, out_dtype=torch.float32, stream=None):
+    out = torch.empty(o_a.shape, dtype=out_dtype, device=o_a.device)
+    lse = torch.empty(lse_a.shape, dtype=torch.float32, device=o_a.device)
+    nkv_lse_merge(H, d, o_a, lse_a, o_b, lse_b, out, lse, stream=stream)
+    return out, lse

@@ -1,0 +1,189 @@
+/*
+ * libnanokv -- compressed-history attention (NanoKV) for AMD Instinct MI355X.
+ *
+ * The method (NanoKV: High-Ratio KV Cache Compression for Autoregressive
+ * Video Generation) keeps the historical K/V cache of an autoregressive video
+ * model as, per token and per branch (K or V):
+ *   - the index of a shared cluster center (abstract; Figure 4(a)),
+ *   - r joint head-channel residual coefficients in INT4 (Figure 4(b)),
+ * with centers, encoder and decoder fitted separately per K/V branch
+ * (Table 5 caption).  History is read either full-dimensionally (decode,
+ * then ordinary attention; Figure 4(a)) or, in NanoKV-Fast, through a fixed
+ * routing policy that sends part of the history to a low-dimensional read in
+ * coefficient space whose result is LSE-merged with the rest (Figure 4(d)).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - W = H * d.  Channel h*d + j of a [*, W] row belongs to head h.
+ *  - Every array is a DEVICE pointer, row-major and contiguous, owned by the
+ *    caller; the library allocates nothing and keeps no state between calls
+ *    (apart from the thread-local error string).  Scratch memory is the
+ *    caller's `ws` buffer, sized by the matching *_workspace_size call.
+ *  - Token, query, center, encoder, decoder and output tensors have the
+ *    element type `nkv_shape.dtype`: NKV_F32 (float) or NKV_BF16 (bfloat16
+ *    bit patterns in uint16).
+ *  - Compressed records: idx int32 [N]; codes uint8 [N, r/2] (two's
+ *    complement INT4, coefficient 2j in the low nibble of byte j); scales
+ *    uint16 [N, r/group] holding IEEE fp16 bit patterns.  A group is `group`
+ *    consecutive coefficients of one token; scale = fp16 round-half-even of
+ *    max|z|/7 and code = clamp(round-half-even(z/scale), -8, 7); a zero scale
+ *    means all-zero codes.
+ *  - LSE outputs are natural-log, float32 [Nq, H].  An empty key set gives
+ *    O = 0 and LSE = -inf.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued asynchronously on it; arguments are validated synchronously
+ *    before anything is enqueued.  A device fault surfaces at the caller's
+ *    next synchronisation.
+ *  - Errors: a non-zero nkv_status; nkv_last_error() (thread-local) gives a
+ *    description.  No C++ exception crosses this interface.  Center indices
+ *    outside [0, A) in the inputs are undefined behaviour.
+ *
+ * Supported set (validated; NKV_EUNSUPPORTED otherwise): 1 <= H; d in
+ * {16, 32, 64, 128}; r even, r % group == 0, group in {8, 16, 32, 64}; for
+ * the Fast read 0 < r_low <= r.  The tuned MFMA kernels serve NKV_BF16 with
+ * d == 128 (r and r_low multiples of 16); every other supported shape runs
+ * on the generic HIP kernels.
+ */
+#ifndef NANOKV_H_
+#define NANOKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NKV_VERSION 1
+#define NKV_MAX_SEGMENTS 64
+
+typedef enum {
+  NKV_OK = 0,
+  NKV_EINVAL = 1,        /* malformed arguments (null pointer, bad size) */
+  NKV_EUNSUPPORTED = 2,  /* well-formed but outside the supported set   */
+  NKV_EWORKSPACE = 3,    /* ws too small (see *_workspace_size)         */
+  NKV_EHIP = 4           /* a HIP launch or runtime call failed         */
+} nkv_status;
+
+typedef enum { NKV_F32 = 0, NKV_BF16 = 1 } nkv_dtype;
+
+typedef enum { NKV_FULL = 0, NKV_LOW = 1 } nkv_route;
+
+typedef struct {
+  int32_t H;            /* heads                                         */
+  int32_t d;            /* head dimension                                */
+  int32_t r;            /* coefficients per token and branch             */
+  int32_t group;        /* INT4 group size (consecutive coefficients)    */
+  int32_t dtype;        /* nkv_dtype of tokens/queries/codec/outputs     */
+  float softmax_scale;  /* tau multiplying every score; <= 0 -> 1/sqrt(d) */
+} nkv_shape;
+
+/* One compressed branch (K or V): Figure 4(b) of the NanoKV pages. */
+typedef struct {
+  const int32_t* idx;      /* [N_hist] center index per token           */
+  const uint8_t* codes;    /* [N_hist, r/2] packed INT4                 */
+  const uint16_t* scales;  /* [N_hist, r/group] fp16 bits               */
+  const void* centers;     /* [A, W] shared cluster centers             */
+  const void* decoder;     /* [W, r] linear decoder D                   */
+  int32_t A;               /* number of centers                         */
+} nkv_branch;
+
+/* A half-open range [begin, end) of history positions and its read mode
+ * (Figure 4(d): a fixed policy routes history to full- or low-dimensional
+ * attention).  Segments must be disjoint and together cover [0, N_hist);
+ * at most NKV_MAX_SEGMENTS ranges per mode after adjacent ranges of the same
+ * mode are joined.  Host memory; read during the call only. */
+typedef struct {
+  int64_t begin;
+  int64_t end;
+  int32_t mode;            /* NKV_FULL or NKV_LOW */
+} nkv_segment;
+
+/* Bytes of workspace nkv_encode needs for N tokens and A centers (0 when
+ * none); SIZE_MAX if the shape is invalid. */
+size_t nkv_encode_workspace_size(const nkv_shape* shape, int64_t N, int32_t A);
+
+/*
+ * Encoder of one branch (NanoKV abstract and Figure 4(b)): for each token
+ * x_t (row of x [N, W]):
+ *   a_t = argmin_a ||x_t - centers[a]||^2   (squared L2, ties -> lowest a)
+ *   z_t = encoder (x_t - centers[a_t])       (encoder [r, W])
+ *   INT4-quantise z_t per group (format above).
+ * Writes idx[t], codes[t, :], scales[t, :].  Appending to a history is
+ * pointer arithmetic on these outputs.  N == 0 is a no-op.
+ */
+nkv_status nkv_encode(const nkv_shape* shape, const void* x, int64_t N,
+                      const void* centers, int32_t A, const void* encoder,
+                      int32_t* idx, uint8_t* codes, uint16_t* scales,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for nkv_attend_full / nkv_attend_fast with the same
+ * arguments (route == NULL, n_seg == 0 means "everything full").  SIZE_MAX
+ * if the arguments are invalid. */
+size_t nkv_attend_workspace_size(const nkv_shape* shape, int32_t A_k,
+                                 int32_t A_v, int64_t N_hist,
+                                 const nkv_segment* route, int32_t n_seg,
+                                 int32_t r_low, int64_t Nq, int64_t N_cur);
+
+/*
+ * NanoKV full-dimensional read (Figure 4(a)/(b)): decode every history token
+ * of both branches (x_hat = centers[idx] + decoder * (code * scale)), then
+ * softmax attention per head with scores tau * q_h . k_h over the decoded
+ * history followed by the uncompressed current chunk cur_k/cur_v [N_cur, W]
+ * (ignored, and may be NULL, when N_cur == 0).  q [Nq, W]; out [Nq, W] (shape dtype);
+ * lse [Nq, H] float32.
+ */
+nkv_status nkv_attend_full(const nkv_shape* shape, const nkv_branch* k,
+                           const nkv_branch* v, int64_t N_hist,
+                           const void* q, int64_t Nq, const void* cur_k,
+                           const void* cur_v, int64_t N_cur, void* out,
+                           float* lse, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * NanoKV-Fast mixed-dimensional read (Figure 4(d)).  History positions in
+ * NKV_FULL segments and the current chunk are read as in nkv_attend_full.
+ * Positions in NKV_LOW segments are read in coefficient space with the
+ * leading r_low coefficients of both branches; per head h, with D_{X,h} the
+ * rows h*d..h*d+d-1 of decoder X:
+ *   q~_h   = D_{K,h}[:, :r_low]^T q_h                        (query reduction)
+ *   s_t    = tau * (q~_h . c^K_t[:r_low] + q_h . centers_K[a^K_t, h])
+ *   O_low  = (D_{V,h}[:, :r_low] sum_t p_t c^V_t[:r_low]
+ *             + sum_t p_t centers_V[a^V_t, h]) / sum_t p_t   (restoration)
+ * with p_t = exp(s_t - max s).  The two partial results are LSE-merged.
+ */
+nkv_status nkv_attend_fast(const nkv_shape* shape, const nkv_branch* k,
+                           const nkv_branch* v, int64_t N_hist,
+                           const nkv_segment* route, int32_t n_seg,
+                           int32_t r_low, const void* q, int64_t Nq,
+                           const void* cur_k, const void* cur_v,
+                           int64_t N_cur, void* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * LSE merge of two partial attentions over disjoint key sets (Figure 4(d)):
+ *   L = log(exp(L_a) + exp(L_b)),  O = exp(L_a - L) O_a + exp(L_b - L) O_b.
+ * o_a, o_b float32 [Nq, H*d]; lse_a, lse_b, lse_out float32 [Nq, H]; out
+ * [Nq, H*d] of out_dtype.  A -inf partition contributes nothing; if both are
+ * -inf, O = 0 and L = -inf.  out/lse_out may alias o_a/lse_a.
+ */
+nkv_status nkv_lse_merge(int64_t Nq, int32_t H, int32_t d, const float* o_a,
+                         const float* lse_a, const float* o_b,
+                         const float* lse_b, void* out, int32_t out_dtype,
+                         float* lse_out, void* stream);
+
+/* Static description of a status code. */
+const char* nkv_status_string(nkv_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* nkv_last_error(void);
+int nkv_version(void);
+
+/* Testing aid: 1 routes every call through the generic HIP kernels even
+ * where the tuned MFMA kernels apply; 0 (default) restores the dispatch. */
+void nkv_force_generic(int on);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NANOKV_H_ */

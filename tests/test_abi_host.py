@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects malformed calls before anything reaches the GPU.
+
+Everything here runs without a GPU: validation returns before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_history_attention_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nanokv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lib.LIB_PATH),
+                                reason="libnanokv.so not built")
+
+EINVAL, EUNSUP, EWS = 1, 2, 3
+FAKE = 0x1000  # non-null pointer that is never dereferenced on these paths
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib.load()
+    names = _declared_functions()
+    assert {"nkv_encode", "nkv_attend_full", "nkv_attend_fast", "nkv_lse_merge"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(lib.EXPORTS) == set(names)
+    assert lib.nkv_version() == 1
+
+
+def _shape(H=2, d=128, r=64, group=32, dtype=1, scale=0.0):
+    return lib.nkv_shape(H, d, r, group, dtype, scale)
+
+
+def _branch(A=4):
+    return lib.nkv_branch(FAKE, FAKE, FAKE, FAKE, FAKE, A)
+
+
+def _encode(shape, N=4, A=4, x=FAKE, ws=None, wsb=0):
+    L = lib.load()
+    sh = None if shape is None else ctypes.byref(shape)
+    return L.nkv_encode(sh, x, N, FAKE, A, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+
+
+def test_encode_validation():
+    L = lib.load()
+    assert _encode(None) == EINVAL
+    assert _encode(_shape(d=100)) == EUNSUP
+    assert _encode(_shape(r=48, group=32)) == EUNSUP
+    assert _encode(_shape(group=12)) == EUNSUP
+    assert _encode(_shape(dtype=7)) == EINVAL
+    assert _encode(_shape(), A=0) == EINVAL
+    assert _encode(_shape(), N=-1) == EINVAL
+    assert _encode(_shape(), x=None) == EINVAL
+    assert _encode(_shape(scale=float("nan"))) == EINVAL
+    assert b"" != L.nkv_last_error()
+    # N == 0 is a no-op that touches nothing
+    assert _encode(_shape(), N=0, x=None) == 0
+
+
+def _attend_fast(shape, route, r_low=16, Nq=4, N_hist=10, N_cur=2, ws=None, wsb=0, q=FAKE,
+                 k=None):
+    L = lib.load()
+    segs, n = lib._segments(route)
+    k = k or _branch()
+    return L.nkv_attend_fast(ctypes.byref(shape), ctypes.byref(k), ctypes.byref(_branch()),
+                             N_hist, segs, n, r_low, q, Nq, FAKE, FAKE, N_cur, FAKE, FAKE, ws,
+                             wsb, None)
+
+
+def test_attend_validation():
+    sh = _shape()
+    ok_route = [(0, 6, 1), (6, 10, 0)]
+    assert _attend_fast(sh, ok_route, ws=None) == EWS           # workspace missing
+    assert _attend_fast(sh, [(0, 6, 1), (5, 10, 0)]) == EINVAL  # overlap
+    assert _attend_fast(sh, [(0, 6, 1)]) == EINVAL              # gap
+    assert _attend_fast(sh, [(0, 6, 1), (6, 11, 0)]) == EINVAL  # out of range
+    assert _attend_fast(sh, [(0, 6, 3), (6, 10, 0)]) == EINVAL  # bad mode
+    assert _attend_fast(sh, ok_route, r_low=0) == EUNSUP
+    assert _attend_fast(sh, ok_route, r_low=65) == EUNSUP
+    assert _attend_fast(sh, ok_route, q=None) == EINVAL
+    bad = _branch()
+    bad.A = 0
+    assert _attend_fast(sh, ok_route, k=bad) == EINVAL
+    many = [(i, i + 1, i % 2) for i in range(200)]
+    assert _attend_fast(sh, many, N_hist=200) == EUNSUP
+    # Nq == 0 with a valid (large enough) workspace is a no-op
+    need = lib.load().nkv_attend_workspace_size(ctypes.byref(sh), 4, 4, 10,
+                                                lib._segments(ok_route)[0], 2, 16, 0, 2)
+    assert need != lib.SIZE_MAX
+    assert _attend_fast(sh, ok_route, Nq=0, ws=FAKE, wsb=need) == 0
+
+
+def test_attend_full_validation():
+    L = lib.load()
+    sh = _shape()
+    k, v = _branch(), _branch()
+    args = lambda N_cur, ck: (ctypes.byref(sh), ctypes.byref(k), ctypes.byref(v), 10, FAKE, 4,
+                              ck, ck, N_cur, FAKE, FAKE, None, 0, None)
+    assert L.nkv_attend_full(*args(3, None)) == EINVAL        # current chunk missing
+    assert L.nkv_attend_full(*args(3, FAKE)) == EWS
+
+
+def test_workspace_size_queries():
+    L = lib.load()
+    sh = _shape()
+    assert L.nkv_attend_workspace_size(ctypes.byref(sh), 4, 4, 10, None, 0, 0, 4, 2) > 0
+    segs, n = lib._segments([(0, 6, 1), (5, 10, 0)])
+    assert L.nkv_attend_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, 16, 4, 2) == lib.SIZE_MAX
+    assert L.nkv_encode_workspace_size(ctypes.byref(_shape(d=100)), 4, 4) == lib.SIZE_MAX
+
+
+def test_merge_validation():
+    L = lib.load()
+    assert L.nkv_lse_merge(4, 0, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == EINVAL
+    assert L.nkv_lse_merge(4, 2, 16, None, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == EINVAL
+    assert L.nkv_lse_merge(4, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 5, FAKE, None) == EINVAL
+    assert L.nkv_lse_merge(0, 2, 16, None, None, None, None, None, 0, None, None) == 0
+
+
+def test_status_strings():
+    L = lib.load()
+    assert L.nkv_status_string(0) == b"ok"
+    assert L.nkv_status_string(3) == b"workspace too small"

@@ -1,0 +1,295 @@
+"""GPU parity: the HIP library against the fp64 oracle, through the C ABI.
+
+Bars: center indices bit-exact; INT4 codes bit-exact outside the rounding
+window (scales per the near-midpoint rule); attention outputs within
+max|err| / max|ref| <= 1e-2 and LSE within 1e-3 absolute.  Fast reads must
+also be closer to the oracle's Fast result than to its full-dimensional
+result (err <= 0.5 * gap), and on the center-scaled variants, where the two
+differ widely, within a tenth of that gap.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_history_attention_amd import lib, synth
+from gpu_cases import (attention_errors, check_encode, device_branch, from_dev, get_case, log,
+                       oracle_branch, oracle_full_chunked, oracle_inputs, q_rows, shape_of,
+                       to_dev)
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL, LSE_TOL = 1e-2, 1e-3
+
+S = synth.small_config
+SMALL = {
+    "S1": S("C3", H=2, r=64, A=16, n_hist=700, Nq=130, N_cur=77, chunk=300, mode="full",
+            n_full_tail=0, r_low=0),
+    "S2": S("C3", H=3, r=96, A=70, n_hist=1500, Nq=150, N_cur=90, chunk=500, r_low=32,
+            n_full_tail=333),
+    "S3": S("C2", H=2, A=200, n_hist=2000, Nq=100, N_cur=50, chunk=700, r_low=48,
+            n_full_tail=700),
+    "S2d": S("C3", H=3, r=96, A=70, n_hist=1500, Nq=150, N_cur=90, chunk=500, r_low=32,
+             n_full_tail=333, center_scale=0.05, seed=21),
+    "C0f": S("C0", mode="fast", r_low=4, n_full_tail=32),
+    "C0d": S("C0", mode="fast", r_low=4, n_full_tail=32, center_scale=0.05),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _cfg(name):
+    return synth.CONFIGS[name] if name in synth.CONFIGS else SMALL[name]
+
+
+# --------------------------------------------------------------------------
+# encode
+# --------------------------------------------------------------------------
+
+def _encode_and_check(cfg, x, b, w):
+    shape = shape_of(cfg)
+    xd = to_dev(x, cfg.dtype)
+    idx, codes, scales = lib.encode(shape, xd, to_dev(w.centers(b), cfg.dtype),
+                                    to_dev(w.encoder(b), cfg.dtype))
+    torch.cuda.synchronize()
+    ref = oracle.encode(x, w.centers(b), w.encoder(b), cfg.group, cfg.dtype)
+    rep = check_encode(idx.cpu().numpy(), codes.cpu().numpy(), scales.cpu().numpy(), ref,
+                       cfg.group)
+    return rep, (idx, codes, scales)
+
+
+@pytest.mark.parametrize("name", ["C0", "S1", "S2", "C1"])
+def test_encode_history_chunk(name):
+    cfg = _cfg(name)
+    w = synth.workload(cfg)
+    for b in range(2):
+        x = w.history_chunk(b, 0)[0]
+        log(f"encode {name} branch {b} N={x.shape[0]} W={cfg.W}")
+        rep, _ = _encode_and_check(cfg, x, b, w)
+        log(f"  {rep}")
+
+
+def test_encode_new_chunk_full_size():
+    cfg = synth.CONFIGS["C4"]
+    w = synth.workload(cfg)
+    for b in range(2):
+        x = w.new_chunk(b)[0]
+        log(f"encode C4 new chunk branch {b} N={x.shape[0]}")
+        rep, _ = _encode_and_check(cfg, x, b, w)
+        log(f"  {rep}")
+
+
+def test_encode_deterministic_and_offset_append():
+    cfg = SMALL["S2"]
+    w = synth.workload(cfg)
+    x = w.history_chunk(0, 0)[0]
+    shape = shape_of(cfg)
+    xd = to_dev(x, cfg.dtype)
+    mu, enc = to_dev(w.centers(0), cfg.dtype), to_dev(w.encoder(0), cfg.dtype)
+    a = lib.encode(shape, xd, mu, enc)
+    # append into the middle of a larger preallocated history
+    n = x.shape[0]
+    hist = (torch.full((n + 50,), -1, dtype=torch.int32, device="cuda"),
+            torch.zeros((n + 50, cfg.r // 2), dtype=torch.uint8, device="cuda"),
+            torch.zeros((n + 50, cfg.r // cfg.group), dtype=torch.int16, device="cuda"))
+    lib.encode(shape, xd, mu, enc, out=tuple(t[20:20 + n] for t in hist))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], hist[0][20:20 + n]) and torch.equal(a[1], hist[1][20:20 + n])
+    assert torch.equal(a[2], hist[2][20:20 + n])
+    assert int(hist[0][:20].max()) == -1 and int(hist[0][20 + n:].max()) == -1
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+def _run_attend(case, rows_sample=None, route=None, r_low=None, fast=None):
+    cfg = case.cfg
+    fast = (cfg.mode == "fast") if fast is None else fast
+    route = cfg.segments() if route is None else route
+    r_low = cfg.r_low if r_low is None else r_low
+    shape = shape_of(cfg)
+    kb, vb = device_branch(case, 0), device_branch(case, 1)
+    q = to_dev(case.w.queries(), cfg.dtype)
+    ck = to_dev(case.w.current(0), cfg.dtype) if cfg.N_cur else None
+    cv = to_dev(case.w.current(1), cfg.dtype) if cfg.N_cur else None
+    n_hist = cfg.n_attend
+    log(f"attend {cfg.name} fast={fast} Nq={cfg.Nq} N_hist={n_hist} N_cur={cfg.N_cur} "
+        f"r_low={r_low} route={route}")
+    if fast:
+        out, lse = lib.attend_fast(shape, kb, vb, n_hist, route, r_low, q, ck, cv)
+    else:
+        out, lse = lib.attend_full(shape, kb, vb, n_hist, q, ck, cv)
+    torch.cuda.synchronize()
+    rows = q_rows(cfg, rows_sample)
+    return from_dev(out)[rows], from_dev(lse)[rows], rows
+
+
+def _oracle_attend(case, rows, fast, route, r_low):
+    cfg = case.cfg
+    q, ck, cv = oracle_inputs(case, rows)
+    kb, vb = oracle_branch(case, 0), oracle_branch(case, 1)
+    if not fast:
+        return oracle_full_chunked(q, kb, vb, ck, cv, cfg)
+    return oracle.attend_fast(q, kb, vb, route, r_low, ck, cv, cfg.H, cfg.d, cfg.tau)
+
+
+def _check_attend(name, sample=None, route=None, r_low=None, drule=None):
+    cfg = _cfg(name)
+    case = get_case(cfg)
+    fast = cfg.mode == "fast"
+    route_ = cfg.segments() if route is None else route
+    r_low_ = cfg.r_low if r_low is None else r_low
+    out, lse, rows = _run_attend(case, sample, route, r_low)
+    ro, rl = _oracle_attend(case, rows, fast, route_, r_low_)
+    rel, lerr = attention_errors(out, lse, ro, rl)
+    log(f"  {name}: rows={len(rows)} max|err|/max|ref|={rel:.3e} max|dLSE|={lerr:.3e}")
+    assert rel <= OUT_TOL and lerr <= LSE_TOL
+    if fast and drule is not None:
+        q, ck, cv = oracle_inputs(case, rows)
+        fo, _ = oracle_full_chunked(q, oracle_branch(case, 0), oracle_branch(case, 1), ck, cv, cfg)
+        gap = float(np.max(np.abs(fo - ro)))
+        err = float(np.max(np.abs(out - ro)))
+        log(f"  {name}: fast-vs-full gap={gap:.3e} err={err:.3e} ratio={err / gap:.3e}")
+        assert err <= drule * gap
+    return rel, lerr
+
+
+@pytest.mark.parametrize("name", ["C0", "S1"])
+def test_attend_full_small(name):
+    _check_attend(name)
+
+
+@pytest.mark.parametrize("name,drule", [("C0f", 0.5), ("C0d", 0.1), ("S2", 0.5), ("S3", 0.5),
+                                        ("S2d", 0.1)])
+def test_attend_fast_small(name, drule):
+    _check_attend(name, drule=drule)
+
+
+def test_attend_full_C1():
+    _check_attend("C1", sample=48)
+
+
+@pytest.mark.parametrize("name", ["C2", "C3"])
+def test_attend_fast_full_size(name):
+    _check_attend(name, sample=40, drule=0.5)
+
+
+def test_encode_append_attend_C4():
+    """Long-rollout step: encode the new chunk into the preallocated history
+    on the GPU, then the Fast read over the 33-chunk history."""
+    cfg = synth.CONFIGS["C4"]
+    case = get_case(cfg)
+    shape = shape_of(cfg)
+    w = case.w
+    n_old = cfg.n_hist
+    brs = []
+    for b in range(2):
+        full = device_branch(case, b, include_new=False)
+        n = cfg.n_attend
+        idx = torch.empty(n, dtype=torch.int32, device="cuda")
+        codes = torch.empty((n, cfg.r // 2), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((n, cfg.r // cfg.group), dtype=torch.int16, device="cuda")
+        idx[:n_old], codes[:n_old], sc[:n_old] = full.idx, full.codes, full.scales
+        lib.encode(shape, to_dev(w.new_chunk(b)[0], cfg.dtype), full.centers,
+                   to_dev(w.encoder(b), cfg.dtype), out=(idx[n_old:], codes[n_old:], sc[n_old:]))
+        brs.append(lib.Branch(idx, codes, sc, full.centers, full.decoder))
+    torch.cuda.synchronize()
+    for b in range(2):
+        rep = check_encode(brs[b].idx[n_old:].cpu().numpy(), brs[b].codes[n_old:].cpu().numpy(),
+                           brs[b].scales[n_old:].cpu().numpy(), case.new_enc[b], cfg.group)
+        log(f"  C4 appended chunk branch {b}: {rep}")
+    q = to_dev(w.queries(), cfg.dtype)
+    ck, cv = to_dev(w.current(0), cfg.dtype), to_dev(w.current(1), cfg.dtype)
+    log("attend C4 fast over 33 chunks")
+    out, lse = lib.attend_fast(shape, brs[0], brs[1], cfg.n_attend, cfg.segments(), cfg.r_low,
+                               q, ck, cv)
+    torch.cuda.synchronize()
+    rows = q_rows(cfg, 32)
+    out, lse = from_dev(out)[rows], from_dev(lse)[rows]
+    ro, rl = _oracle_attend(case, rows, True, cfg.segments(), cfg.r_low)
+    rel, lerr = attention_errors(out, lse, ro, rl)
+    log(f"  C4: max|err|/max|ref|={rel:.3e} max|dLSE|={lerr:.3e}")
+    assert rel <= OUT_TOL and lerr <= LSE_TOL
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+def _edge(name, **kw):
+    cfg = dataclasses.replace(SMALL["S2"], name=name, **kw)
+    return cfg
+
+
+@pytest.mark.parametrize("kw,route", [
+    (dict(n_hist=0), None),                                   # current chunk only
+    (dict(N_cur=0), None),                                    # history only
+    (dict(n_hist=0, N_cur=0), None),                          # nothing: O = 0, LSE = -inf
+    (dict(N_cur=0, n_full_tail=0), None),                     # all history low-dimensional
+    (dict(Nq=1), None),                                       # one query
+    (dict(), [(i * 150, (i + 1) * 150, i % 2) for i in range(10)]),  # interleaved routing
+])
+def test_attend_edge_cases(kw, route):
+    cfg = _edge("edge", **kw)
+    case = get_case(cfg)
+    rows = q_rows(cfg, None)
+    for fast in (False, True):
+        if fast and cfg.n_attend == 0 and route is None:
+            rt = []
+        else:
+            rt = cfg.segments() if route is None else route
+        out, lse, _ = _run_attend(case, None, rt if fast else None, fast=fast)
+        ro, rl = _oracle_attend(case, rows, fast, rt, cfg.r_low)
+        if cfg.n_attend == 0 and cfg.N_cur == 0:
+            assert np.all(out == 0) and np.all(np.isneginf(lse))
+            continue
+        rel, lerr = attention_errors(out, lse, ro, rl)
+        log(f"  edge {kw} fast={fast}: {rel:.3e} {lerr:.3e}")
+        assert rel <= OUT_TOL and lerr <= LSE_TOL
+
+
+def test_fast_with_full_rank_matches_full_read():
+    cfg = SMALL["S2"]
+    case = get_case(cfg)
+    out_f, lse_f, _ = _run_attend(case, fast=False)
+    out_q, lse_q, _ = _run_attend(case, fast=True, r_low=cfg.r)
+    rel, lerr = attention_errors(out_q, lse_q, out_f, lse_f)
+    log(f"  r_low=r vs full on GPU: {rel:.3e} {lerr:.3e}")
+    assert rel <= OUT_TOL and lerr <= LSE_TOL
+
+
+# --------------------------------------------------------------------------
+# LSE merge
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_lse_merge(out_dt):
+    rng = np.random.default_rng(2)
+    Nq, H, d = 37, 3, 128
+    oa, ob = rng.standard_normal((2, Nq, H * d))
+    la, lb = rng.standard_normal((2, Nq, H)) * 3
+    la[0, :] = -np.inf
+    lb[1, 1] = -np.inf
+    la[2, 2] = lb[2, 2] = -np.inf
+    ro, rl = oracle.lse_merge([(oa, la), (ob, lb)], H, d)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    dt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    out, lse = lib.lse_merge(H, d, dev(oa), dev(la), dev(ob), dev(lb), out_dtype=dt)
+    torch.cuda.synchronize()
+    out, lse = from_dev(out), from_dev(lse)
+    tol = 1e-6 if out_dt == "f32" else 8e-3
+    assert np.max(np.abs(out - ro)) <= tol * np.max(np.abs(ro))
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert np.max(np.abs(lse[fin] - rl[fin])) < 1e-5
+    assert np.all(out[2, 2 * d:3 * d] == 0)
