@@ -1,0 +1,190 @@
+// Flash attention forward over decoded history and the current chunk
+// (NanoKV full-dimensional read, Figure 4(a): attention itself is unchanged
+// once K/V are reconstructed).  bf16 MFMA for QK^T and PV, fp32 online
+// softmax in base 2 with the softmax scale folded into one FMA, lazy
+// rescaling (the running maximum only moves when a tile exceeds it by more
+// than 2^8), natural-log LSE out.
+//
+// Layout: Q [Nq, W] bf16; K_all [Nk_pad, W] bf16 rows; V^T [H][128][ld]
+// bf16 (per-head transposed so PV operands are contiguous along keys).
+// Keys beyond Nk up to the 64-key padding are zero and masked.
+//
+// Block = 4 waves x 32 queries of one head; each tile of 64 keys is staged
+// through double-buffered LDS.  Per wave and tile: S^T = K Q^T is 2 x 8
+// MFMA 32x32x16 (lane = query column, 32 keys per lane), O^T += V^T P^T is
+// 4 x 4 MFMAs whose B operand is the wave's own P in registers.
+#include "tuned_internal.hpp"
+
+namespace nkv {
+
+constexpr int FA_KS = 136;  // LDS row stride of the K tile (128 + 8 bf16)
+constexpr int FA_VS = 68;   // LDS row stride of the V^T tile (64 + 4 bf16)
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q, int64_t Nq, int H,
+                                                  float c, const uint16_t* __restrict__ K,
+                                                  const uint16_t* __restrict__ VT, int64_t Nk,
+                                                  int64_t ld, void* __restrict__ out,
+                                                  float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][FA_KT * FA_KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][128 * FA_VS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+  const int h = blockIdx.y;
+  const int W = H * 128;
+  const int64_t q0 = (int64_t)blockIdx.x * FA_QB + wave * 32;
+  const int64_t qrow = q0 + (lane & 31);
+  const bool qok = qrow < Nq;
+
+  bf16x8 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    qf[ks] = qok ? as_bf16x8(ld_u32x4(Q + qrow * W + h * 128 + 16 * ks + 8 * hl))
+                 : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = zero16();
+  float m_run = -INFINITY, l_part = 0.f;
+
+  const int64_t ntiles = (Nk + FA_KT - 1) / FA_KT;
+  u32x4 rk[4], rv[4];
+  auto fetch = [&](int64_t t0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cidx = tid + 256 * j;
+      const int kr = cidx >> 4, kc = (cidx & 15) * 8;
+      rk[j] = ld_u32x4(K + (t0 + kr) * W + h * 128 + kc);
+      const int vd = cidx >> 3, vc = (cidx & 7) * 8;
+      rv[j] = ld_u32x4(VT + ((int64_t)h * 128 + vd) * ld + t0 + vc);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cidx = tid + 256 * j;
+      const int kr = cidx >> 4, kc = (cidx & 15) * 8;
+      *reinterpret_cast<u32x4*>(&sK[buf][kr * FA_KS + kc]) = rk[j];
+      const int vd = cidx >> 3, vc = (cidx & 7) * 8;
+      *reinterpret_cast<u32x2*>(&sV[buf][vd * FA_VS + vc]) = u32x2{rv[j][0], rv[j][1]};
+      *reinterpret_cast<u32x2*>(&sV[buf][vd * FA_VS + vc + 4]) = u32x2{rv[j][2], rv[j][3]};
+    }
+  };
+
+  if (ntiles > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int64_t tile = 0; tile < ntiles; ++tile) {
+    const int buf = (int)(tile & 1);
+    if (tile + 1 < ntiles) fetch((tile + 1) * FA_KT);
+    // ---- S^T = K Q^T ------------------------------------------------------
+    f32x16 s[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            &sK[buf][(kb * 32 + (lane & 31)) * FA_KS + 16 * ks + 8 * hl]));
+        s[kb] = mfma_bf16(a, qf[ks], s[kb]);
+      }
+    }
+    if ((tile + 1) * FA_KT > Nk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (tile * FA_KT + kb * 32 + acc_row(e, lane) >= Nk) s[kb][e] = -INFINITY;
+    }
+    // ---- online softmax (base 2, lazy rescale) ----------------------------
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c;
+    if (mt > m_run + 8.f) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+      l_part *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      m_run = mt;
+    }
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 pk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * u], c, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * u + 1], c, -m_run));
+          l_part += p0 + p1;
+          pk[u] = pack_bf16x2(p0, p1);
+        }
+        pb[2 * kb + half] = as_bf16x8(pk);
+      }
+    }
+    // ---- O^T += V^T P^T ---------------------------------------------------
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint16_t* vrow = &sV[buf][(db * 32 + (lane & 31)) * FA_VS + 16 * j + 4 * hl];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+        const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o[db] = mfma_bf16(a, pb[j], o[db]);
+      }
+    }
+    if (tile + 1 < ntiles) {
+      stash(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  // ---- epilogue -------------------------------------------------------------
+  const float l = l_part + __shfl_xor(l_part, 32, 64);
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  if (qok) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = db * 32 + g * 8 + hl * 4;  // 4 consecutive dims e = 4g .. 4g+3
+        const int64_t base = qrow * W + h * 128 + dim;
+        if (OUT_F32) {
+          float* of = static_cast<float*>(out);
+          *reinterpret_cast<f32x4*>(of + base) =
+              f32x4{o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                    o[db][4 * g + 3] * inv};
+        } else {
+          uint16_t* ob = static_cast<uint16_t*>(out);
+          *reinterpret_cast<u32x2*>(ob + base) =
+              u32x2{pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                    pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+        }
+      }
+    }
+    if (hl == 0)
+      lse[qrow * H + h] = (l > 0.f) ? (m_run + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+nkv_status launch_flash(const uint16_t* q, int64_t Nq, int H, float tau, const uint16_t* kall,
+                        const uint16_t* vt, int64_t Nk, int64_t ld, bool out_f32, void* out,
+                        float* lse, hipStream_t st) {
+  if (Nq == 0) return NKV_OK;
+  const float c = tau * 1.4426950408889634f;
+  dim3 grid((unsigned)ceil_div(Nq, FA_QB), (unsigned)H);
+  if (out_f32)
+    hipLaunchKernelGGL(k_flash<true>, grid, dim3(256), 0, st, q, Nq, H, c, kall, vt, Nk, ld, out, lse);
+  else
+    hipLaunchKernelGGL(k_flash<false>, grid, dim3(256), 0, st, q, Nq, H, c, kall, vt, Nk, ld, out, lse);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
+}  // namespace nkv

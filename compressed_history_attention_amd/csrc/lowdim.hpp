@@ -1,0 +1,15 @@
+// NanoKV-Fast low-dimensional read on the tuned path.
+#pragma once
+
+#include "tuned_internal.hpp"
+
+namespace nkv {
+
+size_t low_workspace_bytes(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& low,
+                           int32_t r_low, int64_t Nq);
+// Writes O_low fp32 [Nq, W] and LSE_low [Nq, H] for the low-routed tokens.
+nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
+                      const RangeTable& low, int32_t r_low, float tau, const uint16_t* q,
+                      int64_t Nq, float* o_low, float* lse_low, char* ws, hipStream_t st);
+
+}  // namespace nkv

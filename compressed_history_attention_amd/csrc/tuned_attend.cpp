@@ -1,0 +1,78 @@
+// Orchestration of the tuned (MFMA) attention path: workspace layout and the
+// sequence of kernels for the full-dimensional and the Fast reads.
+#include "tuned_internal.hpp"
+#include "lowdim.hpp"
+
+namespace nkv {
+
+bool tuned_available() { return true; }
+
+namespace {
+
+struct Layout {
+  int64_t nk = 0, nk_pad = 0;
+  size_t kall = 0, vt = 0, o_full = 0, lse_full = 0, o_low = 0, lse_low = 0, low = 0;
+  size_t total = 0;
+};
+
+Layout make_layout(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& full,
+                   const RangeTable& low, int32_t r_low, int64_t Nq, int64_t N_cur) {
+  Layout L;
+  const int64_t W = (int64_t)s->H * s->d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.nk = full.total + N_cur;
+  L.nk_pad = ceil_div(L.nk, FA_KT) * FA_KT;
+  L.kall = take(sizeof(uint16_t) * L.nk_pad * W);
+  L.vt = take(sizeof(uint16_t) * L.nk_pad * W);
+  if (low.total > 0) {
+    L.o_full = take(sizeof(float) * Nq * W);
+    L.lse_full = take(sizeof(float) * Nq * s->H);
+    L.o_low = take(sizeof(float) * Nq * W);
+    L.lse_low = take(sizeof(float) * Nq * s->H);
+    L.low = take(low_workspace_bytes(s, A_k, A_v, low, r_low, Nq));
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t tuned_attend_workspace(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& full,
+                              const RangeTable& low, int32_t r_low, int64_t Nq, int64_t N_cur) {
+  return make_layout(s, A_k, A_v, full, low, r_low, Nq, N_cur).total;
+}
+
+nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
+                        const RangeTable& full, const RangeTable& low, int32_t r_low, float tau,
+                        const void* q, int64_t Nq, const void* cur_k, const void* cur_v,
+                        int64_t N_cur, void* out, float* lse, char* ws, size_t ws_bytes,
+                        hipStream_t st) {
+  const Layout L = make_layout(s, kb.A, vb.A, full, low, r_low, Nq, N_cur);
+  const int H = s->H, W = H * s->d;
+  uint16_t* kall = reinterpret_cast<uint16_t*>(ws + L.kall);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
+  nkv_status e;
+  if ((e = launch_decode_tuned(kb, W, s->r, s->group, full, kall, 0, false, st))) return e;
+  if ((e = launch_decode_tuned(vb, W, s->r, s->group, full, vt, L.nk_pad, true, st))) return e;
+  if ((e = launch_stage_current(static_cast<const uint16_t*>(cur_k),
+                                static_cast<const uint16_t*>(cur_v), N_cur, L.nk_pad - full.total,
+                                W, kall, vt, L.nk_pad, full.total, st)))
+    return e;
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  if (low.total == 0)
+    return launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, false, out, lse, st);
+  float* of = reinterpret_cast<float*>(ws + L.o_full);
+  float* lf = reinterpret_cast<float*>(ws + L.lse_full);
+  float* ol = reinterpret_cast<float*>(ws + L.o_low);
+  float* ll = reinterpret_cast<float*>(ws + L.lse_low);
+  if ((e = launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, st))) return e;
+  if ((e = launch_low(s, kb, vb, low, r_low, tau, qb, Nq, ol, ll, ws + L.low, st))) return e;
+  return launch_lse_merge(Nq, H, s->d, of, lf, ol, ll, out, NKV_BF16, lse, st);
+}
+
+}  // namespace nkv

@@ -1,0 +1,319 @@
+// Tuned encoder and decoder of libnanokv (bf16, MFMA).
+//
+// Encoder (NanoKV abstract; Figure 4(b)):
+//   1. ||mu_a||^2 per center (fp32).
+//   2. Distance GEMM  d(a, t) = ||mu_a||^2 - 2 mu_a . x_t  on bf16 MFMA (bf16
+//      products are exact in fp32); the epilogue reduces each token's
+//      column to (min distance, lowest index) and merges blocks with a
+//      64-bit atomicMin on (order-preserving distance bits << 32 | a).
+//   3. Projection GEMM z = E (x - mu_a): the fp32 residual (exact for bf16
+//      inputs) is split into three bf16 terms hi + mid + lo = e, so three
+//      exact-product MFMA passes with fp32 accumulation give the projection
+//      at fp32 accuracy.
+//   4. INT4 group quantisation of z.
+// Decoder (Figure 4(b)): x_hat = mu_a + D (code * scale) as a GEMM whose A
+// loader dequantises INT4 on the fly and whose epilogue adds the center and
+// writes bf16 rows (K) or per-head transposed columns (V).
+#include "quant.hpp"
+#include "tuned_internal.hpp"
+
+namespace nkv {
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+__global__ void k_center_norms(const uint16_t* __restrict__ mu, int A, int W, float* __restrict__ out) {
+  const int a = blockIdx.x;
+  float acc = 0.f;
+  for (int w = threadIdx.x; w < W; w += 64) {
+    const float v = bf16_bits_to_f32(mu[(int64_t)a * W + w]);
+    acc = fmaf(v, v, acc);
+  }
+  acc = wave_sum(acc);
+  if (threadIdx.x == 0) out[a] = acc;
+}
+
+__global__ void k_fill_u64(uint64_t* p, int64_t n, uint64_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void k_unpack_idx(const uint64_t* __restrict__ keys, int64_t n, int32_t* __restrict__ idx) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) idx[i] = (int32_t)(keys[i] & 0xffffffffu);
+}
+
+__device__ __forceinline__ u32x4 load8_bf16(const uint16_t* base, int64_t row, int ld, int k,
+                                            bool ok) {
+  if (!ok) return u32x4{0u, 0u, 0u, 0u};
+  return ld_u32x4(base + row * ld + k);
+}
+
+// ---------------------------------------------------------------------------
+// distance GEMM with argmin epilogue: rows = centers, cols = tokens
+// ---------------------------------------------------------------------------
+struct DistProblem {
+  int M, N, K;  // M = A centers, N = tokens, K = W
+  const uint16_t* mu;
+  const uint16_t* x;
+  const float* mu2;
+  uint64_t* keys;
+  __device__ u32x4 load_a(int, int m, int k) const { return load8_bf16(mu, m, K, k, m < M && k < K); }
+  __device__ u32x4 load_b(int, int n, int k) const { return load8_bf16(x, n, K, k, n < N && k < K); }
+  __device__ void epilogue(int, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float best = INFINITY;
+      int besta = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int a = m0 + 32 * i + acc_row(e, lane);
+          if (a < M) {
+            const float dist = mu2[a] - 2.f * acc[i][j][e];
+            if (dist < best || (dist == best && a < besta)) { best = dist; besta = a; }
+          }
+        }
+      }
+      const float ob = __shfl_xor(best, 32, 64);
+      const int oa = __shfl_xor(besta, 32, 64);
+      if (ob < best || (ob == best && oa < besta)) { best = ob; besta = oa; }
+      const int n = n0 + 32 * j + (lane & 31);
+      if (lane < 32 && n < N && besta != 0x7fffffff) {
+        const uint64_t key = ((uint64_t)ordered_bits(best) << 32) | (uint32_t)besta;
+        atomicMin(reinterpret_cast<unsigned long long*>(keys + n), (unsigned long long)key);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// projection GEMM: rows = tokens, cols = coefficients, K = 3 W (split terms)
+// ---------------------------------------------------------------------------
+struct ProjProblem {
+  int M, N, K;  // M = tokens, N = r, K = 3 W
+  int W;
+  const uint16_t* x;
+  const uint16_t* mu;
+  const int32_t* idx;
+  const uint16_t* enc;  // [r, W]
+  float* z;             // [tokens, r]
+  __device__ u32x4 load_a(int, int m, int k) const {
+    if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    const int part = k / W, w = k - part * W;
+    const u32x4 xv = ld_u32x4(x + (int64_t)m * W + w);
+    const u32x4 mv = ld_u32x4(mu + (int64_t)idx[m] * W + w);
+    u32x4 out;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float e2[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const float xf = bf16_bits_to_f32(uint16_t(xv[h] >> (16 * s)));
+        const float mf = bf16_bits_to_f32(uint16_t(mv[h] >> (16 * s)));
+        float e = xf - mf;
+        // e = hi + mid + lo, each a bf16 value (round-half-even)
+        const float hi = bf16_bits_to_f32(f32_to_bf16_bits(e));
+        if (part == 0) { e2[s] = hi; continue; }
+        const float r1 = e - hi;
+        const float mid = bf16_bits_to_f32(f32_to_bf16_bits(r1));
+        e2[s] = (part == 1) ? mid : (r1 - mid);
+      }
+      out[h] = pack_bf16x2(e2[0], e2[1]);
+    }
+    return out;
+  }
+  __device__ u32x4 load_b(int, int n, int k) const {
+    if (n >= N || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    const int w = k % W;
+    return ld_u32x4(enc + (int64_t)n * W + w);
+  }
+  __device__ void epilogue(int, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + 32 * i + acc_row(e, lane), n = n0 + 32 * j + (lane & 31);
+          if (m < M && n < N) z[(int64_t)m * N + n] = acc[i][j][e];
+        }
+  }
+};
+
+__global__ void k_quantize_rows(const float* __restrict__ z, int64_t N, int r, int group,
+                                uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+  const int ng = r / group;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N * ng) return;
+  const int64_t t = i / ng;
+  const int g = (int)(i - t * ng);
+  quantize_group(z + t * r + g * group, group, codes + t * (r / 2) + g * (group / 2),
+                 scales + t * ng + g);
+}
+
+size_t tuned_encode_workspace(const nkv_shape* s, int64_t N, int32_t A) {
+  size_t off = 0;
+  off = align_up(off + sizeof(float) * A, 256);
+  off = align_up(off + sizeof(uint64_t) * N, 256);
+  off = align_up(off + sizeof(float) * N * s->r, 256);
+  return off;
+}
+
+nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void* centers,
+                        int32_t A, const void* enc, int32_t* idx, uint8_t* codes,
+                        uint16_t* scales, char* ws, size_t ws_bytes, hipStream_t st) {
+  const int W = s->H * s->d, r = s->r;
+  float* mu2 = reinterpret_cast<float*>(ws);
+  size_t off = align_up(sizeof(float) * A, 256);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ws + off);
+  off = align_up(off + sizeof(uint64_t) * N, 256);
+  float* z = reinterpret_cast<float*>(ws + off);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* mub = static_cast<const uint16_t*>(centers);
+  hipLaunchKernelGGL(k_center_norms, dim3(A), dim3(64), 0, st, mub, A, W, mu2);
+  NKV_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N,
+                     ~0ull);
+  NKV_LAUNCH_CHECK();
+  DistProblem dp{A, (int)N, W, mub, xb, mu2, keys};
+  nkv_status e = launch_gemm(dp, 1, st);
+  if (e) return e;
+  hipLaunchKernelGGL(k_unpack_idx, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N, idx);
+  NKV_LAUNCH_CHECK();
+  ProjProblem pp{(int)N, r, 3 * W, W, xb, mub, idx, static_cast<const uint16_t*>(enc), z};
+  if ((e = launch_gemm(pp, 1, st))) return e;
+  const int64_t ng = N * (r / s->group);
+  hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)ceil_div(ng, 256)), dim3(256), 0, st, z, N,
+                     r, s->group, codes, scales);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// decoder GEMM: rows = compacted tokens, cols = channels (128 = one head)
+// ---------------------------------------------------------------------------
+struct DecodeProblem {
+  int M, N, K;            // M = tokens in the list, N = W, K = r
+  int group;
+  BranchArgs b;
+  RangeTable rows;
+  uint16_t* out;          // K: row-major [*, W] at row offset; V: [H][128][ld]
+  int64_t ld;             // V^T key stride
+  bool transposed;
+  __device__ u32x4 load_a(int, int m, int k) const {
+    if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    const int64_t t = map_index(rows, m);
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(b.codes + t * (K / 2) + k / 2);
+    const float sc = fp16_bits_to_f32(b.scales[t * (K / group) + k / group]);
+    u32x4 out;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int n0 = (c >> (8 * h)) & 15, n1 = (c >> (8 * h + 4)) & 15;
+      const float v0 = (float)(n0 - ((n0 & 8) << 1)) * sc;
+      const float v1 = (float)(n1 - ((n1 & 8) << 1)) * sc;
+      out[h] = pack_bf16x2(v0, v1);
+    }
+    return out;
+  }
+  __device__ u32x4 load_b(int, int n, int k) const {
+    if (n >= N || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    return ld_u32x4(static_cast<const uint16_t*>(b.decoder) + (int64_t)n * K + k);
+  }
+  __device__ void epilogue(int, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+    const uint16_t* mu = static_cast<const uint16_t*>(b.centers);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int ai[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * i + acc_row(e, lane);
+        ai[e] = (m < M) ? b.idx[map_index(rows, m)] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + 32 * j + (lane & 31);
+        if (n >= N) continue;
+        if (!transposed) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = m0 + 32 * i + acc_row(e, lane);
+            if (m < M)
+              out[(int64_t)m * N + n] =
+                  f32_to_bf16_bits(acc[i][j][e] + bf16_bits_to_f32(mu[(int64_t)ai[e] * N + n]));
+          }
+        } else {
+          const int h = n >> 7, dd = n & 127;
+          uint16_t* col = out + ((int64_t)h * 128 + dd) * ld;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = m0 + 32 * i + acc_row(e, lane);
+            if (m < M)
+              col[m] = f32_to_bf16_bits(acc[i][j][e] + bf16_bits_to_f32(mu[(int64_t)ai[e] * N + n]));
+          }
+        }
+      }
+    }
+  }
+};
+
+nkv_status launch_decode_tuned(const BranchArgs& b, int W, int r, int group,
+                               const RangeTable& rows, uint16_t* out, int64_t ld, bool transposed,
+                               hipStream_t st) {
+  if (rows.total == 0) return NKV_OK;
+  DecodeProblem p{(int)rows.total, W, r, group, b, rows, out, ld, transposed};
+  return launch_gemm(p, 1, st);
+}
+
+// ---------------------------------------------------------------------------
+// current chunk -> attention workspace (K rows; V per-head transposed),
+// plus zero padding of the key tail
+// ---------------------------------------------------------------------------
+__global__ void k_copy_rows(const uint16_t* __restrict__ src, int64_t n_rows, int W,
+                            uint16_t* __restrict__ dst, int64_t pad_rows) {
+  // 8 bf16 per thread; rows beyond n_rows up to pad_rows are zero-filled
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = W / 8;
+  if (i >= pad_rows * per_row) return;
+  const int64_t row = i / per_row;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (row < n_rows) v = ld_u32x4(src + i * 8);
+  *reinterpret_cast<u32x4*>(dst + i * 8) = v;
+}
+
+// V [n, W] -> V^T[h][dd][key0 + t] for t < n; zero for n <= t < n_pad
+__global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict__ src, int64_t n,
+                                                     int64_t n_pad, int W, uint16_t* __restrict__ dst,
+                                                     int64_t ld, int64_t key0) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int tt = i / 64, cc = i % 64;
+    tile[tt][cc] = (t0 + tt < n) ? src[(t0 + tt) * W + c0 + cc] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, tt = i % 64;
+    const int c = c0 + cc;
+    if (t0 + tt < n_pad) dst[((int64_t)(c >> 7) * 128 + (c & 127)) * ld + key0 + t0 + tt] = tile[tt][cc];
+  }
+}
+
+nkv_status launch_stage_current(const uint16_t* ck, const uint16_t* cv, int64_t n_cur,
+                                int64_t n_pad_tail, int W, uint16_t* kall, uint16_t* vt,
+                                int64_t ld, int64_t key0, hipStream_t st) {
+  // rows key0 .. key0 + n_pad_tail of K_all: current chunk then zeros
+  if (n_pad_tail <= 0) return NKV_OK;
+  const int64_t nthreads = n_pad_tail * (W / 8);
+  hipLaunchKernelGGL(k_copy_rows, dim3((unsigned)ceil_div(nthreads, 256)), dim3(256), 0, st, ck,
+                     n_cur, W, kall + key0 * W, n_pad_tail);
+  NKV_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_transpose_v, dim3((unsigned)ceil_div(n_pad_tail, 64), W / 64), dim3(256), 0,
+                     st, cv, n_cur, n_pad_tail, W, vt, ld, key0);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
+}  // namespace nkv

@@ -1,0 +1,23 @@
+// Internal interfaces between the tuned (MFMA) kernels of libnanokv.
+#pragma once
+
+#include "gemm.hpp"
+#include "tuned.hpp"
+
+namespace nkv {
+
+constexpr int FA_KT = 64;     // keys per flash-attention tile (key padding unit)
+constexpr int FA_QB = 128;    // queries per flash-attention block
+
+nkv_status launch_decode_tuned(const BranchArgs& b, int W, int r, int group,
+                               const RangeTable& rows, uint16_t* out, int64_t ld, bool transposed,
+                               hipStream_t st);
+nkv_status launch_stage_current(const uint16_t* ck, const uint16_t* cv, int64_t n_cur,
+                                int64_t n_pad_tail, int W, uint16_t* kall, uint16_t* vt,
+                                int64_t ld, int64_t key0, hipStream_t st);
+// out_f32: write fp32 O [Nq, W] (for merging) instead of bf16
+nkv_status launch_flash(const uint16_t* q, int64_t Nq, int H, float tau, const uint16_t* kall,
+                        const uint16_t* vt, int64_t Nk, int64_t ld, bool out_f32, void* out,
+                        float* lse, hipStream_t st);
+
+}  // namespace nkv
