@@ -58,7 +58,7 @@ static float tau_of(const nkv_shape* s) {
 static bool tuned_applies(const nkv_shape* s, int32_t r_low) {
   if (g_force_generic || !tuned_available()) return false;
   return s->dtype == NKV_BF16 && s->d == 128 && s->r % 32 == 0 &&
-         (r_low == 0 || (r_low % 16 == 0));
+         (r_low == 0 || (r_low % 16 == 0 && r_low <= 128));
 }
 
 // Build FULL / LOW range tables from a route; adjacent same-mode ranges are

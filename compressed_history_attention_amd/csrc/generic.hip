@@ -7,6 +7,8 @@
 // (query, head) row (attention).
 #include <float.h>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 #include "quant.hpp"
 
@@ -194,12 +196,9 @@ __global__ __launch_bounds__(64) void k_low_generic(
   float* ps = qh + d;                    // 64 probabilities
   int* pv = reinterpret_cast<int*>(ps + 64);  // 64 history positions
   const int lane = threadIdx.x;
-  int64_t row = blockIdx.x;
-  if (rows) {
-    if (row >= *nrows) return;
-    row = rows[row];
-  }
-  if (row >= Nq * H) return;
+  const int64_t n_rows = rows ? (int64_t)*nrows : Nq * H;
+  for (int64_t ri = blockIdx.x; ri < n_rows; ri += gridDim.x) {
+  const int64_t row = rows ? (int64_t)rows[ri] : ri;
   const int64_t qi = row / H;
   const int h = (int)(row % H);
   const int W = H * d;
@@ -283,6 +282,8 @@ __global__ __launch_bounds__(64) void k_low_generic(
     o_low[qi * W + h * d + i] = val * inv;
   }
   if (lane == 0) lse_low[qi * H + h] = (l > 0.f) ? m + logf(l) : -INFINITY;
+  __builtin_amdgcn_wave_barrier();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -363,7 +364,8 @@ nkv_status launch_low_generic(int dt, const void* q, int64_t Nq, int H, int d, i
     if (lds > 64 * 1024)
       NKV_HIP_CHECK(hipFuncSetAttribute((const void*)k_low_generic<DT>,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-    hipLaunchKernelGGL(k_low_generic<DT>, dim3((unsigned)max_rows), dim3(64), lds, s, q, Nq, H,
+    const unsigned grid = (unsigned)std::min<int64_t>(max_rows, rows ? 4096 : max_rows);
+    hipLaunchKernelGGL(k_low_generic<DT>, dim3(grid), dim3(64), lds, s, q, Nq, H,
                        d, r, group, r_low, tau, kb, vb, low, rows, nrows, o_low, lse_low);
     NKV_LAUNCH_CHECK();
   });

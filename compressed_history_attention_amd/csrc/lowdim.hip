@@ -1,0 +1,781 @@
+// NanoKV-Fast low-dimensional read on the tuned path (NanoKV pages,
+// Figure 4(d): queries are reduced into coefficient space, scored and
+// accumulated there, and the output dimension is restored before LSE
+// merging; the abstract: the stored coefficients are reused).
+//
+// Per head h and low-routed token t (leading r_low coefficients c):
+//   s = tau (q~_h . c^K_t + T_h[a^K_t]),   T_h[a] = q_h . mu^K_{a,h}
+//   acc_h += p c^V_t,   M_h[a^V_t] += p,   O = (D_{V,h} acc_h + M_h mu^V_h) / sum p
+//
+// Design for CDNA4:
+//  * The coefficients of a token are shared by every head (joint
+//    head-channel coding), so one staged coefficient tile feeds 128 query
+//    rows of a head through MFMA: scores as fp16 MFMA (q~ . c), the
+//    coefficient accumulation as bf16 MFMA (P c^V).
+//  * The per-row center tables T (read) and M (accumulate) have A entries per
+//    row -- too large for LDS at 128 rows.  Low-routed tokens are therefore
+//    counting-sorted into buckets by (a^V range, a^K range) of 64 centers
+//    each; a block walks the buckets in order, keeps only the 64-entry slice
+//    of T (recomputed per bucket by MFMA, q_h . mu^K exact-product bf16) and
+//    of M (flushed to HBM when its a^V range is finished) in LDS, and gathers
+//    / scatter-adds them per score with conflict-free LDS accesses.
+//  * Softmax uses a per-row upper bound B on every score instead of a
+//    running maximum (B = tau (max over present centers of T + |q~| max|c^K|)),
+//    so p = 2^(x - B) <= 1 needs no rescaling of the LDS tables and partial
+//    sums from any split simply add.  Rows whose bound could be loose by
+//    more than 2^60 are recomputed exactly by the generic kernel.
+#include <algorithm>
+
+#include "lowdim.hpp"
+#include "prof.hpp"
+
+namespace nkv {
+
+namespace {
+
+constexpr int NT = 64;        // keys per tile (bucket padding unit)
+constexpr int CR = 64;        // centers per range
+constexpr int RB = 128;       // query rows per block
+constexpr int TS = 65;        // LDS row stride of the center tables (64 + sentinel)
+constexpr int CHUNK = 1024;   // tokens per counting chunk
+constexpr float BOUND_GAP_LIMIT = 60.f;  // log2 units
+
+struct Plan {
+  int64_t n_low = 0, nchunk = 0, max_tiles = 0, max_slots = 0, rows = 0;
+  int GK = 0, GV = 0, NB = 0, rlp = 0, rp = 0, ra = 0, av = 0, avp = 0;
+  // byte offsets inside the low-path workspace
+  size_t dkt, mvt, qt32, qt16, bound, tmax, present, misc, flags, cnt, base, tile_start, bcount,
+      tile_bucket, perm, ck, cvt, koff, voff, acc, wmass, ell, total;
+};
+
+Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& low, int32_t r_low,
+               int64_t Nq) {
+  Plan P;
+  const int64_t W = (int64_t)s->H * s->d;
+  P.n_low = low.total;
+  P.rows = Nq * s->H;
+  P.GK = (int)ceil_div(A_k, CR);
+  P.GV = (int)ceil_div(A_v, CR);
+  P.NB = P.GK * P.GV;
+  P.nchunk = ceil_div(P.n_low, CHUNK);
+  P.max_tiles = ceil_div(P.n_low, NT) + P.NB;
+  P.max_slots = P.max_tiles * NT;
+  P.rlp = (int)ceil_div(r_low, 16) * 16;
+  P.rp = (int)ceil_div(r_low, 32) * 32;
+  P.ra = P.rp;
+  P.av = (int)ceil_div(A_v, 32) * 32;
+  P.avp = P.av;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  P.dkt = take(sizeof(uint16_t) * r_low * W);
+  P.mvt = take(sizeof(uint16_t) * W * P.avp);
+  P.qt32 = take(sizeof(float) * P.rows * r_low);
+  P.qt16 = take(sizeof(uint16_t) * P.rows * P.rlp);
+  P.bound = take(sizeof(float) * P.rows);
+  P.tmax = take(sizeof(uint32_t) * P.rows);
+  P.present = take(sizeof(uint32_t) * A_k);
+  P.misc = take(sizeof(uint32_t) * 4);
+  P.flags = take(sizeof(int32_t) * P.rows);
+  P.cnt = take(sizeof(int32_t) * P.nchunk * P.NB);
+  P.base = take(sizeof(int32_t) * P.nchunk * P.NB);
+  P.tile_start = take(sizeof(int32_t) * (P.NB + 1));
+  P.bcount = take(sizeof(int32_t) * P.NB);
+  P.tile_bucket = take(sizeof(int32_t) * P.max_tiles);
+  P.perm = take(sizeof(int32_t) * P.max_slots);
+  P.ck = take(sizeof(uint16_t) * P.max_slots * P.rlp);
+  P.cvt = take(sizeof(uint16_t) * P.max_tiles * P.rp * NT);
+  P.koff = take(sizeof(int32_t) * P.max_slots);
+  P.voff = take(sizeof(int32_t) * P.max_slots);
+  P.acc = take(sizeof(float) * P.rows * r_low);
+  P.wmass = take(sizeof(float) * P.rows * A_v);
+  P.ell = take(sizeof(float) * P.rows);
+  P.total = off;
+  return P;
+}
+
+// ---------------------------------------------------------------------------
+// preparation kernels
+// ---------------------------------------------------------------------------
+__global__ void k_zero_u32(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// dst[c][r] = src[r][c] for r < R, c < C (bf16); dst row stride ldd (zero pad
+// for r in [R, ldd) when pad_zero).
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int R,
+                                                        int C, int lds, uint16_t* __restrict__ dst,
+                                                        int ldd) {
+  __shared__ uint16_t tile[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i / 64, cc = i % 64;
+    tile[rr][cc] = (r0 + rr < R && c0 + cc < C) ? src[(int64_t)(r0 + rr) * lds + c0 + cc] : 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, rr = i % 64;
+    if (c0 + cc < C && r0 + rr < ldd) dst[(int64_t)(c0 + cc) * ldd + r0 + rr] = tile[rr][cc];
+  }
+}
+
+__device__ __forceinline__ int bucket_of(const BranchArgs& kb, const BranchArgs& vb, int64_t t,
+                                         int GK) {
+  return (vb.idx[t] / CR) * GK + kb.idx[t] / CR;
+}
+
+__global__ __launch_bounds__(256) void k_bucket_count(BranchArgs kb, BranchArgs vb, RangeTable low,
+                                                      int GK, int NB, int32_t* __restrict__ cnt,
+                                                      uint32_t* __restrict__ present) {
+  extern __shared__ int lc[];
+  for (int b = threadIdx.x; b < NB; b += 256) lc[b] = 0;
+  __syncthreads();
+  const int64_t j0 = (int64_t)blockIdx.x * CHUNK;
+  for (int i = threadIdx.x; i < CHUNK; i += 256) {
+    const int64_t j = j0 + i;
+    if (j < low.total) {
+      const int64_t t = map_index(low, j);
+      atomicAdd(&lc[bucket_of(kb, vb, t, GK)], 1);
+      present[kb.idx[t]] = 1u;
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < NB; b += 256) cnt[(int64_t)blockIdx.x * NB + b] = lc[b];
+}
+
+// one block: bucket totals, padded tile ranges, per-chunk bases, tile->bucket
+__global__ __launch_bounds__(1024) void k_bucket_scan(const int32_t* __restrict__ cnt, int nchunk,
+                                                      int NB, int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ tile_start,
+                                                      int32_t* __restrict__ bcount,
+                                                      int32_t* __restrict__ tile_bucket) {
+  extern __shared__ int sh[];   // NB tiles per bucket, then 1024 partial sums
+  int* ntile = sh;
+  int* part = sh + NB;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < NB; b += 1024) {
+    int tot = 0;
+    for (int c = 0; c < nchunk; ++c) tot += cnt[(int64_t)c * NB + b];
+    bcount[b] = tot;
+    ntile[b] = (tot + NT - 1) / NT;
+  }
+  __syncthreads();
+  const int per = (NB + 1023) / 1024;
+  const int lo = tid * per, hi = min(NB, lo + per);
+  int sum = 0;
+  for (int b = lo; b < hi; ++b) sum += ntile[b];
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    tile_start[NB] = run;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int b = lo; b < hi; ++b) {
+    const int nt = ntile[b];
+    tile_start[b] = run;
+    for (int k = 0; k < nt; ++k) tile_bucket[run + k] = b;
+    int acc = run * NT;
+    for (int c = 0; c < nchunk; ++c) {
+      base[(int64_t)c * NB + b] = acc;
+      acc += cnt[(int64_t)c * NB + b];
+    }
+    run += nt;
+  }
+}
+
+// stable scatter: slot = base[chunk][bucket] + rank of the token among the
+// chunk's earlier tokens of the same bucket
+__global__ __launch_bounds__(256) void k_bucket_scatter(BranchArgs kb, BranchArgs vb, RangeTable low,
+                                                        int GK, int NB,
+                                                        const int32_t* __restrict__ base,
+                                                        int32_t* __restrict__ perm) {
+  __shared__ int bid[CHUNK];
+  const int64_t j0 = (int64_t)blockIdx.x * CHUNK;
+  const int n = (int)min<int64_t>(CHUNK, low.total - j0);
+  for (int i = threadIdx.x; i < n; i += 256) bid[i] = bucket_of(kb, vb, map_index(low, j0 + i), GK);
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int b = bid[i];
+    int rank = 0;
+    for (int k = 0; k < i; ++k) rank += (bid[k] == b);
+    perm[base[(int64_t)blockIdx.x * NB + b] + rank] = (int32_t)map_index(low, j0 + i);
+  }
+}
+
+// one thread per padded slot: dequantised K coefficients (fp16 rows), V
+// coefficients (bf16, per-tile transposed), table offsets, max |c^K|^2
+__global__ __launch_bounds__(256) void k_build_tiles(
+    BranchArgs kb, BranchArgs vb, int r, int group, int r_low, int rlp, int rp,
+    const int32_t* __restrict__ tile_start, const int32_t* __restrict__ tile_bucket,
+    const int32_t* __restrict__ bcount, int NB, const int32_t* __restrict__ perm,
+    uint16_t* __restrict__ ck, uint16_t* __restrict__ cvt, int32_t* __restrict__ koff,
+    int32_t* __restrict__ voff, uint32_t* __restrict__ cmax2) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nslots = (int64_t)tile_start[NB] * NT;
+  if (p >= nslots) return;
+  const int64_t tile = p / NT;
+  const int key = (int)(p - tile * NT);
+  const int b = tile_bucket[tile];
+  const bool real = (p - (int64_t)tile_start[b] * NT) < bcount[b];
+  uint16_t* ckrow = ck + p * rlp;
+  uint16_t* cvcol = cvt + tile * rp * NT + key;
+  if (!real) {
+    for (int j = 0; j < rlp; j += 8) *reinterpret_cast<u32x4*>(ckrow + j) = u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < rp; ++j) cvcol[j * NT] = 0;
+    koff[p] = CR * 4;
+    voff[p] = CR * 4;
+    return;
+  }
+  const int64_t t = perm[p];
+  const uint8_t* kc = kb.codes + t * (r / 2);
+  const uint16_t* ks = kb.scales + t * (r / group);
+  const uint8_t* vc = vb.codes + t * (r / 2);
+  const uint16_t* vs = vb.scales + t * (r / group);
+  float n2 = 0.f;
+  for (int j = 0; j < rlp; j += 2) {
+    float v0 = 0.f, v1 = 0.f;
+    if (j < r_low) {
+      v0 = (float)code_at(kc, j) * fp16_bits_to_f32(ks[j / group]);
+      v1 = (float)code_at(kc, j + 1) * fp16_bits_to_f32(ks[(j + 1) / group]);
+    }
+    n2 = fmaf(v0, v0, fmaf(v1, v1, n2));
+    *reinterpret_cast<uint32_t*>(ckrow + j) = pack_f16x2(v0, v1);
+  }
+  for (int j = 0; j < rp; ++j) {
+    const float v = (j < r_low) ? (float)code_at(vc, j) * fp16_bits_to_f32(vs[j / group]) : 0.f;
+    cvcol[j * NT] = f32_to_bf16_bits(v);
+  }
+  koff[p] = (kb.idx[t] % CR) * 4;
+  voff[p] = (vb.idx[t] % CR) * 4;
+  atomicMax(cmax2, ordered_bits(n2));
+}
+
+// q~ = per-head Q_h D_{K,h}[:, :r_low]  (rows = queries, cols = coefficients)
+struct QtProblem {
+  int M, N, K;  // Nq, r_low, 128
+  int H;
+  const uint16_t* q;
+  const uint16_t* dkt;  // [r_low, W]
+  float* qt32;          // [Nq*H, r_low]
+  __device__ u32x4 load_a(int z, int m, int k) const {
+    if (m >= M) return u32x4{0u, 0u, 0u, 0u};
+    return ld_u32x4(q + (int64_t)m * H * 128 + z * 128 + k);
+  }
+  __device__ u32x4 load_b(int z, int n, int k) const {
+    if (n >= N) return u32x4{0u, 0u, 0u, 0u};
+    return ld_u32x4(dkt + (int64_t)n * H * 128 + z * 128 + k);
+  }
+  __device__ void epilogue(int z, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + 32 * i + acc_row(e, lane), n = n0 + 32 * j + (lane & 31);
+          if (m < M && n < N) qt32[((int64_t)m * H + z) * N + n] = acc[i][j][e];
+        }
+  }
+};
+
+// max over centers present in the low set of q_h . mu^K_{a,h}
+// (rows = centers, cols = queries)
+struct TmaxProblem {
+  int M, N, K;  // A_k, Nq, 128
+  int H;
+  const uint16_t* muk;
+  const uint16_t* q;
+  const uint32_t* present;
+  uint32_t* tmax;  // [Nq*H] ordered bits
+  __device__ u32x4 load_a(int z, int m, int k) const {
+    if (m >= M) return u32x4{0u, 0u, 0u, 0u};
+    return ld_u32x4(muk + (int64_t)m * H * 128 + z * 128 + k);
+  }
+  __device__ u32x4 load_b(int z, int n, int k) const {
+    if (n >= N) return u32x4{0u, 0u, 0u, 0u};
+    return ld_u32x4(q + (int64_t)n * H * 128 + z * 128 + k);
+  }
+  __device__ void epilogue(int z, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float best = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + 32 * i + acc_row(e, lane);
+          if (m < M && present[m]) best = fmaxf(best, acc[i][j][e]);
+        }
+      best = fmaxf(best, __shfl_xor(best, 32, 64));
+      const int n = n0 + 32 * j + (lane & 31);
+      if (lane < 32 && n < N && best > -INFINITY)
+        atomicMax(tmax + (int64_t)n * H + z, ordered_bits(best));
+    }
+  }
+};
+
+// per-row bound, fp16 q~, and the list of rows needing the exact fallback
+__global__ void k_row_bound(const float* __restrict__ qt32, int64_t rows, int r_low, int rlp,
+                            float c, const uint32_t* __restrict__ tmax,
+                            const uint32_t* __restrict__ misc, float* __restrict__ bound,
+                            uint16_t* __restrict__ qt16, int32_t* __restrict__ flags,
+                            int32_t* __restrict__ nflag) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  const float cmax = sqrtf(from_ordered_bits(misc[0]));
+  const float* qr = qt32 + row * r_low;
+  float n2 = 0.f, amax = 0.f;
+  for (int j = 0; j < r_low; ++j) {
+    n2 = fmaf(qr[j], qr[j], n2);
+    amax = fmaxf(amax, fabsf(qr[j]));
+  }
+  const float qn = sqrtf(n2);
+  const float T = from_ordered_bits(tmax[row]);
+  const float B = c * (T + 1e-5f * fabsf(T) + 1.001f * qn * cmax) + 1e-3f;
+  bound[row] = B;
+  const bool bad = !(2.f * c * qn * cmax <= BOUND_GAP_LIMIT) || !(amax < 30000.f) ||
+                   !(cmax < 30000.f) || !(fabsf(B) < 1e30f);
+  if (bad) flags[atomicAdd(nflag, 1)] = (int32_t)row;
+  uint16_t* o = qt16 + row * rlp;
+  for (int j = 0; j < rlp; j += 2) {
+    const float a = j < r_low ? qr[j] : 0.f, b = j + 1 < r_low ? qr[j + 1] : 0.f;
+    *reinterpret_cast<uint32_t*>(o + j) = pack_f16x2(a, b);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the main low-dimensional kernel
+// ---------------------------------------------------------------------------
+struct MainArgs {
+  const uint16_t* q;
+  const uint16_t* muk;
+  const uint16_t* qt16;
+  const float* bound;
+  const uint16_t* ck;
+  const uint16_t* cvt;
+  const int32_t* koff;
+  const int32_t* voff;
+  const int32_t* tile_start;
+  const int32_t* bcount;
+  float* acc;
+  float* wmass;
+  float* ell;
+  int64_t Nq;
+  int H, A_k, A_v, GK, GV, r_low;
+  float c;
+};
+
+template <int RLP>
+__global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
+  constexpr int RP = (RLP + 31) / 32 * 32;   // coefficient rows of the V tile
+  constexpr int NPB = RP / 32;               // 32-wide coefficient blocks
+  constexpr int CKS = RLP + 8;               // LDS row stride of the K tile (fp16)
+  constexpr int CVS = 68;                    // LDS row stride of the V tile (bf16)
+  constexpr int CKC = NT * RLP / 8;          // 16-byte chunks per K tile
+  constexpr int CVC = RP * NT / 8;           // 16-byte chunks per V tile
+  constexpr int NCH = CKC + CVC + 32;        // + key/value offsets
+  constexpr int PER = (NCH + 511) / 512;
+  __shared__ __attribute__((aligned(16))) float sTW[2 * RB * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t sCK[2][NT * CKS];
+  __shared__ __attribute__((aligned(16))) uint16_t sCV[2][RP * CVS];
+  __shared__ __attribute__((aligned(16))) int32_t sOff[2][2 * NT];
+  __shared__ float sEll[RB];
+  float* sT = sTW;
+  float* sW = sTW + RB * TS;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+  const int rg = wave & 3, kh = wave >> 2;
+  const int h = blockIdx.y;
+  const int W = a.H * 128;
+  const int rloc = rg * 32 + (lane & 31);
+  const int64_t qrow = (int64_t)blockIdx.x * RB + rloc;
+  const bool rok = qrow < a.Nq;
+  const int64_t grow = qrow * a.H + h;
+
+  // per-lane operands
+  bf16x8 qh[8];
+  f16x8 qtf[RLP / 16];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    qh[ks] = rok ? as_bf16x8(ld_u32x4(a.q + qrow * W + h * 128 + 16 * ks + 8 * hl))
+                 : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+  for (int ks = 0; ks < RLP / 16; ++ks)
+    qtf[ks] = rok ? as_f16x8(ld_u32x4(a.qt16 + grow * RLP + 16 * ks + 8 * hl))
+                  : as_f16x8(u32x4{0u, 0u, 0u, 0u});
+  const float Bq = rok ? a.bound[grow] : 0.f;
+  f32x16 accT[NPB];
+#pragma unroll
+  for (int i = 0; i < NPB; ++i) accT[i] = zero16();
+
+  for (int i = tid; i < RB * TS; i += 512) sW[i] = 0.f;
+  if (tid < RB) sEll[tid] = 0.f;
+
+  u32x4 stg[PER];
+  auto fetch = [&](int64_t tile) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int cidx = tid + 512 * u;
+      if (cidx < CKC) {
+        stg[u] = ld_u32x4(a.ck + tile * NT * RLP + cidx * 8);
+      } else if (cidx < CKC + CVC) {
+        stg[u] = ld_u32x4(a.cvt + tile * RP * NT + (cidx - CKC) * 8);
+      } else if (cidx < NCH) {
+        const int o = cidx - CKC - CVC;  // 0..15 key offsets, 16..31 value offsets
+        const int32_t* src = (o < 16) ? a.koff : a.voff;
+        stg[u] = ld_u32x4(src + tile * NT + (o & 15) * 4);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int cidx = tid + 512 * u;
+      if (cidx < CKC) {
+        const int row = cidx / (RLP / 8), col = (cidx % (RLP / 8)) * 8;
+        *reinterpret_cast<u32x4*>(&sCK[buf][row * CKS + col]) = stg[u];
+      } else if (cidx < CKC + CVC) {
+        const int ci = cidx - CKC;
+        const int row = ci / 8, col = (ci % 8) * 8;
+        *reinterpret_cast<u32x2*>(&sCV[buf][row * CVS + col]) = u32x2{stg[u][0], stg[u][1]};
+        *reinterpret_cast<u32x2*>(&sCV[buf][row * CVS + col + 4]) = u32x2{stg[u][2], stg[u][3]};
+      } else if (cidx < NCH) {
+        const int o = cidx - CKC - CVC;
+        *reinterpret_cast<u32x4*>(&sOff[buf][(o >> 4) * NT + (o & 15) * 4]) = stg[u];
+      }
+    }
+  };
+
+  const char* sTrow = reinterpret_cast<const char*>(sT + rloc * TS);
+  float* sWrow = sW + rloc * TS;
+  __syncthreads();
+
+  for (int gv = 0; gv < a.GV; ++gv) {
+    for (int gk = 0; gk < a.GK; ++gk) {
+      const int b = gv * a.GK + gk;
+      const int cnt = a.bcount[b];
+      if (cnt == 0) continue;
+      const int64_t t0 = a.tile_start[b];
+      const int nt = a.tile_start[b + 1] - (int)t0;
+      // ---- T slice: T^T[center][row] = mu^K_{center,h} . q_h (exact products)
+      {
+        f32x16 tt = zero16();
+        const int cen = gk * CR + kh * 32 + (lane & 31);
+        const bool cok = cen < a.A_k;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 m = cok ? as_bf16x8(ld_u32x4(a.muk + (int64_t)cen * W + h * 128 + 16 * ks + 8 * hl))
+                               : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+          tt = mfma_bf16(m, qh[ks], tt);
+        }
+        fetch(t0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int cl = kh * 32 + acc_row(e, lane);
+          sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[e], a.c, -Bq) : -INFINITY;
+        }
+        if (kh == 0 && hl == 0) sT[rloc * TS + CR] = -INFINITY;
+        stash(0);
+      }
+      __syncthreads();
+      for (int it = 0; it < nt; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < nt) fetch(t0 + it + 1);
+        const int real = min(NT, cnt - it * NT);
+        if (kh * 32 < real) {
+          // ---- scores S^T[key][row] = c^K . q~ (fp16 MFMA) ----------------
+          f32x16 s = zero16();
+#pragma unroll
+          for (int ks = 0; ks < RLP / 16; ++ks) {
+            const f16x8 ca = as_f16x8(*reinterpret_cast<const u32x4*>(
+                &sCK[buf][(kh * 32 + (lane & 31)) * CKS + 16 * ks + 8 * hl]));
+            s = mfma_f16(ca, qtf[ks], s);
+          }
+          // ---- p = 2^(c s + c T - B); center-mass scatter ------------------
+          float p[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int key = kh * 32 + g * 8 + hl * 4;
+            const int32_t* ko = &sOff[buf][key];
+            const int32_t* vo = &sOff[buf][NT + key];
+            const u32x4 kov = *reinterpret_cast<const u32x4*>(ko);
+            const u32x4 vov = *reinterpret_cast<const u32x4*>(vo);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float tv = *reinterpret_cast<const float*>(sTrow + kov[u]);
+              const float x = fmaf(s[4 * g + u], a.c, tv);
+              const float pv = __builtin_amdgcn_exp2f(x);
+              p[4 * g + u] = pv;
+              atomicAdd(reinterpret_cast<float*>(reinterpret_cast<char*>(sWrow) + vov[u]), pv);
+            }
+          }
+          // ---- acc^T[coef][row] += c^V^T P^T (bf16 MFMA) --------------------
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            u32x4 pk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(p[8 * j + 2 * u], p[8 * j + 2 * u + 1]);
+            const bf16x8 pb = as_bf16x8(pk);
+#pragma unroll
+            for (int db = 0; db < NPB; ++db) {
+              const uint16_t* vrow = &sCV[buf][(db * 32 + (lane & 31)) * CVS + kh * 32 + 16 * j + 4 * hl];
+              const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+              const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+              accT[db] = mfma_bf16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, accT[db]);
+            }
+          }
+        }
+        if (it + 1 < nt) stash(buf ^ 1);
+        __syncthreads();
+      }
+    }
+    // ---- flush the finished a^V range of the center masses ------------------
+    {
+      const int row = tid >> 2, part = tid & 3;
+      const int64_t q = (int64_t)blockIdx.x * RB + row;
+      float* src = sW + row * TS + part * 16;
+      float sum = 0.f;
+      float* dst = a.wmass + (q * a.H + h) * a.A_v + gv * CR + part * 16;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float v = src[i];
+        sum += v;
+        if (q < a.Nq && gv * CR + part * 16 + i < a.A_v) dst[i] = v;
+        src[i] = 0.f;
+      }
+      sum += __shfl_xor(sum, 1, 64);
+      sum += __shfl_xor(sum, 2, 64);
+      if (part == 0) {
+        sEll[row] += sum;
+        sW[row * TS + CR] = 0.f;
+      }
+    }
+    __syncthreads();
+  }
+  // ---- combine the two key halves' coefficient sums ---------------------------
+  float* red = sTW;  // RB x (RP + 1) floats
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < NPB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[rloc * (RP + 1) + db * 32 + acc_row(e, lane)] = accT[db][e];
+  }
+  __syncthreads();
+  if (kh == 0 && rok) {
+#pragma unroll
+    for (int db = 0; db < NPB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int dim = db * 32 + acc_row(e, lane);
+        if (dim < a.r_low)
+          a.acc[grow * a.r_low + dim] = accT[db][e] + red[rloc * (RP + 1) + dim];
+      }
+  }
+  if (tid < RB) {
+    const int64_t q = (int64_t)blockIdx.x * RB + tid;
+    if (q < a.Nq) a.ell[q * a.H + h] = sEll[tid];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// restoration: O_low = (D_{V,h} acc + M mu^V_h) / ell,  LSE = (B + log2 ell) ln 2
+// GEMM over K = [acc hi | acc lo | M hi | M lo] (fp32 split into bf16 pairs)
+// ---------------------------------------------------------------------------
+struct RestoreProblem {
+  int M, N, K;  // Nq, 128, 2 ra + 2 av
+  int H, r, r_low, ra, A_v, av;
+  const float* acc;
+  const float* wmass;
+  const uint16_t* dv;    // [W, r]
+  const uint16_t* mvt;   // [W, av]
+  const float* ell;
+  const float* bound;
+  float* o_low;
+  float* lse_low;
+  __device__ u32x4 load_a(int z, int m, int k) const {
+    if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    const int64_t row = (int64_t)m * H + z;
+    float v[8];
+    bool lo;
+    if (k < 2 * ra) {
+      lo = k >= ra;
+      const int j = lo ? k - ra : k;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (j + i < r_low) ? acc[row * r_low + j + i] : 0.f;
+    } else {
+      const int kk = k - 2 * ra;
+      lo = kk >= av;
+      const int c = lo ? kk - av : kk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (c + i < A_v) ? wmass[row * A_v + c + i] : 0.f;
+    }
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x0 = v[2 * i], x1 = v[2 * i + 1];
+      if (lo) {
+        x0 -= (float)(__bf16)x0;
+        x1 -= (float)(__bf16)x1;
+      }
+      out[i] = pack_bf16x2(x0, x1);
+    }
+    return out;
+  }
+  __device__ u32x4 load_b(int z, int n, int k) const {
+    if (n >= N || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    const int64_t ch = (int64_t)z * 128 + n;
+    if (k < 2 * ra) {
+      const int j = k >= ra ? k - ra : k;
+      if (j >= r_low) return u32x4{0u, 0u, 0u, 0u};
+      return ld_u32x4(dv + ch * r + j);
+    }
+    const int kk = k - 2 * ra;
+    const int c = kk >= av ? kk - av : kk;
+    return ld_u32x4(mvt + ch * av + c);
+  }
+  __device__ void epilogue(int z, int m0, int n0, int lane, const f32x16 (&accv)[2][2]) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * i + acc_row(e, lane);
+        if (m >= M) continue;
+        const int64_t row = (int64_t)m * H + z;
+        const float l = ell[row];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + 32 * j + (lane & 31);
+          if (n < N) o_low[(int64_t)m * H * 128 + z * 128 + n] = accv[i][j][e] * inv;
+          if (n == 0)
+            lse_low[row] = l > 0.f ? (bound[row] + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+        }
+      }
+  }
+};
+
+template <int RLP>
+nkv_status launch_main(const MainArgs& m, int64_t Nq, int H, hipStream_t st) {
+  dim3 grid((unsigned)ceil_div(Nq, RB), (unsigned)H);
+  hipLaunchKernelGGL(k_low_main<RLP>, grid, dim3(512), 0, st, m);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
+}  // namespace
+
+size_t low_workspace_bytes(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& low,
+                           int32_t r_low, int64_t Nq) {
+  return make_plan(s, A_k, A_v, low, r_low, Nq).total;
+}
+
+nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
+                      const RangeTable& low, int32_t r_low, float tau, const uint16_t* q,
+                      int64_t Nq, float* o_low, float* lse_low, char* ws, hipStream_t st) {
+  const Plan P = make_plan(s, kb.A, vb.A, low, r_low, Nq);
+  const int H = s->H, W = H * s->d, r = s->r;
+  const float c = tau * 1.4426950408889634f;
+  auto at = [&](size_t off) { return ws + off; };
+  uint16_t* dkt = reinterpret_cast<uint16_t*>(at(P.dkt));
+  uint16_t* mvt = reinterpret_cast<uint16_t*>(at(P.mvt));
+  float* qt32 = reinterpret_cast<float*>(at(P.qt32));
+  uint16_t* qt16 = reinterpret_cast<uint16_t*>(at(P.qt16));
+  float* bound = reinterpret_cast<float*>(at(P.bound));
+  uint32_t* tmax = reinterpret_cast<uint32_t*>(at(P.tmax));
+  uint32_t* present = reinterpret_cast<uint32_t*>(at(P.present));
+  uint32_t* misc = reinterpret_cast<uint32_t*>(at(P.misc));
+  int32_t* flags = reinterpret_cast<int32_t*>(at(P.flags));
+  int32_t* cnt = reinterpret_cast<int32_t*>(at(P.cnt));
+  int32_t* base = reinterpret_cast<int32_t*>(at(P.base));
+  int32_t* tile_start = reinterpret_cast<int32_t*>(at(P.tile_start));
+  int32_t* bcount = reinterpret_cast<int32_t*>(at(P.bcount));
+  int32_t* tile_bucket = reinterpret_cast<int32_t*>(at(P.tile_bucket));
+  int32_t* perm = reinterpret_cast<int32_t*>(at(P.perm));
+  uint16_t* ck = reinterpret_cast<uint16_t*>(at(P.ck));
+  uint16_t* cvt = reinterpret_cast<uint16_t*>(at(P.cvt));
+  int32_t* koff = reinterpret_cast<int32_t*>(at(P.koff));
+  int32_t* voff = reinterpret_cast<int32_t*>(at(P.voff));
+  float* acc = reinterpret_cast<float*>(at(P.acc));
+  float* wmass = reinterpret_cast<float*>(at(P.wmass));
+  float* ell = reinterpret_cast<float*>(at(P.ell));
+  nkv_status e;
+  {
+  ProfScope ps_prep("low_prep", st);
+
+  // zero the counters, presence flags and row maxima (kernels: capturable)
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(P.rows, 256)), dim3(256), 0, st, tmax, P.rows);
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(kb.A, 256)), dim3(256), 0, st, present, (int64_t)kb.A);
+  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, st, misc, (int64_t)4);
+  NKV_LAUNCH_CHECK();
+  // transposed decoder rows for the query reduction, transposed V centers
+  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(W, 64), (unsigned)ceil_div(r_low, 64)),
+                     dim3(256), 0, st, static_cast<const uint16_t*>(kb.decoder), W, r_low, r, dkt, W);
+  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(P.avp, 64), (unsigned)ceil_div(W, 64)),
+                     dim3(256), 0, st, static_cast<const uint16_t*>(vb.centers), vb.A, W, W, mvt,
+                     P.avp);
+  NKV_LAUNCH_CHECK();
+  // bucket sort of the low-routed tokens
+  const int nch = (int)P.nchunk;
+  hipLaunchKernelGGL(k_bucket_count, dim3(nch), dim3(256), P.NB * sizeof(int), st, kb, vb, low,
+                     P.GK, P.NB, cnt, present);
+  hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), (P.NB + 1024) * sizeof(int), st, cnt, nch,
+                     P.NB, base, tile_start, bcount, tile_bucket);
+  hipLaunchKernelGGL(k_bucket_scatter, dim3(nch), dim3(256), 0, st, kb, vb, low, P.GK, P.NB, base,
+                     perm);
+  hipLaunchKernelGGL(k_build_tiles, dim3((unsigned)ceil_div(P.max_slots, 256)), dim3(256), 0, st,
+                     kb, vb, r, s->group, r_low, P.rlp, P.rp, tile_start, tile_bucket, bcount, P.NB,
+                     perm, ck, cvt, koff, voff, misc);
+  NKV_LAUNCH_CHECK();
+  // query reduction and per-row score bounds
+  QtProblem qp{(int)Nq, r_low, 128, H, q, dkt, qt32};
+  if ((e = launch_gemm(qp, H, st))) return e;
+  TmaxProblem tp{kb.A, (int)Nq, 128, H, static_cast<const uint16_t*>(kb.centers), q, present, tmax};
+  if ((e = launch_gemm(tp, H, st))) return e;
+  hipLaunchKernelGGL(k_row_bound, dim3((unsigned)ceil_div(P.rows, 256)), dim3(256), 0, st, qt32,
+                     P.rows, r_low, P.rlp, c, tmax, misc, bound, qt16, flags,
+                     reinterpret_cast<int32_t*>(misc + 1));
+  NKV_LAUNCH_CHECK();
+  }
+  // main pass
+  {
+  ProfScope ps_main("low_main", st);
+  MainArgs m{q, static_cast<const uint16_t*>(kb.centers), qt16, bound, ck, cvt, koff, voff,
+             tile_start, bcount, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.GV, r_low, c};
+  switch (P.rlp) {
+    case 16: e = launch_main<16>(m, Nq, H, st); break;
+    case 32: e = launch_main<32>(m, Nq, H, st); break;
+    case 48: e = launch_main<48>(m, Nq, H, st); break;
+    case 64: e = launch_main<64>(m, Nq, H, st); break;
+    case 80: e = launch_main<80>(m, Nq, H, st); break;
+    case 96: e = launch_main<96>(m, Nq, H, st); break;
+    case 112: e = launch_main<112>(m, Nq, H, st); break;
+    case 128: e = launch_main<128>(m, Nq, H, st); break;
+    default: set_error("tuned low-dimensional read supports r_low <= 128"); return NKV_EUNSUPPORTED;
+  }
+  if (e) return e;
+  }
+  // restoration
+  {
+  ProfScope ps_restore("low_restore", st);
+  RestoreProblem rp{(int)Nq, 128, 2 * P.ra + 2 * P.av, H, r, r_low, P.ra, vb.A, P.av, acc, wmass,
+                    static_cast<const uint16_t*>(vb.decoder), mvt, ell, bound, o_low, lse_low};
+  if ((e = launch_gemm(rp, H, st))) return e;
+  }
+  // rows whose bound may be loose: exact generic recomputation
+  ProfScope ps_fallback("low_fallback", st);
+  return launch_low_generic(NKV_BF16, q, Nq, H, s->d, r, s->group, r_low, tau, kb, vb, low, flags,
+                            reinterpret_cast<int32_t*>(misc + 1), P.rows, o_low, lse_low, st);
+}
+
+}  // namespace nkv

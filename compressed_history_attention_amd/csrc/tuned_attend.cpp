@@ -1,7 +1,8 @@
 // Orchestration of the tuned (MFMA) attention path: workspace layout and the
 // sequence of kernels for the full-dimensional and the Fast reads.
-#include "tuned_internal.hpp"
 #include "lowdim.hpp"
+#include "prof.hpp"
+#include "tuned_internal.hpp"
 
 namespace nkv {
 
@@ -57,21 +58,33 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
   uint16_t* kall = reinterpret_cast<uint16_t*>(ws + L.kall);
   uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
   nkv_status e;
-  if ((e = launch_decode_tuned(kb, W, s->r, s->group, full, kall, 0, false, st))) return e;
-  if ((e = launch_decode_tuned(vb, W, s->r, s->group, full, vt, L.nk_pad, true, st))) return e;
-  if ((e = launch_stage_current(static_cast<const uint16_t*>(cur_k),
-                                static_cast<const uint16_t*>(cur_v), N_cur, L.nk_pad - full.total,
-                                W, kall, vt, L.nk_pad, full.total, st)))
-    return e;
+  {
+    ProfScope ps("decode", st);
+    if ((e = launch_decode_tuned(kb, W, s->r, s->group, full, kall, 0, false, st))) return e;
+    if ((e = launch_decode_tuned(vb, W, s->r, s->group, full, vt, L.nk_pad, true, st))) return e;
+  }
+  {
+    ProfScope ps("stage_current", st);
+    if ((e = launch_stage_current(static_cast<const uint16_t*>(cur_k),
+                                  static_cast<const uint16_t*>(cur_v), N_cur,
+                                  L.nk_pad - full.total, W, kall, vt, L.nk_pad, full.total, st)))
+      return e;
+  }
   const uint16_t* qb = static_cast<const uint16_t*>(q);
-  if (low.total == 0)
+  if (low.total == 0) {
+    ProfScope ps("flash", st);
     return launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, false, out, lse, st);
+  }
   float* of = reinterpret_cast<float*>(ws + L.o_full);
   float* lf = reinterpret_cast<float*>(ws + L.lse_full);
   float* ol = reinterpret_cast<float*>(ws + L.o_low);
   float* ll = reinterpret_cast<float*>(ws + L.lse_low);
-  if ((e = launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, st))) return e;
+  {
+    ProfScope ps("flash", st);
+    if ((e = launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, st))) return e;
+  }
   if ((e = launch_low(s, kb, vb, low, r_low, tau, qb, Nq, ol, ll, ws + L.low, st))) return e;
+  ProfScope ps("merge", st);
   return launch_lse_merge(Nq, H, s->d, of, lf, ol, ll, out, NKV_BF16, lse, st);
 }
 

@@ -14,6 +14,7 @@
 // Decoder (Figure 4(b)): x_hat = mu_a + D (code * scale) as a GEMM whose A
 // loader dequantises INT4 on the fly and whose epilogue adds the center and
 // writes bf16 rows (K) or per-head transposed columns (V).
+#include "prof.hpp"
 #include "quant.hpp"
 #include "tuned_internal.hpp"
 
@@ -172,18 +173,25 @@ nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void
   float* z = reinterpret_cast<float*>(ws + off);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* mub = static_cast<const uint16_t*>(centers);
+  nkv_status e;
+  {
+  ProfScope ps("encode_assign", st);
   hipLaunchKernelGGL(k_center_norms, dim3(A), dim3(64), 0, st, mub, A, W, mu2);
   NKV_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N,
                      ~0ull);
   NKV_LAUNCH_CHECK();
   DistProblem dp{A, (int)N, W, mub, xb, mu2, keys};
-  nkv_status e = launch_gemm(dp, 1, st);
-  if (e) return e;
+  if ((e = launch_gemm(dp, 1, st))) return e;
   hipLaunchKernelGGL(k_unpack_idx, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N, idx);
   NKV_LAUNCH_CHECK();
+  }
+  {
+  ProfScope ps("encode_project", st);
   ProjProblem pp{(int)N, r, 3 * W, W, xb, mub, idx, static_cast<const uint16_t*>(enc), z};
   if ((e = launch_gemm(pp, 1, st))) return e;
+  }
+  ProfScope ps("encode_quantize", st);
   const int64_t ng = N * (r / s->group);
   hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)ceil_div(ng, 256)), dim3(256), 0, st, z, N,
                      r, s->group, codes, scales);

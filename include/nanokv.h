@@ -182,6 +182,20 @@ int nkv_version(void);
  * where the tuned MFMA kernels apply; 0 (default) restores the dispatch. */
 void nkv_force_generic(int on);
 
+/* Profiling aid (not thread-safe).  While enabled, each kernel stage of the
+ * tuned path is bracketed by HIP events recorded on the call's stream.
+ * nkv_profile_read waits for the recorded events, writes up to max_entries
+ * per-stage totals (elapsed milliseconds and number of launches) and clears
+ * them; it returns the number of stages written, or -1 on a HIP error. */
+typedef struct {
+  char name[32];
+  double ms;
+  int32_t count;
+} nkv_prof_entry;
+
+void nkv_profile_enable(int on);
+int nkv_profile_read(nkv_prof_entry* out, int32_t max_entries);
+
 #ifdef __cplusplus
 }
 #endif
