@@ -181,9 +181,9 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
   const size_t need = nkv_attend_workspace_size(shape, k->A, v->A, N_hist, fast ? route : nullptr,
                                                 fast ? n_seg : 0, r_low, Nq, N_cur);
   if (need == SIZE_MAX) return NKV_EINVAL;
+  if (Nq == 0) return NKV_OK;
   if (need > 0 && (!ws || ws_bytes < need))
     NKV_FAIL(NKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  if (Nq == 0) return NKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream_);
   const float tau = tau_of(shape);
   const int dt = shape->dtype, H = shape->H, d = shape->d, r = shape->r, g = shape->group;
@@ -260,10 +260,10 @@ nkv_status nkv_encode(const nkv_shape* shape, const void* x, int64_t N, const vo
   if (A > 65536) NKV_FAIL(NKV_EUNSUPPORTED, "A above 65536");
   if (!centers || !encoder) NKV_FAIL(NKV_EINVAL, "NULL centers/encoder");
   if (N > 0 && (!x || !idx || !codes || !scales)) NKV_FAIL(NKV_EINVAL, "NULL x/idx/codes/scales with N>0");
+  if (N == 0) return NKV_OK;
   const size_t need = nkv_encode_workspace_size(shape, N, A);
   if (need > 0 && (!ws || ws_bytes < need))
     NKV_FAIL(NKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  if (N == 0) return NKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int W = shape->H * shape->d;
   if (tuned_applies(shape, 0))

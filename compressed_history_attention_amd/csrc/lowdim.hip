@@ -40,12 +40,31 @@ constexpr int TS = 65;        // LDS row stride of the center tables (64 + senti
 constexpr int CHUNK = 1024;   // tokens per counting chunk
 constexpr float BOUND_GAP_LIMIT = 60.f;  // log2 units
 
+// Tile image: the exact LDS layout the main kernel consumes, so a tile moves
+// from HBM/L2 to LDS with plain 1 KiB direct-to-LDS loads.
+//   [0, ck_bytes)        K coefficients, 64 keys x (rlp + 8) fp16 (padded rows)
+//   [cv_off, +cv_bytes)  V coefficients then the a^V one-hot, (rp + 64) x 68 bf16
+//   [ko_off, +256)       per key: byte offset of its a^K slot in the T table row
+struct TileGeom {
+  int rlp, rp, cks, cvr, ck_bytes, cv_off, cv_bytes, ko_off, bytes;
+};
+constexpr int CVS = 68;
+__host__ __device__ constexpr TileGeom tile_geom(int rlp) {
+  const int rp = (rlp + 31) / 32 * 32;
+  const int cks = rlp + 8, cvr = rp + CR;
+  const int ck_bytes = NT * cks * 2, cv_bytes = cvr * CVS * 2;
+  const int ko_off = ck_bytes + cv_bytes;
+  return TileGeom{rlp, rp, cks, cvr, ck_bytes, ck_bytes, cv_bytes, ko_off,
+                  (ko_off + NT * 4 + 1023) / 1024 * 1024};
+}
+
 struct Plan {
   int64_t n_low = 0, nchunk = 0, max_tiles = 0, max_slots = 0, rows = 0;
   int GK = 0, GV = 0, NB = 0, rlp = 0, rp = 0, ra = 0, av = 0, avp = 0;
+  TileGeom g;
   // byte offsets inside the low-path workspace
   size_t dkt, mvt, qt32, qt16, bound, tmax, present, misc, flags, cnt, base, tile_start, bcount,
-      tile_bucket, perm, ck, cvt, koff, voff, acc, wmass, ell, total;
+      tile_bucket, perm, img, acc, wmass, ell, total;
 };
 
 Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& low, int32_t r_low,
@@ -65,6 +84,7 @@ Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& l
   P.ra = P.rp;
   P.av = (int)ceil_div(A_v, 32) * 32;
   P.avp = P.av;
+  P.g = tile_geom(P.rlp);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -86,10 +106,7 @@ Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& l
   P.bcount = take(sizeof(int32_t) * P.NB);
   P.tile_bucket = take(sizeof(int32_t) * P.max_tiles);
   P.perm = take(sizeof(int32_t) * P.max_slots);
-  P.ck = take(sizeof(uint16_t) * P.max_slots * P.rlp);
-  P.cvt = take(sizeof(uint16_t) * P.max_tiles * P.rp * NT);
-  P.koff = take(sizeof(int32_t) * P.max_slots);
-  P.voff = take(sizeof(int32_t) * P.max_slots);
+  P.img = take((size_t)P.max_tiles * P.g.bytes);
   P.acc = take(sizeof(float) * P.rows * r_low);
   P.wmass = take(sizeof(float) * P.rows * A_v);
   P.ell = take(sizeof(float) * P.rows);
@@ -213,14 +230,15 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(BranchArgs kb, BranchArg
   }
 }
 
-// one thread per padded slot: dequantised K coefficients (fp16 rows), V
-// coefficients (bf16, per-tile transposed), table offsets, max |c^K|^2
-__global__ __launch_bounds__(256) void k_build_tiles(
-    BranchArgs kb, BranchArgs vb, int r, int group, int r_low, int rlp, int rp,
+// one thread per padded slot (key) writes its column of the tile image:
+// dequantised K coefficients (fp16 row), V coefficients and the a^V one-hot
+// (bf16 column), the T-table offset of its a^K; dummies get zeros and the
+// -inf sentinel offset.  Also max |c^K[:r_low]|^2 over real keys.
+__global__ __launch_bounds__(256) void k_build_images(
+    BranchArgs kb, BranchArgs vb, int r, int group, int r_low, TileGeom g,
     const int32_t* __restrict__ tile_start, const int32_t* __restrict__ tile_bucket,
     const int32_t* __restrict__ bcount, int NB, const int32_t* __restrict__ perm,
-    uint16_t* __restrict__ ck, uint16_t* __restrict__ cvt, int32_t* __restrict__ koff,
-    int32_t* __restrict__ voff, uint32_t* __restrict__ cmax2) {
+    char* __restrict__ img, uint32_t* __restrict__ cmax2) {
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nslots = (int64_t)tile_start[NB] * NT;
   if (p >= nslots) return;
@@ -228,13 +246,18 @@ __global__ __launch_bounds__(256) void k_build_tiles(
   const int key = (int)(p - tile * NT);
   const int b = tile_bucket[tile];
   const bool real = (p - (int64_t)tile_start[b] * NT) < bcount[b];
-  uint16_t* ckrow = ck + p * rlp;
-  uint16_t* cvcol = cvt + tile * rp * NT + key;
+  char* base = img + tile * g.bytes;
+  uint16_t* ckrow = reinterpret_cast<uint16_t*>(base) + key * g.cks;
+  uint16_t* cvcol = reinterpret_cast<uint16_t*>(base + g.cv_off) + key;
+  int32_t* ko = reinterpret_cast<int32_t*>(base + g.ko_off);
+  if (key < CVS - NT) {  // row padding columns 64..67 of the V/one-hot rows
+    for (int j = 0; j < g.cvr; ++j) cvcol[j * CVS + NT] = 0;
+  }
+  for (int j = g.rlp; j < g.cks; ++j) ckrow[j] = 0;
   if (!real) {
-    for (int j = 0; j < rlp; j += 8) *reinterpret_cast<u32x4*>(ckrow + j) = u32x4{0u, 0u, 0u, 0u};
-    for (int j = 0; j < rp; ++j) cvcol[j * NT] = 0;
-    koff[p] = CR * 4;
-    voff[p] = CR * 4;
+    for (int j = 0; j < g.rlp; j += 2) *reinterpret_cast<uint32_t*>(ckrow + j) = 0u;
+    for (int j = 0; j < g.cvr; ++j) cvcol[j * CVS] = 0;
+    ko[key] = CR * 4;
     return;
   }
   const int64_t t = perm[p];
@@ -243,7 +266,7 @@ __global__ __launch_bounds__(256) void k_build_tiles(
   const uint8_t* vc = vb.codes + t * (r / 2);
   const uint16_t* vs = vb.scales + t * (r / group);
   float n2 = 0.f;
-  for (int j = 0; j < rlp; j += 2) {
+  for (int j = 0; j < g.rlp; j += 2) {
     float v0 = 0.f, v1 = 0.f;
     if (j < r_low) {
       v0 = (float)code_at(kc, j) * fp16_bits_to_f32(ks[j / group]);
@@ -252,12 +275,13 @@ __global__ __launch_bounds__(256) void k_build_tiles(
     n2 = fmaf(v0, v0, fmaf(v1, v1, n2));
     *reinterpret_cast<uint32_t*>(ckrow + j) = pack_f16x2(v0, v1);
   }
-  for (int j = 0; j < rp; ++j) {
+  for (int j = 0; j < g.rp; ++j) {
     const float v = (j < r_low) ? (float)code_at(vc, j) * fp16_bits_to_f32(vs[j / group]) : 0.f;
-    cvcol[j * NT] = f32_to_bf16_bits(v);
+    cvcol[j * CVS] = f32_to_bf16_bits(v);
   }
-  koff[p] = (kb.idx[t] % CR) * 4;
-  voff[p] = (vb.idx[t] % CR) * 4;
+  const int av = vb.idx[t] % CR;
+  for (int c = 0; c < CR; ++c) cvcol[(g.rp + c) * CVS] = (c == av) ? uint16_t(0x3F80) : uint16_t(0);
+  ko[key] = (kb.idx[t] % CR) * 4;
   atomicMax(cmax2, ordered_bits(n2));
 }
 
@@ -362,37 +386,63 @@ struct MainArgs {
   const uint16_t* muk;
   const uint16_t* qt16;
   const float* bound;
-  const uint16_t* ck;
-  const uint16_t* cvt;
-  const int32_t* koff;
-  const int32_t* voff;
+  const char* img;
   const int32_t* tile_start;
-  const int32_t* bcount;
+  const int32_t* tile_bucket;
   float* acc;
   float* wmass;
   float* ell;
   int64_t Nq;
-  int H, A_k, A_v, GK, GV, r_low;
+  int H, A_k, A_v, GK, NB, r_low;
   float c;
 };
 
 template <int RLP>
+struct MainGeo {
+  static constexpr TileGeom G = tile_geom(RLP);
+  static constexpr int RP = G.rp, NPB = RP / 32, CHUNKS = G.bytes / 1024;
+  static constexpr int T_BYTES = RB * TS * 4;
+  static constexpr int STAGES = (3 * G.bytes + T_BYTES <= 160 * 1024) ? 3 : 2;
+};
+
+// one wave's share of a tile: 1 KiB chunks w, w + 8, ... straight into LDS
+template <int RLP>
+__device__ __forceinline__ void load_tile(const char* __restrict__ src, char* lds, int wave,
+                                          int lane) {
+  constexpr int C = MainGeo<RLP>::CHUNKS;
+#pragma unroll
+  for (int c = wave; c < C; c += 8)
+    __builtin_amdgcn_global_load_lds(src + c * 1024 + lane * 16,
+                                     (__attribute__((address_space(3))) void*)(lds + c * 1024), 16,
+                                     0, 0);
+}
+
+// wait until this wave's loads of the oldest in-flight tile have landed
+template <int RLP>
+__device__ __forceinline__ void wait_tile(int wave) {
+  constexpr int C = MainGeo<RLP>::CHUNKS, S = MainGeo<RLP>::STAGES;
+  constexpr int KLO = C / 8;                    // loads per tile of waves >= C % 8
+  if (S == 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else if (wave < C % 8) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KLO + 1) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KLO) : "memory");
+  }
+}
+
+template <int RLP>
 __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
-  constexpr int RP = (RLP + 31) / 32 * 32;   // coefficient rows of the V tile
-  constexpr int NPB = RP / 32;               // 32-wide coefficient blocks
-  constexpr int CKS = RLP + 8;               // LDS row stride of the K tile (fp16)
-  constexpr int CVS = 68;                    // LDS row stride of the V tile (bf16)
-  constexpr int CKC = NT * RLP / 8;          // 16-byte chunks per K tile
-  constexpr int CVC = RP * NT / 8;           // 16-byte chunks per V tile
-  constexpr int NCH = CKC + CVC + 32;        // + key/value offsets
-  constexpr int PER = (NCH + 511) / 512;
-  __shared__ __attribute__((aligned(16))) float sTW[2 * RB * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t sCK[2][NT * CKS];
-  __shared__ __attribute__((aligned(16))) uint16_t sCV[2][RP * CVS];
-  __shared__ __attribute__((aligned(16))) int32_t sOff[2][2 * NT];
-  __shared__ float sEll[RB];
-  float* sT = sTW;
-  float* sW = sTW + RB * TS;
+  using Geo = MainGeo<RLP>;
+  constexpr TileGeom G = Geo::G;
+  constexpr int RP = Geo::RP, NPB = Geo::NPB, ST = Geo::STAGES;
+  // one array per pipeline stage: the stage of every LDS access is static,
+  // so the compiler can see that reading one stage does not alias the
+  // direct-to-LDS loads in flight into another
+  __shared__ __attribute__((aligned(1024))) char sB0[G.bytes];
+  __shared__ __attribute__((aligned(1024))) char sB1[G.bytes];
+  __shared__ __attribute__((aligned(1024))) char sB2[ST == 3 ? G.bytes : 16];
+  __shared__ __attribute__((aligned(16))) float sT[RB * TS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
   const int rg = wave & 3, kh = wave >> 2;
@@ -402,190 +452,182 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
   const int64_t qrow = (int64_t)blockIdx.x * RB + rloc;
   const bool rok = qrow < a.Nq;
   const int64_t grow = qrow * a.H + h;
+  const uint16_t* qsrc = a.q + (rok ? qrow : 0) * W + h * 128 + 8 * hl;
 
-  // per-lane operands
-  bf16x8 qh[8];
   f16x8 qtf[RLP / 16];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    qh[ks] = rok ? as_bf16x8(ld_u32x4(a.q + qrow * W + h * 128 + 16 * ks + 8 * hl))
-                 : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
   for (int ks = 0; ks < RLP / 16; ++ks)
     qtf[ks] = rok ? as_f16x8(ld_u32x4(a.qt16 + grow * RLP + 16 * ks + 8 * hl))
                   : as_f16x8(u32x4{0u, 0u, 0u, 0u});
   const float Bq = rok ? a.bound[grow] : 0.f;
-  f32x16 accT[NPB];
+  f32x16 accT[NPB], accW[2];
 #pragma unroll
   for (int i = 0; i < NPB; ++i) accT[i] = zero16();
+  accW[0] = zero16();
+  accW[1] = zero16();
+  float lsum = 0.f;
 
-  for (int i = tid; i < RB * TS; i += 512) sW[i] = 0.f;
-  if (tid < RB) sEll[tid] = 0.f;
-
-  u32x4 stg[PER];
-  auto fetch = [&](int64_t tile) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int cidx = tid + 512 * u;
-      if (cidx < CKC) {
-        stg[u] = ld_u32x4(a.ck + tile * NT * RLP + cidx * 8);
-      } else if (cidx < CKC + CVC) {
-        stg[u] = ld_u32x4(a.cvt + tile * RP * NT + (cidx - CKC) * 8);
-      } else if (cidx < NCH) {
-        const int o = cidx - CKC - CVC;  // 0..15 key offsets, 16..31 value offsets
-        const int32_t* src = (o < 16) ? a.koff : a.voff;
-        stg[u] = ld_u32x4(src + tile * NT + (o & 15) * 4);
-      }
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int cidx = tid + 512 * u;
-      if (cidx < CKC) {
-        const int row = cidx / (RLP / 8), col = (cidx % (RLP / 8)) * 8;
-        *reinterpret_cast<u32x4*>(&sCK[buf][row * CKS + col]) = stg[u];
-      } else if (cidx < CKC + CVC) {
-        const int ci = cidx - CKC;
-        const int row = ci / 8, col = (ci % 8) * 8;
-        *reinterpret_cast<u32x2*>(&sCV[buf][row * CVS + col]) = u32x2{stg[u][0], stg[u][1]};
-        *reinterpret_cast<u32x2*>(&sCV[buf][row * CVS + col + 4]) = u32x2{stg[u][2], stg[u][3]};
-      } else if (cidx < NCH) {
-        const int o = cidx - CKC - CVC;
-        *reinterpret_cast<u32x4*>(&sOff[buf][(o >> 4) * NT + (o & 15) * 4]) = stg[u];
-      }
-    }
-  };
-
+  const int ntiles = a.tile_start[a.NB];
   const char* sTrow = reinterpret_cast<const char*>(sT + rloc * TS);
-  float* sWrow = sW + rloc * TS;
-  __syncthreads();
 
-  for (int gv = 0; gv < a.GV; ++gv) {
-    for (int gk = 0; gk < a.GK; ++gk) {
-      const int b = gv * a.GK + gk;
-      const int cnt = a.bcount[b];
-      if (cnt == 0) continue;
-      const int64_t t0 = a.tile_start[b];
-      const int nt = a.tile_start[b + 1] - (int)t0;
-      // ---- T slice: T^T[center][row] = mu^K_{center,h} . q_h (exact products)
-      {
-        f32x16 tt = zero16();
-        const int cen = gk * CR + kh * 32 + (lane & 31);
-        const bool cok = cen < a.A_k;
+  // flush the masses of a finished a^V range: key halves meet in LDS
+  auto flush = [&](int gv) {
+    __syncthreads();
+    if (kh == 1) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 m = cok ? as_bf16x8(ld_u32x4(a.muk + (int64_t)cen * W + h * 128 + 16 * ks + 8 * hl))
-                               : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-          tt = mfma_bf16(m, qh[ks], tt);
-        }
-        fetch(t0);
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sT[rloc * TS + cb * 32 + acc_row(e, lane)] = accW[cb][e];
+    }
+    __syncthreads();
+    if (kh == 0 && rok) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int cl = kh * 32 + acc_row(e, lane);
-          sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[e], a.c, -Bq) : -INFINITY;
+          const int c = cb * 32 + acc_row(e, lane);
+          if (gv * CR + c < a.A_v)
+            a.wmass[grow * a.A_v + gv * CR + c] = accW[cb][e] + sT[rloc * TS + c];
         }
-        if (kh == 0 && hl == 0) sT[rloc * TS + CR] = -INFINITY;
-        stash(0);
-      }
+    }
+    accW[0] = zero16();
+    accW[1] = zero16();
+  };
+
+  if (0 < ntiles) load_tile<RLP>(a.img, sB0, wave, lane);
+  if (ST == 3 && 1 < ntiles) load_tile<RLP>(a.img + G.bytes, sB1, wave, lane);
+
+  int prev_gv = -1;
+  // one tile: consume `cur`, start loading tile t + ST - 1 into `nxt`
+  auto body = [&](int t, const char* cur, char* nxt) {
+    const int b = a.tile_bucket[t];
+    const int t0 = a.tile_start[b];
+    if (t == t0) {
+      // ---- new bucket: (flush,) then the T slice of its a^K range -------------
+      const int gv = b / a.GK, gk = b - gv * a.GK;
+      if (gv != prev_gv && prev_gv >= 0) flush(prev_gv);
+      prev_gv = gv;
       __syncthreads();
-      for (int it = 0; it < nt; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < nt) fetch(t0 + it + 1);
-        const int real = min(NT, cnt - it * NT);
-        if (kh * 32 < real) {
-          // ---- scores S^T[key][row] = c^K . q~ (fp16 MFMA) ----------------
-          f32x16 s = zero16();
+      f32x16 tt = zero16();
+      const int cen = gk * CR + kh * 32 + (lane & 31);
+      const bool cok = cen < a.A_k;
+      const uint16_t* msrc = a.muk + (int64_t)(cok ? cen : 0) * W + h * 128 + 8 * hl;
 #pragma unroll
-          for (int ks = 0; ks < RLP / 16; ++ks) {
-            const f16x8 ca = as_f16x8(*reinterpret_cast<const u32x4*>(
-                &sCK[buf][(kh * 32 + (lane & 31)) * CKS + 16 * ks + 8 * hl]));
-            s = mfma_f16(ca, qtf[ks], s);
-          }
-          // ---- p = 2^(c s + c T - B); center-mass scatter ------------------
-          float p[16];
+      for (int ks = 0; ks < 8; ++ks) {
+        bf16x8 m = as_bf16x8(ld_u32x4(msrc + 16 * ks));
+        bf16x8 qv = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
+        if (!cok) m = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        if (!rok) qv = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        tt = mfma_bf16(m, qv, tt);
+      }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int key = kh * 32 + g * 8 + hl * 4;
-            const int32_t* ko = &sOff[buf][key];
-            const int32_t* vo = &sOff[buf][NT + key];
-            const u32x4 kov = *reinterpret_cast<const u32x4*>(ko);
-            const u32x4 vov = *reinterpret_cast<const u32x4*>(vo);
+      for (int e = 0; e < 16; ++e) {
+        const int cl = kh * 32 + acc_row(e, lane);
+        sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[e], a.c, -Bq) : -INFINITY;
+      }
+      if (kh == 0 && hl == 0) sT[rloc * TS + CR] = -INFINITY;
+    }
+    if (t + 1 < ntiles)
+      wait_tile<RLP>(wave);
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + ST - 1 < ntiles)
+      load_tile<RLP>(a.img + (int64_t)(t + ST - 1) * G.bytes, nxt, wave, lane);
+    const char* buf = cur;
+    const uint16_t* sCK = reinterpret_cast<const uint16_t*>(buf);
+    const uint16_t* sCV = reinterpret_cast<const uint16_t*>(buf + G.cv_off);
+    const int32_t* sKO = reinterpret_cast<const int32_t*>(buf + G.ko_off);
+    // ---- scores S^T[key][row] = c^K . q~ (fp16 MFMA) ------------------------
+    f32x16 s = zero16();
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float tv = *reinterpret_cast<const float*>(sTrow + kov[u]);
-              const float x = fmaf(s[4 * g + u], a.c, tv);
-              const float pv = __builtin_amdgcn_exp2f(x);
-              p[4 * g + u] = pv;
-              atomicAdd(reinterpret_cast<float*>(reinterpret_cast<char*>(sWrow) + vov[u]), pv);
-            }
-          }
-          // ---- acc^T[coef][row] += c^V^T P^T (bf16 MFMA) --------------------
+    for (int ks = 0; ks < RLP / 16; ++ks) {
+      const f16x8 ca = as_f16x8(
+          *reinterpret_cast<const u32x4*>(&sCK[(kh * 32 + (lane & 31)) * G.cks + 16 * ks + 8 * hl]));
+      s = mfma_f16(ca, qtf[ks], s);
+    }
+    // ---- p = 2^(c s + c T - B) ----------------------------------------------
+    u32x4 pk[2];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            u32x4 pk;
+    for (int g = 0; g < 4; ++g) {
+      const u32x4 kov = *reinterpret_cast<const u32x4*>(&sKO[kh * 32 + g * 8 + hl * 4]);
+      float pv[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(p[8 * j + 2 * u], p[8 * j + 2 * u + 1]);
-            const bf16x8 pb = as_bf16x8(pk);
+      for (int u = 0; u < 4; ++u) {
+        const float tv = *reinterpret_cast<const float*>(sTrow + kov[u]);
+        pv[u] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + u], a.c, tv));
+        lsum += pv[u];
+      }
+      pk[g >> 1][(g & 1) * 2] = pack_bf16x2(pv[0], pv[1]);
+      pk[g >> 1][(g & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+    }
+    const bf16x8 pb[2] = {as_bf16x8(pk[0]), as_bf16x8(pk[1])};
+    // ---- [acc^T ; M^T][coef|center][row] += [c^V ; onehot(a^V)]^T P^T -------
 #pragma unroll
-            for (int db = 0; db < NPB; ++db) {
-              const uint16_t* vrow = &sCV[buf][(db * 32 + (lane & 31)) * CVS + kh * 32 + 16 * j + 4 * hl];
-              const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-              const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-              accT[db] = mfma_bf16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, accT[db]);
-            }
-          }
-        }
-        if (it + 1 < nt) stash(buf ^ 1);
-        __syncthreads();
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int db = 0; db < NPB + 2; ++db) {
+        const uint16_t* vrow = &sCV[(db * 32 + (lane & 31)) * CVS + kh * 32 + 16 * j + 4 * hl];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+        const bf16x8 av = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        if (db < NPB)
+          accT[db] = mfma_bf16(av, pb[j], accT[db]);
+        else
+          accW[db - NPB] = mfma_bf16(av, pb[j], accW[db - NPB]);
       }
     }
-    // ---- flush the finished a^V range of the center masses ------------------
-    {
-      const int row = tid >> 2, part = tid & 3;
-      const int64_t q = (int64_t)blockIdx.x * RB + row;
-      float* src = sW + row * TS + part * 16;
-      float sum = 0.f;
-      float* dst = a.wmass + (q * a.H + h) * a.A_v + gv * CR + part * 16;
+  };
+  if (ST == 3) {
+    for (int t = 0; t < ntiles; t += 3) {
+      body(t, sB0, sB2);
+      if (t + 1 < ntiles) body(t + 1, sB1, sB0);
+      if (t + 2 < ntiles) body(t + 2, sB2, sB1);
+    }
+  } else {
+    for (int t = 0; t < ntiles; t += 2) {
+      body(t, sB0, sB1);
+      if (t + 1 < ntiles) body(t + 1, sB1, sB0);
+    }
+  }
+  if (prev_gv >= 0) flush(prev_gv);
+  __syncthreads();
+  // ---- combine the key halves: coefficient sums (64 dims per pass), ell ------
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float v = src[i];
-        sum += v;
-        if (q < a.Nq && gv * CR + part * 16 + i < a.A_v) dst[i] = v;
-        src[i] = 0.f;
-      }
-      sum += __shfl_xor(sum, 1, 64);
-      sum += __shfl_xor(sum, 2, 64);
-      if (part == 0) {
-        sEll[row] += sum;
-        sW[row * TS + CR] = 0.f;
-      }
+  for (int pass = 0; pass < (NPB + 1) / 2; ++pass) {
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 2 * pass; db < min(NPB, 2 * pass + 2); ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          sT[rloc * TS + (db - 2 * pass) * 32 + acc_row(e, lane)] = accT[db][e];
+    }
+    __syncthreads();
+    if (kh == 0 && rok) {
+#pragma unroll
+      for (int db = 2 * pass; db < min(NPB, 2 * pass + 2); ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int dim = db * 32 + acc_row(e, lane);
+          if (dim < a.r_low)
+            a.acc[grow * a.r_low + dim] =
+                accT[db][e] + sT[rloc * TS + (db - 2 * pass) * 32 + acc_row(e, lane)];
+        }
     }
     __syncthreads();
   }
-  // ---- combine the two key halves' coefficient sums ---------------------------
-  float* red = sTW;  // RB x (RP + 1) floats
-  if (kh == 1) {
-#pragma unroll
-    for (int db = 0; db < NPB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) red[rloc * (RP + 1) + db * 32 + acc_row(e, lane)] = accT[db][e];
-  }
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (kh == 1 && hl == 0) sT[rloc] = lsum;
   __syncthreads();
-  if (kh == 0 && rok) {
-#pragma unroll
-    for (int db = 0; db < NPB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int dim = db * 32 + acc_row(e, lane);
-        if (dim < a.r_low)
-          a.acc[grow * a.r_low + dim] = accT[db][e] + red[rloc * (RP + 1) + dim];
-      }
-  }
-  if (tid < RB) {
-    const int64_t q = (int64_t)blockIdx.x * RB + tid;
-    if (q < a.Nq) a.ell[q * a.H + h] = sEll[tid];
-  }
+  if (kh == 0 && hl == 0 && rok) a.ell[grow] = lsum + sT[rloc];
+}
+
+template <int RLP>
+nkv_status launch_main(const MainArgs& m, int64_t Nq, int H, hipStream_t st) {
+  dim3 grid((unsigned)ceil_div(Nq, RB), (unsigned)H);
+  hipLaunchKernelGGL(k_low_main<RLP>, grid, dim3(512), 0, st, m);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -665,13 +707,6 @@ struct RestoreProblem {
   }
 };
 
-template <int RLP>
-nkv_status launch_main(const MainArgs& m, int64_t Nq, int H, hipStream_t st) {
-  dim3 grid((unsigned)ceil_div(Nq, RB), (unsigned)H);
-  hipLaunchKernelGGL(k_low_main<RLP>, grid, dim3(512), 0, st, m);
-  NKV_LAUNCH_CHECK();
-  return NKV_OK;
-}
 
 }  // namespace
 
@@ -702,10 +737,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   int32_t* bcount = reinterpret_cast<int32_t*>(at(P.bcount));
   int32_t* tile_bucket = reinterpret_cast<int32_t*>(at(P.tile_bucket));
   int32_t* perm = reinterpret_cast<int32_t*>(at(P.perm));
-  uint16_t* ck = reinterpret_cast<uint16_t*>(at(P.ck));
-  uint16_t* cvt = reinterpret_cast<uint16_t*>(at(P.cvt));
-  int32_t* koff = reinterpret_cast<int32_t*>(at(P.koff));
-  int32_t* voff = reinterpret_cast<int32_t*>(at(P.voff));
+  char* img = at(P.img);
   float* acc = reinterpret_cast<float*>(at(P.acc));
   float* wmass = reinterpret_cast<float*>(at(P.wmass));
   float* ell = reinterpret_cast<float*>(at(P.ell));
@@ -733,9 +765,9 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
                      P.NB, base, tile_start, bcount, tile_bucket);
   hipLaunchKernelGGL(k_bucket_scatter, dim3(nch), dim3(256), 0, st, kb, vb, low, P.GK, P.NB, base,
                      perm);
-  hipLaunchKernelGGL(k_build_tiles, dim3((unsigned)ceil_div(P.max_slots, 256)), dim3(256), 0, st,
-                     kb, vb, r, s->group, r_low, P.rlp, P.rp, tile_start, tile_bucket, bcount, P.NB,
-                     perm, ck, cvt, koff, voff, misc);
+  hipLaunchKernelGGL(k_build_images, dim3((unsigned)ceil_div(P.max_slots, 256)), dim3(256), 0, st,
+                     kb, vb, r, s->group, r_low, P.g, tile_start, tile_bucket, bcount, P.NB, perm,
+                     img, misc);
   NKV_LAUNCH_CHECK();
   // query reduction and per-row score bounds
   QtProblem qp{(int)Nq, r_low, 128, H, q, dkt, qt32};
@@ -750,8 +782,8 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   // main pass
   {
   ProfScope ps_main("low_main", st);
-  MainArgs m{q, static_cast<const uint16_t*>(kb.centers), qt16, bound, ck, cvt, koff, voff,
-             tile_start, bcount, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.GV, r_low, c};
+  MainArgs m{q, static_cast<const uint16_t*>(kb.centers), qt16, bound, img, tile_start,
+             tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.NB, r_low, c};
   switch (P.rlp) {
     case 16: e = launch_main<16>(m, Nq, H, st); break;
     case 32: e = launch_main<32>(m, Nq, H, st); break;

@@ -51,6 +51,10 @@ class nkv_segment(ctypes.Structure):
     _fields_ = [("begin", ctypes.c_int64), ("end", ctypes.c_int64), ("mode", ctypes.c_int32)]
 
 
+class nkv_prof_entry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("ms", ctypes.c_double), ("count", ctypes.c_int32)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -77,6 +81,8 @@ def load() -> ctypes.CDLL:
         "nkv_attend_fast": (ctypes.c_int, [SH, BR, BR, I64, SG, I32, I32, P, I64, P, P, I64, P,
                                            P, P, SZ, P]),
         "nkv_lse_merge": (ctypes.c_int, [I64, I32, I32, P, P, P, P, P, I32, P, P]),
+        "nkv_profile_enable": (None, [ctypes.c_int]),
+        "nkv_profile_read": (ctypes.c_int, [ctypes.POINTER(nkv_prof_entry), I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -88,7 +94,8 @@ def load() -> ctypes.CDLL:
 
 EXPORTS = ("nkv_version", "nkv_last_error", "nkv_status_string", "nkv_force_generic",
            "nkv_encode_workspace_size", "nkv_encode", "nkv_attend_workspace_size",
-           "nkv_attend_full", "nkv_attend_fast", "nkv_lse_merge")
+           "nkv_attend_full", "nkv_attend_fast", "nkv_lse_merge", "nkv_profile_enable",
+           "nkv_profile_read")
 
 
 def _check(status: int):
@@ -171,6 +178,19 @@ def nkv_version() -> int:
 
 def nkv_force_generic(on: bool) -> None:
     load().nkv_force_generic(1 if on else 0)
+
+
+def nkv_profile_enable(on: bool) -> None:
+    load().nkv_profile_enable(1 if on else 0)
+
+
+def nkv_profile_read(max_entries: int = 64) -> dict:
+    """{stage: (total ms, launches)} recorded since the last read."""
+    buf = (nkv_prof_entry * max_entries)()
+    n = load().nkv_profile_read(buf, max_entries)
+    if n < 0:
+        raise NkvError(4, "profile read failed")
+    return {buf[i].name.decode(): (buf[i].ms, buf[i].count) for i in range(n)}
 
 
 def nkv_encode_workspace_size(shape: Shape, N: int, A: int) -> int:

@@ -110,7 +110,7 @@ size_t nkv_encode_workspace_size(const nkv_shape* shape, int64_t N, int32_t A);
  *   z_t = encoder (x_t - centers[a_t])       (encoder [r, W])
  *   INT4-quantise z_t per group (format above).
  * Writes idx[t], codes[t, :], scales[t, :].  Appending to a history is
- * pointer arithmetic on these outputs.  N == 0 is a no-op.
+ * pointer arithmetic on these outputs.  N == 0 is a no-op (ws may be NULL).
  */
 nkv_status nkv_encode(const nkv_shape* shape, const void* x, int64_t N,
                       const void* centers, int32_t A, const void* encoder,
@@ -131,7 +131,7 @@ size_t nkv_attend_workspace_size(const nkv_shape* shape, int32_t A_k,
  * softmax attention per head with scores tau * q_h . k_h over the decoded
  * history followed by the uncompressed current chunk cur_k/cur_v [N_cur, W]
  * (ignored, and may be NULL, when N_cur == 0).  q [Nq, W]; out [Nq, W] (shape dtype);
- * lse [Nq, H] float32.
+ * lse [Nq, H] float32.  Nq == 0 is a no-op after validation (ws may be NULL).
  */
 nkv_status nkv_attend_full(const nkv_shape* shape, const nkv_branch* k,
                            const nkv_branch* v, int64_t N_hist,
