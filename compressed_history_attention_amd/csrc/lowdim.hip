@@ -402,7 +402,10 @@ struct MainGeo {
   static constexpr TileGeom G = tile_geom(RLP);
   static constexpr int RP = G.rp, NPB = RP / 32, CHUNKS = G.bytes / 1024;
   static constexpr int T_BYTES = RB * TS * 4;
-  static constexpr int STAGES = (3 * G.bytes + T_BYTES <= 160 * 1024) ? 3 : 2;
+  static constexpr int Q_BYTES = RB * 256;   // the block's 128 query rows of one head (bf16)
+  static constexpr int M_BYTES = CR * 256;   // one 64-center slice of mu^K for one head (bf16)
+  // the T-slice operands live in LDS when they fit next to two tile stages
+  static constexpr bool LDS_T = 2 * G.bytes + T_BYTES + Q_BYTES + M_BYTES <= 160 * 1024;
 };
 
 // one wave's share of a tile: 1 KiB chunks w, w + 8, ... straight into LDS
@@ -417,31 +420,39 @@ __device__ __forceinline__ void load_tile(const char* __restrict__ src, char* ld
                                      0, 0);
 }
 
-// wait until this wave's loads of the oldest in-flight tile have landed
-template <int RLP>
-__device__ __forceinline__ void wait_tile(int wave) {
-  constexpr int C = MainGeo<RLP>::CHUNKS, S = MainGeo<RLP>::STAGES;
-  constexpr int KLO = C / 8;                    // loads per tile of waves >= C % 8
-  if (S == 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else if (wave < C % 8) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KLO + 1) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KLO) : "memory");
+// 256-byte bf16 rows (128 channels of one head) into LDS, four rows per 1 KiB
+// load, with the 16-byte blocks of row r stored at block (j ^ (r & 15)) so
+// that 32 lanes reading one block of 32 different rows hit distinct banks.
+__device__ __forceinline__ void load_rows_swizzled(const uint16_t* __restrict__ base, int64_t ld,
+                                                   int nrows, int valid, char* lds, int wave,
+                                                   int lane) {
+  for (int c = wave; c < nrows / 4; c += 8) {
+    const int r = 4 * c + (lane >> 4), jp = lane & 15;
+    const int j = jp ^ (r & 15);
+    const int rr = r < valid ? r : 0;
+    __builtin_amdgcn_global_load_lds(base + rr * ld + j * 8,
+                                     (__attribute__((address_space(3))) void*)(lds + c * 1024), 16,
+                                     0, 0);
   }
+}
+
+__device__ __forceinline__ u32x4 lds_row_block(const char* lds, int r, int j) {
+  return *reinterpret_cast<const u32x4*>(lds + r * 256 + ((j ^ (r & 15)) << 4));
 }
 
 template <int RLP>
 __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
   using Geo = MainGeo<RLP>;
   constexpr TileGeom G = Geo::G;
-  constexpr int RP = Geo::RP, NPB = Geo::NPB, ST = Geo::STAGES;
+  constexpr int RP = Geo::RP, NPB = Geo::NPB;
+  constexpr bool LT = Geo::LDS_T;
   // one array per pipeline stage: the stage of every LDS access is static,
   // so the compiler can see that reading one stage does not alias the
-  // direct-to-LDS loads in flight into another
+  // direct-to-LDS loads in flight into the other
   __shared__ __attribute__((aligned(1024))) char sB0[G.bytes];
   __shared__ __attribute__((aligned(1024))) char sB1[G.bytes];
-  __shared__ __attribute__((aligned(1024))) char sB2[ST == 3 ? G.bytes : 16];
+  __shared__ __attribute__((aligned(1024))) char sQ[LT ? Geo::Q_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char sM[LT ? Geo::M_BYTES : 16];
   __shared__ __attribute__((aligned(16))) float sT[RB * TS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
@@ -449,10 +460,11 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
   const int h = blockIdx.y;
   const int W = a.H * 128;
   const int rloc = rg * 32 + (lane & 31);
-  const int64_t qrow = (int64_t)blockIdx.x * RB + rloc;
+  const int64_t q0 = (int64_t)blockIdx.x * RB;
+  const int64_t qrow = q0 + rloc;
   const bool rok = qrow < a.Nq;
   const int64_t grow = qrow * a.H + h;
-  const uint16_t* qsrc = a.q + (rok ? qrow : 0) * W + h * 128 + 8 * hl;
+  const int nvalid = (int)min<int64_t>(RB, a.Nq - q0);
 
   f16x8 qtf[RLP / 16];
 #pragma unroll
@@ -469,6 +481,13 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
 
   const int ntiles = a.tile_start[a.NB];
   const char* sTrow = reinterpret_cast<const char*>(sT + rloc * TS);
+  const uint16_t* qbase = a.q + q0 * W + h * 128;
+
+  // mu^K rows of the 64-center slice gk for this head
+  auto load_mu = [&](int gk) {
+    const int valid = min(CR, a.A_k - gk * CR);
+    load_rows_swizzled(a.muk + (int64_t)gk * CR * W + h * 128, W, CR, valid, sM, wave, lane);
+  };
 
   // flush the masses of a finished a^V range: key halves meet in LDS
   auto flush = [&](int gv) {
@@ -492,52 +511,70 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
     }
     accW[0] = zero16();
     accW[1] = zero16();
+    __syncthreads();
   };
 
+  // T^T[center][row] = mu^K_{center,h} . q_h (exact bf16 products), scaled
+  // to c T - B and written to the LDS score table
+  auto t_slice = [&](int gk) {
+    f32x16 tt = zero16();
+    const int cl0 = kh * 32 + (lane & 31);
+    if constexpr (LT) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 m = as_bf16x8(lds_row_block(sM, cl0, 2 * ks + hl));
+        const bf16x8 qv = as_bf16x8(lds_row_block(sQ, rloc, 2 * ks + hl));
+        tt = mfma_bf16(m, qv, tt);
+      }
+    } else {
+      const int cen = gk * CR + cl0;
+      const bool cok = cen < a.A_k;
+      const uint16_t* msrc = a.muk + (int64_t)(cok ? cen : 0) * W + h * 128 + 8 * hl;
+      const uint16_t* qsrc = qbase + (int64_t)(rok ? rloc : 0) * W + 8 * hl;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 m = as_bf16x8(ld_u32x4(msrc + 16 * ks));
+        const bf16x8 qv = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
+        tt = mfma_bf16(m, qv, tt);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int cl = kh * 32 + acc_row(e, lane);
+      sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[e], a.c, -Bq) : -INFINITY;
+    }
+    if (kh == 0 && hl == 0) sT[rloc * TS + CR] = -INFINITY;
+  };
+
+  if constexpr (LT) {
+    load_rows_swizzled(qbase, W, RB, nvalid, sQ, wave, lane);
+    if (0 < ntiles) load_mu(a.tile_bucket[0] % a.GK);
+  }
   if (0 < ntiles) load_tile<RLP>(a.img, sB0, wave, lane);
-  if (ST == 3 && 1 < ntiles) load_tile<RLP>(a.img + G.bytes, sB1, wave, lane);
 
   int prev_gv = -1;
-  // one tile: consume `cur`, start loading tile t + ST - 1 into `nxt`
+  // one tile: consume `cur`, start loading tile t + 1 into `nxt`
   auto body = [&](int t, const char* cur, char* nxt) {
     const int b = a.tile_bucket[t];
     const int t0 = a.tile_start[b];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     if (t == t0) {
       // ---- new bucket: (flush,) then the T slice of its a^K range -------------
       const int gv = b / a.GK, gk = b - gv * a.GK;
       if (gv != prev_gv && prev_gv >= 0) flush(prev_gv);
       prev_gv = gv;
+      t_slice(gk);
       __syncthreads();
-      f32x16 tt = zero16();
-      const int cen = gk * CR + kh * 32 + (lane & 31);
-      const bool cok = cen < a.A_k;
-      const uint16_t* msrc = a.muk + (int64_t)(cok ? cen : 0) * W + h * 128 + 8 * hl;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 m = as_bf16x8(ld_u32x4(msrc + 16 * ks));
-        bf16x8 qv = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
-        if (!cok) m = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-        if (!rok) qv = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-        tt = mfma_bf16(m, qv, tt);
+      if constexpr (LT) {
+        const int tn = a.tile_start[b + 1];
+        if (tn < ntiles) load_mu(a.tile_bucket[tn] % a.GK);
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int cl = kh * 32 + acc_row(e, lane);
-        sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[e], a.c, -Bq) : -INFINITY;
-      }
-      if (kh == 0 && hl == 0) sT[rloc * TS + CR] = -INFINITY;
     }
-    if (t + 1 < ntiles)
-      wait_tile<RLP>(wave);
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + ST - 1 < ntiles)
-      load_tile<RLP>(a.img + (int64_t)(t + ST - 1) * G.bytes, nxt, wave, lane);
-    const char* buf = cur;
-    const uint16_t* sCK = reinterpret_cast<const uint16_t*>(buf);
-    const uint16_t* sCV = reinterpret_cast<const uint16_t*>(buf + G.cv_off);
-    const int32_t* sKO = reinterpret_cast<const int32_t*>(buf + G.ko_off);
+    if (t + 1 < ntiles) load_tile<RLP>(a.img + (int64_t)(t + 1) * G.bytes, nxt, wave, lane);
+    const uint16_t* sCK = reinterpret_cast<const uint16_t*>(cur);
+    const uint16_t* sCV = reinterpret_cast<const uint16_t*>(cur + G.cv_off);
+    const int32_t* sKO = reinterpret_cast<const int32_t*>(cur + G.ko_off);
     // ---- scores S^T[key][row] = c^K . q~ (fp16 MFMA) ------------------------
     f32x16 s = zero16();
 #pragma unroll
@@ -578,20 +615,11 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
       }
     }
   };
-  if (ST == 3) {
-    for (int t = 0; t < ntiles; t += 3) {
-      body(t, sB0, sB2);
-      if (t + 1 < ntiles) body(t + 1, sB1, sB0);
-      if (t + 2 < ntiles) body(t + 2, sB2, sB1);
-    }
-  } else {
-    for (int t = 0; t < ntiles; t += 2) {
-      body(t, sB0, sB1);
-      if (t + 1 < ntiles) body(t + 1, sB1, sB0);
-    }
+  for (int t = 0; t < ntiles; t += 2) {
+    body(t, sB0, sB1);
+    if (t + 1 < ntiles) body(t + 1, sB1, sB0);
   }
   if (prev_gv >= 0) flush(prev_gv);
-  __syncthreads();
   // ---- combine the key halves: coefficient sums (64 dims per pass), ell ------
 #pragma unroll
   for (int pass = 0; pass < (NPB + 1) / 2; ++pass) {
@@ -653,14 +681,28 @@ struct RestoreProblem {
     if (k < 2 * ra) {
       lo = k >= ra;
       const int j = lo ? k - ra : k;
+      if (j + 8 <= r_low) {  // r_low % 16 == 0: 32-byte aligned row chunk
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(acc + row * r_low + j);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(acc + row * r_low + j + 4);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (j + i < r_low) ? acc[row * r_low + j + i] : 0.f;
+        for (int i = 0; i < 4; ++i) { v[i] = x0[i]; v[4 + i] = x1[i]; }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      }
     } else {
       const int kk = k - 2 * ra;
       lo = kk >= av;
       const int c = lo ? kk - av : kk;
+      if ((A_v & 3) == 0 && c + 8 <= A_v) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(wmass + row * A_v + c);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(wmass + row * A_v + c + 4);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (c + i < A_v) ? wmass[row * A_v + c + i] : 0.f;
+        for (int i = 0; i < 4; ++i) { v[i] = x0[i]; v[4 + i] = x1[i]; }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (c + i < A_v) ? wmass[row * A_v + c + i] : 0.f;
+      }
     }
     u32x4 out;
 #pragma unroll

@@ -93,15 +93,16 @@ struct DistProblem {
 // projection GEMM: rows = tokens, cols = coefficients, K = 3 W (split terms)
 // ---------------------------------------------------------------------------
 struct ProjProblem {
-  int M, N, K;  // M = tokens, N = r, K = 3 W
+  int M, N, K;  // M = tokens, N = r, K = 3 W / splits (one split per grid z)
   int W;
   const uint16_t* x;
   const uint16_t* mu;
   const int32_t* idx;
   const uint16_t* enc;  // [r, W]
-  float* z;             // [tokens, r]
-  __device__ u32x4 load_a(int, int m, int k) const {
+  float* z;             // [splits][tokens, r] partial sums
+  __device__ u32x4 load_a(int zs, int m, int k) const {
     if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    k += zs * K;
     const int part = k / W, w = k - part * W;
     const u32x4 xv = ld_u32x4(x + (int64_t)m * W + w);
     const u32x4 mv = ld_u32x4(mu + (int64_t)idx[m] * W + w);
@@ -125,12 +126,13 @@ struct ProjProblem {
     }
     return out;
   }
-  __device__ u32x4 load_b(int, int n, int k) const {
+  __device__ u32x4 load_b(int zs, int n, int k) const {
     if (n >= N || k >= K) return u32x4{0u, 0u, 0u, 0u};
-    const int w = k % W;
+    const int w = (k + zs * K) % W;
     return ld_u32x4(enc + (int64_t)n * W + w);
   }
-  __device__ void epilogue(int, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+  __device__ void epilogue(int zs, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+    float* zp = z + (int64_t)zs * M * N;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -138,27 +140,43 @@ struct ProjProblem {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int m = m0 + 32 * i + acc_row(e, lane), n = n0 + 32 * j + (lane & 31);
-          if (m < M && n < N) z[(int64_t)m * N + n] = acc[i][j][e];
+          if (m < M && n < N) zp[(int64_t)m * N + n] = acc[i][j][e];
         }
   }
 };
 
-__global__ void k_quantize_rows(const float* __restrict__ z, int64_t N, int r, int group,
-                                uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+// split-K factor of the projection (fixed per width, so results are
+// deterministic): the three residual terms, each possibly halved
+inline int proj_splits(int W) {
+  if ((3 * W) % (6 * GEMM_BK) == 0) return 6;
+  if ((3 * W) % (3 * GEMM_BK) == 0) return 3;
+  return 1;
+}
+
+// sum the split partials in a fixed order, then quantise one group
+__global__ void k_quantize_rows(const float* __restrict__ z, int splits, int64_t N, int r,
+                                int group, uint8_t* __restrict__ codes,
+                                uint16_t* __restrict__ scales) {
   const int ng = r / group;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N * ng) return;
   const int64_t t = i / ng;
   const int g = (int)(i - t * ng);
-  quantize_group(z + t * r + g * group, group, codes + t * (r / 2) + g * (group / 2),
-                 scales + t * ng + g);
+  float zz[64];
+  const float* src = z + t * r + g * group;
+  for (int j = 0; j < group; ++j) {
+    float v = src[j];
+    for (int sp = 1; sp < splits; ++sp) v += src[(int64_t)sp * N * r + j];
+    zz[j] = v;
+  }
+  quantize_group(zz, group, codes + t * (r / 2) + g * (group / 2), scales + t * ng + g);
 }
 
 size_t tuned_encode_workspace(const nkv_shape* s, int64_t N, int32_t A) {
   size_t off = 0;
   off = align_up(off + sizeof(float) * A, 256);
   off = align_up(off + sizeof(uint64_t) * N, 256);
-  off = align_up(off + sizeof(float) * N * s->r, 256);
+  off = align_up(off + sizeof(float) * N * s->r * proj_splits(s->H * s->d), 256);
   return off;
 }
 
@@ -174,6 +192,7 @@ nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* mub = static_cast<const uint16_t*>(centers);
   nkv_status e;
+  const int splits = proj_splits(W);
   {
   ProfScope ps("encode_assign", st);
   hipLaunchKernelGGL(k_center_norms, dim3(A), dim3(64), 0, st, mub, A, W, mu2);
@@ -188,13 +207,13 @@ nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void
   }
   {
   ProfScope ps("encode_project", st);
-  ProjProblem pp{(int)N, r, 3 * W, W, xb, mub, idx, static_cast<const uint16_t*>(enc), z};
-  if ((e = launch_gemm(pp, 1, st))) return e;
+  ProjProblem pp{(int)N, r, 3 * W / splits, W, xb, mub, idx, static_cast<const uint16_t*>(enc), z};
+  if ((e = launch_gemm(pp, splits, st))) return e;
   }
   ProfScope ps("encode_quantize", st);
   const int64_t ng = N * (r / s->group);
-  hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)ceil_div(ng, 256)), dim3(256), 0, st, z, N,
-                     r, s->group, codes, scales);
+  hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)ceil_div(ng, 256)), dim3(256), 0, st, z,
+                     splits, N, r, s->group, codes, scales);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }
@@ -266,11 +285,62 @@ struct DecodeProblem {
   }
 };
 
+// V decode in the transposed orientation (rows = channels, cols = tokens):
+// lanes own tokens, so the per-head transposed V^T[h][d][token] stores are
+// contiguous along tokens.
+struct DecodeTProblem {
+  int M, N, K;            // M = W channels, N = tokens in the list, K = r
+  int group;
+  BranchArgs b;
+  RangeTable rows;
+  uint16_t* out;          // [W][ld] (= [H][128][ld])
+  int64_t ld;
+  __device__ u32x4 load_a(int, int m, int k) const {
+    if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    return ld_u32x4(static_cast<const uint16_t*>(b.decoder) + (int64_t)m * K + k);
+  }
+  __device__ u32x4 load_b(int, int n, int k) const {
+    if (n >= N || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    const int64_t t = map_index(rows, n);
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(b.codes + t * (K / 2) + k / 2);
+    const float sc = fp16_bits_to_f32(b.scales[t * (K / group) + k / group]);
+    u32x4 out;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int n0 = (c >> (8 * h)) & 15, n1 = (c >> (8 * h + 4)) & 15;
+      out[h] = pack_bf16x2((float)(n0 - ((n0 & 8) << 1)) * sc, (float)(n1 - ((n1 & 8) << 1)) * sc);
+    }
+    return out;
+  }
+  __device__ void epilogue(int, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+    const uint16_t* mu = static_cast<const uint16_t*>(b.centers);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 32 * j + (lane & 31);
+      if (n >= N) continue;
+      const int64_t a = b.idx[map_index(rows, n)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + 32 * i + acc_row(e, lane);
+          if (m < M)
+            out[(int64_t)m * ld + n] =
+                f32_to_bf16_bits(acc[i][j][e] + bf16_bits_to_f32(mu[a * M + m]));
+        }
+    }
+  }
+};
+
 nkv_status launch_decode_tuned(const BranchArgs& b, int W, int r, int group,
                                const RangeTable& rows, uint16_t* out, int64_t ld, bool transposed,
                                hipStream_t st) {
   if (rows.total == 0) return NKV_OK;
-  DecodeProblem p{(int)rows.total, W, r, group, b, rows, out, ld, transposed};
+  if (transposed) {
+    DecodeTProblem p{W, (int)rows.total, r, group, b, rows, out, ld};
+    return launch_gemm(p, 1, st);
+  }
+  DecodeProblem p{(int)rows.total, W, r, group, b, rows, out, ld, false};
   return launch_gemm(p, 1, st);
 }
 
