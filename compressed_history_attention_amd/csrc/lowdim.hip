@@ -484,13 +484,13 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
   const uint16_t* qbase = a.q + q0 * W + h * 128;
 
   // mu^K rows of the 64-center slice gk for this head
-  auto load_mu = [&](int gk) {
+  auto load_mu = [&](int gk) __attribute__((always_inline)) {
     const int valid = min(CR, a.A_k - gk * CR);
     load_rows_swizzled(a.muk + (int64_t)gk * CR * W + h * 128, W, CR, valid, sM, wave, lane);
   };
 
   // flush the masses of a finished a^V range: key halves meet in LDS
-  auto flush = [&](int gv) {
+  auto flush = [&](int gv) __attribute__((always_inline)) {
     __syncthreads();
     if (kh == 1) {
 #pragma unroll
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
 
   // T^T[center][row] = mu^K_{center,h} . q_h (exact bf16 products), scaled
   // to c T - B and written to the LDS score table
-  auto t_slice = [&](int gk) {
+  auto t_slice = [&](int gk) __attribute__((always_inline)) {
     f32x16 tt = zero16();
     const int cl0 = kh * 32 + (lane & 31);
     if constexpr (LT) {
@@ -554,7 +554,7 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
 
   int prev_gv = -1;
   // one tile: consume `cur`, start loading tile t + 1 into `nxt`
-  auto body = [&](int t, const char* cur, char* nxt) {
+  auto body = [&](int t, const char* cur, char* nxt) __attribute__((always_inline)) {
     const int b = a.tile_bucket[t];
     const int t0 = a.tile_start[b];
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -619,27 +619,33 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
     body(t, sB0, sB1);
     if (t + 1 < ntiles) body(t + 1, sB1, sB0);
   }
+  // no row or tile load may still be in flight into LDS when the block ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (prev_gv >= 0) flush(prev_gv);
   // ---- combine the key halves: coefficient sums (64 dims per pass), ell ------
 #pragma unroll
   for (int pass = 0; pass < (NPB + 1) / 2; ++pass) {
     if (kh == 1) {
 #pragma unroll
-      for (int db = 2 * pass; db < min(NPB, 2 * pass + 2); ++db)
+      for (int db = 0; db < NPB; ++db)
+        if ((db >> 1) == pass) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          sT[rloc * TS + (db - 2 * pass) * 32 + acc_row(e, lane)] = accT[db][e];
+          for (int e = 0; e < 16; ++e)
+            sT[rloc * TS + (db & 1) * 32 + acc_row(e, lane)] = accT[db][e];
+        }
     }
     __syncthreads();
     if (kh == 0 && rok) {
 #pragma unroll
-      for (int db = 2 * pass; db < min(NPB, 2 * pass + 2); ++db)
+      for (int db = 0; db < NPB; ++db)
+        if ((db >> 1) == pass) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int dim = db * 32 + acc_row(e, lane);
-          if (dim < a.r_low)
-            a.acc[grow * a.r_low + dim] =
-                accT[db][e] + sT[rloc * TS + (db - 2 * pass) * 32 + acc_row(e, lane)];
+          for (int e = 0; e < 16; ++e) {
+            const int dim = db * 32 + acc_row(e, lane);
+            if (dim < a.r_low)
+              a.acc[grow * a.r_low + dim] =
+                  accT[db][e] + sT[rloc * TS + (db & 1) * 32 + acc_row(e, lane)];
+          }
         }
     }
     __syncthreads();
@@ -785,7 +791,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   float* ell = reinterpret_cast<float*>(at(P.ell));
   nkv_status e;
   {
-  ProfScope ps_prep("low_prep", st);
+  ProfScope ps_prep("low_prep_tables", st);
 
   // zero the counters, presence flags and row maxima (kernels: capturable)
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(P.rows, 256)), dim3(256), 0, st, tmax, P.rows);
@@ -799,6 +805,9 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
                      dim3(256), 0, st, static_cast<const uint16_t*>(vb.centers), vb.A, W, W, mvt,
                      P.avp);
   NKV_LAUNCH_CHECK();
+  }
+  {
+  ProfScope ps_sort("low_prep_sort", st);
   // bucket sort of the low-routed tokens
   const int nch = (int)P.nchunk;
   hipLaunchKernelGGL(k_bucket_count, dim3(nch), dim3(256), P.NB * sizeof(int), st, kb, vb, low,
@@ -807,10 +816,16 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
                      P.NB, base, tile_start, bcount, tile_bucket);
   hipLaunchKernelGGL(k_bucket_scatter, dim3(nch), dim3(256), 0, st, kb, vb, low, P.GK, P.NB, base,
                      perm);
+  }
+  {
+  ProfScope ps_img("low_prep_images", st);
   hipLaunchKernelGGL(k_build_images, dim3((unsigned)ceil_div(P.max_slots, 256)), dim3(256), 0, st,
                      kb, vb, r, s->group, r_low, P.g, tile_start, tile_bucket, bcount, P.NB, perm,
                      img, misc);
   NKV_LAUNCH_CHECK();
+  }
+  {
+  ProfScope ps_q("low_prep_query", st);
   // query reduction and per-row score bounds
   QtProblem qp{(int)Nq, r_low, 128, H, q, dkt, qt32};
   if ((e = launch_gemm(qp, H, st))) return e;

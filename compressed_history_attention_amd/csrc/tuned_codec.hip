@@ -153,23 +153,33 @@ inline int proj_splits(int W) {
   return 1;
 }
 
-// sum the split partials in a fixed order, then quantise one group
-__global__ void k_quantize_rows(const float* __restrict__ z, int splits, int64_t N, int r,
-                                int group, uint8_t* __restrict__ codes,
-                                uint16_t* __restrict__ scales) {
-  const int ng = r / group;
+// one thread per coefficient: sum the split partials in a fixed order, then
+// quantise its group with lane shuffles (groups never straddle a wave since
+// the group size divides 64 and r is a multiple of it)
+__global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__ z, int splits,
+                                                       int64_t N, int r, int group,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint16_t* __restrict__ scales) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= N * ng) return;
-  const int64_t t = i / ng;
-  const int g = (int)(i - t * ng);
-  float zz[64];
-  const float* src = z + t * r + g * group;
-  for (int j = 0; j < group; ++j) {
-    float v = src[j];
-    for (int sp = 1; sp < splits; ++sp) v += src[(int64_t)sp * N * r + j];
-    zz[j] = v;
+  const bool ok = i < N * r;
+  float v = 0.f;
+  if (ok) {
+    v = z[i];
+    for (int sp = 1; sp < splits; ++sp) v += z[(int64_t)sp * N * r + i];
   }
-  quantize_group(zz, group, codes + t * (r / 2) + g * (group / 2), scales + t * ng + g);
+  float m = fabsf(v);
+  for (int o = group >> 1; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float u = m / 7.0f;  // IEEE division
+  const __half sh = __float2half_rn(u);
+  const float sf = __half2float(sh);
+  int c = 0;
+  if (sf > 0.f) c = (int)fminf(7.f, fmaxf(-8.f, rintf(v / sf)));
+  const int c1 = __shfl_down(c, 1, 64);
+  if (!ok) return;
+  const int64_t t = i / r;
+  const int j = (int)(i - t * r);
+  if ((j & 1) == 0) codes[t * (r / 2) + j / 2] = uint8_t((c & 15) | ((c1 & 15) << 4));
+  if (j % group == 0) scales[t * (r / group) + j / group] = __half_as_ushort(sh);
 }
 
 size_t tuned_encode_workspace(const nkv_shape* s, int64_t N, int32_t A) {
@@ -211,8 +221,7 @@ nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void
   if ((e = launch_gemm(pp, splits, st))) return e;
   }
   ProfScope ps("encode_quantize", st);
-  const int64_t ng = N * (r / s->group);
-  hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)ceil_div(ng, 256)), dim3(256), 0, st, z,
+  hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)ceil_div(N * r, 256)), dim3(256), 0, st, z,
                      splits, N, r, s->group, codes, scales);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
