@@ -35,7 +35,6 @@ namespace {
 
 constexpr int NT = 64;        // keys per tile (bucket padding unit)
 constexpr int CR = 64;        // centers per range
-constexpr int RB = 128;       // query rows per block
 constexpr int TS = 65;        // LDS row stride of the center tables (64 + sentinel)
 constexpr int CHUNK = 1024;   // tokens per counting chunk
 constexpr float BOUND_GAP_LIMIT = 60.f;  // log2 units
@@ -45,17 +44,21 @@ constexpr float BOUND_GAP_LIMIT = 60.f;  // log2 units
 //   [0, ck_bytes)        K coefficients, 64 keys x (rlp + 8) fp16 (padded rows)
 //   [cv_off, +cv_bytes)  V coefficients then the a^V one-hot, (rp + 64) x 68 bf16
 //   [ko_off, +256)       per key: byte offset of its a^K slot in the T table row
+//   [hd_off, +16)        header: the facts of the FOLLOWING tile (its bucket,
+//                        whether it opens that bucket, the a^K range of the
+//                        bucket after it or -1), so a kernel learns them while
+//                        it works on this tile; zero after the last tile
 struct TileGeom {
-  int rlp, rp, cks, cvr, ck_bytes, cv_off, cv_bytes, ko_off, bytes;
+  int rlp, rp, cks, cvr, ck_bytes, cv_off, cv_bytes, ko_off, hd_off, bytes;
 };
 constexpr int CVS = 68;
 __host__ __device__ constexpr TileGeom tile_geom(int rlp) {
   const int rp = (rlp + 31) / 32 * 32;
   const int cks = rlp + 8, cvr = rp + CR;
   const int ck_bytes = NT * cks * 2, cv_bytes = cvr * CVS * 2;
-  const int ko_off = ck_bytes + cv_bytes;
-  return TileGeom{rlp, rp, cks, cvr, ck_bytes, ck_bytes, cv_bytes, ko_off,
-                  (ko_off + NT * 4 + 1023) / 1024 * 1024};
+  const int ko_off = ck_bytes + cv_bytes, hd_off = ko_off + NT * 4;
+  return TileGeom{rlp, rp, cks, cvr, ck_bytes, ck_bytes, cv_bytes, ko_off, hd_off,
+                  (hd_off + 16 + 1023) / 1024 * 1024};
 }
 
 struct Plan {
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(BranchArgs kb, BranchArg
 __global__ __launch_bounds__(256) void k_build_images(
     BranchArgs kb, BranchArgs vb, int r, int group, int r_low, TileGeom g,
     const int32_t* __restrict__ tile_start, const int32_t* __restrict__ tile_bucket,
-    const int32_t* __restrict__ bcount, int NB, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ bcount, int NB, int GK, const int32_t* __restrict__ perm,
     char* __restrict__ img, uint32_t* __restrict__ cmax2) {
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nslots = (int64_t)tile_start[NB] * NT;
@@ -247,6 +250,17 @@ __global__ __launch_bounds__(256) void k_build_images(
   const int b = tile_bucket[tile];
   const bool real = (p - (int64_t)tile_start[b] * NT) < bcount[b];
   char* base = img + tile * g.bytes;
+  if (key == 0) {
+    const int64_t ntl = tile_start[NB];
+    u32x4 hd = {0u, 0u, 0u, 0u};
+    if (tile + 1 < ntl) {
+      const int bn = tile_bucket[tile + 1];
+      const int tn = tile_start[bn + 1];
+      hd = u32x4{(uint32_t)bn, tile + 1 == tile_start[bn] ? 1u : 0u,
+                 (uint32_t)(tn < ntl ? tile_bucket[tn] % GK : -1), 0u};
+    }
+    *reinterpret_cast<u32x4*>(base + g.hd_off) = hd;
+  }
   uint16_t* ckrow = reinterpret_cast<uint16_t*>(base) + key * g.cks;
   uint16_t* cvcol = reinterpret_cast<uint16_t*>(base + g.cv_off) + key;
   int32_t* ko = reinterpret_cast<int32_t*>(base + g.ko_off);
@@ -349,7 +363,7 @@ struct TmaxProblem {
   }
 };
 
-// per-row bound, fp16 q~, and the list of rows needing the exact fallback
+// per-row bound, fp16 c q~, and the list of rows needing the exact fallback
 __global__ void k_row_bound(const float* __restrict__ qt32, int64_t rows, int r_low, int rlp,
                             float c, const uint32_t* __restrict__ tmax,
                             const uint32_t* __restrict__ misc, float* __restrict__ bound,
@@ -368,12 +382,13 @@ __global__ void k_row_bound(const float* __restrict__ qt32, int64_t rows, int r_
   const float T = from_ordered_bits(tmax[row]);
   const float B = c * (T + 1e-5f * fabsf(T) + 1.001f * qn * cmax) + 1e-3f;
   bound[row] = B;
-  const bool bad = !(2.f * c * qn * cmax <= BOUND_GAP_LIMIT) || !(amax < 30000.f) ||
+  const bool bad = !(2.f * c * qn * cmax <= BOUND_GAP_LIMIT) || !(c * amax < 30000.f) ||
                    !(cmax < 30000.f) || !(fabsf(B) < 1e30f);
   if (bad) flags[atomicAdd(nflag, 1)] = (int32_t)row;
+  // fp16 c q~: the main kernel's score MFMA then yields c s directly
   uint16_t* o = qt16 + row * rlp;
   for (int j = 0; j < rlp; j += 2) {
-    const float a = j < r_low ? qr[j] : 0.f, b = j + 1 < r_low ? qr[j + 1] : 0.f;
+    const float a = j < r_low ? c * qr[j] : 0.f, b = j + 1 < r_low ? c * qr[j + 1] : 0.f;
     *reinterpret_cast<uint32_t*>(o + j) = pack_f16x2(a, b);
   }
 }
@@ -397,22 +412,26 @@ struct MainArgs {
   float c;
 };
 
+constexpr int RBW = 256;                // query rows per block: 8 waves x 32 rows
+constexpr int LDS_BYTES = 160 * 1024;
+
 template <int RLP>
-struct MainGeo {
+struct RowsGeo {
   static constexpr TileGeom G = tile_geom(RLP);
-  static constexpr int RP = G.rp, NPB = RP / 32, CHUNKS = G.bytes / 1024;
-  static constexpr int T_BYTES = RB * TS * 4;
-  static constexpr int Q_BYTES = RB * 256;   // the block's 128 query rows of one head (bf16)
-  static constexpr int M_BYTES = CR * 256;   // one 64-center slice of mu^K for one head (bf16)
-  // the T-slice operands live in LDS when they fit next to two tile stages
-  static constexpr bool LDS_T = 2 * G.bytes + T_BYTES + Q_BYTES + M_BYTES <= 160 * 1024;
+  static constexpr int NPB = G.rp / 32, CHUNKS = G.bytes / 1024;
+  static constexpr int T_BYTES = RBW * TS * 4;
+  static constexpr int M_BYTES = CR * 256;  // one 64-center slice of mu^K for one head (bf16)
+  // the mu^K slice is staged in LDS when it fits next to two tile stages
+  static constexpr bool SM = 2 * G.bytes + T_BYTES + M_BYTES <= LDS_BYTES;
+  static_assert(2 * G.bytes + T_BYTES <= LDS_BYTES, "tile stages exceed LDS");
+  static constexpr int DMA_PER_WAVE = (CHUNKS + 7) / 8;
 };
 
 // one wave's share of a tile: 1 KiB chunks w, w + 8, ... straight into LDS
 template <int RLP>
 __device__ __forceinline__ void load_tile(const char* __restrict__ src, char* lds, int wave,
                                           int lane) {
-  constexpr int C = MainGeo<RLP>::CHUNKS;
+  constexpr int C = RowsGeo<RLP>::CHUNKS;
 #pragma unroll
   for (int c = wave; c < C; c += 8)
     __builtin_amdgcn_global_load_lds(src + c * 1024 + lane * 16,
@@ -440,31 +459,41 @@ __device__ __forceinline__ u32x4 lds_row_block(const char* lds, int r, int j) {
   return *reinterpret_cast<const u32x4*>(lds + r * 256 + ((j ^ (r & 15)) << 4));
 }
 
+// ---------------------------------------------------------------------------
+// Main kernel.  One block = 256 query rows of one head; wave w owns rows
+// 32w..32w+31 and scores them against all 64 keys of every tile, so each
+// tile brought into LDS feeds 8 x 32 MFMAs and rows never meet across waves.
+//   S^T[key][row] = T[row][a^K] + (c q~) . c^K       (T gathered into the
+//                                                     accumulator, fp16 MFMA)
+//   p = 2^S                                          (bound B already in T)
+//   [acc^T ; M^T][coef|center][row] += [c^V ; onehot(a^V)]^T P^T   (bf16 MFMA)
+// Tiles are double buffered with direct-to-LDS loads; each wave spreads its
+// share of the next tile's loads over the first steps of its math, and the
+// header of every tile already names the bucket facts of the next one.
+// ---------------------------------------------------------------------------
 template <int RLP>
-__global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
-  using Geo = MainGeo<RLP>;
+__global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
+  using Geo = RowsGeo<RLP>;
   constexpr TileGeom G = Geo::G;
-  constexpr int RP = Geo::RP, NPB = Geo::NPB;
-  constexpr bool LT = Geo::LDS_T;
+  constexpr int NPB = Geo::NPB;
+  constexpr bool SM = Geo::SM;
   // one array per pipeline stage: the stage of every LDS access is static,
   // so the compiler can see that reading one stage does not alias the
   // direct-to-LDS loads in flight into the other
   __shared__ __attribute__((aligned(1024))) char sB0[G.bytes];
   __shared__ __attribute__((aligned(1024))) char sB1[G.bytes];
-  __shared__ __attribute__((aligned(1024))) char sQ[LT ? Geo::Q_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char sM[LT ? Geo::M_BYTES : 16];
-  __shared__ __attribute__((aligned(16))) float sT[RB * TS];
+  __shared__ __attribute__((aligned(1024))) char sM[SM ? Geo::M_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) float sT[RBW * TS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
-  const int rg = wave & 3, kh = wave >> 2;
   const int h = blockIdx.y;
   const int W = a.H * 128;
-  const int rloc = rg * 32 + (lane & 31);
-  const int64_t q0 = (int64_t)blockIdx.x * RB;
+  const int64_t q0 = (int64_t)blockIdx.x * RBW;
+  const int rloc = wave * 32 + (lane & 31);
   const int64_t qrow = q0 + rloc;
   const bool rok = qrow < a.Nq;
-  const int64_t grow = qrow * a.H + h;
-  const int nvalid = (int)min<int64_t>(RB, a.Nq - q0);
+  const bool active = q0 + wave * 32 < a.Nq;  // the wave owns at least one row
+  const int64_t grow = (rok ? qrow : q0) * a.H + h;
 
   f16x8 qtf[RLP / 16];
 #pragma unroll
@@ -481,7 +510,7 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
 
   const int ntiles = a.tile_start[a.NB];
   const char* sTrow = reinterpret_cast<const char*>(sT + rloc * TS);
-  const uint16_t* qbase = a.q + q0 * W + h * 128;
+  const uint16_t* qsrc = a.q + (rok ? qrow : q0) * W + h * 128 + 8 * hl;
 
   // mu^K rows of the 64-center slice gk for this head
   auto load_mu = [&](int gk) __attribute__((always_inline)) {
@@ -489,131 +518,217 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
     load_rows_swizzled(a.muk + (int64_t)gk * CR * W + h * 128, W, CR, valid, sM, wave, lane);
   };
 
-  // flush the masses of a finished a^V range: key halves meet in LDS
+  // the k-th of this wave's 1 KiB chunks of tile tt into `dst`
+  auto dma = [&](int tt, char* dst, int k) __attribute__((always_inline)) {
+    const int c = wave + 8 * k;
+    if (c < Geo::CHUNKS && tt < ntiles)
+      __builtin_amdgcn_global_load_lds(a.img + (int64_t)tt * G.bytes + c * 1024 + lane * 16,
+                                       (__attribute__((address_space(3))) void*)(dst + c * 1024),
+                                       16, 0, 0);
+  };
+
+  // masses of a finished a^V range straight from the accumulators
   auto flush = [&](int gv) __attribute__((always_inline)) {
-    __syncthreads();
-    if (kh == 1) {
+    if (rok) {
+      float* dst = a.wmass + grow * a.A_v + gv * CR;
+      const int lim = a.A_v - gv * CR;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sT[rloc * TS + cb * 32 + acc_row(e, lane)] = accW[cb][e];
-    }
-    __syncthreads();
-    if (kh == 0 && rok) {
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int c = cb * 32 + e4 * 8 + hl * 4;
+          if ((a.A_v & 3) == 0 && c + 4 <= lim) {
+            *reinterpret_cast<f32x4*>(dst + c) =
+                f32x4{accW[cb][4 * e4], accW[cb][4 * e4 + 1], accW[cb][4 * e4 + 2],
+                      accW[cb][4 * e4 + 3]};
+          } else {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int c = cb * 32 + acc_row(e, lane);
-          if (gv * CR + c < a.A_v)
-            a.wmass[grow * a.A_v + gv * CR + c] = accW[cb][e] + sT[rloc * TS + c];
+            for (int u = 0; u < 4; ++u)
+              if (c + u < lim) dst[c + u] = accW[cb][4 * e4 + u];
+          }
         }
     }
     accW[0] = zero16();
     accW[1] = zero16();
-    __syncthreads();
-  };
+    };
 
-  // T^T[center][row] = mu^K_{center,h} . q_h (exact bf16 products), scaled
-  // to c T - B and written to the LDS score table
+  // T[row][center] = c mu^K_{center,h} . q_h - B for the wave's rows
+  // (exact bf16 products, fp32 sums) into the wave's own rows of sT
   auto t_slice = [&](int gk) __attribute__((always_inline)) {
-    f32x16 tt = zero16();
-    const int cl0 = kh * 32 + (lane & 31);
-    if constexpr (LT) {
+    bf16x8 qv[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qv[ks] = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      f32x16 tt = zero16();
+      const int cen = gk * CR + cb * 32 + (lane & 31);
+      const uint16_t* msrc = a.muk + (int64_t)(cen < a.A_k ? cen : 0) * W + h * 128 + 8 * hl;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 m = as_bf16x8(lds_row_block(sM, cl0, 2 * ks + hl));
-        const bf16x8 qv = as_bf16x8(lds_row_block(sQ, rloc, 2 * ks + hl));
-        tt = mfma_bf16(m, qv, tt);
+        bf16x8 m;
+        if constexpr (SM)
+          m = as_bf16x8(lds_row_block(sM, cb * 32 + (lane & 31), 2 * ks + hl));
+        else
+          m = as_bf16x8(ld_u32x4(msrc + 16 * ks));
+        tt = mfma_bf16(m, qv[ks], tt);
       }
-    } else {
-      const int cen = gk * CR + cl0;
-      const bool cok = cen < a.A_k;
-      const uint16_t* msrc = a.muk + (int64_t)(cok ? cen : 0) * W + h * 128 + 8 * hl;
-      const uint16_t* qsrc = qbase + (int64_t)(rok ? rloc : 0) * W + 8 * hl;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 m = as_bf16x8(ld_u32x4(msrc + 16 * ks));
-        const bf16x8 qv = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
-        tt = mfma_bf16(m, qv, tt);
+      for (int e = 0; e < 16; ++e) {
+        const int cl = cb * 32 + acc_row(e, lane);
+        sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[e], a.c, -Bq) : -INFINITY;
       }
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int cl = kh * 32 + acc_row(e, lane);
-      sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[e], a.c, -Bq) : -INFINITY;
-    }
-    if (kh == 0 && hl == 0) sT[rloc * TS + CR] = -INFINITY;
+    if (hl == 0) sT[rloc * TS + CR] = -INFINITY;
   };
 
-  if constexpr (LT) {
-    load_rows_swizzled(qbase, W, RB, nvalid, sQ, wave, lane);
-    if (0 < ntiles) load_mu(a.tile_bucket[0] % a.GK);
+  // bucket facts of the tile about to be processed: tile 0's from the tables,
+  // every later tile's from the header of the tile before it
+  int cur_b = 0, cur_first = 0, cur_ngk = -1;
+  if (ntiles > 0) {
+    cur_b = a.tile_bucket[0];
+    cur_first = 1;
+    const int tn = a.tile_start[cur_b + 1];
+    cur_ngk = tn < ntiles ? a.tile_bucket[tn] % a.GK : -1;
+    if constexpr (SM) load_mu(cur_b % a.GK);
+    load_tile<RLP>(a.img, sB0, wave, lane);
   }
-  if (0 < ntiles) load_tile<RLP>(a.img, sB0, wave, lane);
 
   int prev_gv = -1;
-  // one tile: consume `cur`, start loading tile t + 1 into `nxt`
+  // one tile: consume `cur`, load tile t + 1 into `nxt` while computing
   auto body = [&](int t, const char* cur, char* nxt) __attribute__((always_inline)) {
-    const int b = a.tile_bucket[t];
-    const int t0 = a.tile_start[b];
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t == t0) {
+    if (cur_first) {
       // ---- new bucket: (flush,) then the T slice of its a^K range -------------
-      const int gv = b / a.GK, gk = b - gv * a.GK;
+      const int gv = cur_b / a.GK, gk = cur_b - gv * a.GK;
       if (gv != prev_gv && prev_gv >= 0) flush(prev_gv);
       prev_gv = gv;
-      t_slice(gk);
-      __syncthreads();
-      if constexpr (LT) {
-        const int tn = a.tile_start[b + 1];
-        if (tn < ntiles) load_mu(a.tile_bucket[tn] % a.GK);
+      if (active) t_slice(gk);
+      if constexpr (SM) {
+        __syncthreads();  // sM is free once every wave has its T slice
+        if (cur_ngk >= 0) load_mu(cur_ngk);
       }
     }
-    if (t + 1 < ntiles) load_tile<RLP>(a.img + (int64_t)(t + 1) * G.bytes, nxt, wave, lane);
+    // this tile's header: the bucket facts of tile t + 1
+    auto next_facts = [&]() __attribute__((always_inline)) {
+      const u32x4 hd = *reinterpret_cast<const u32x4*>(cur + G.hd_off);
+      cur_b = __builtin_amdgcn_readfirstlane((int)hd[0]);
+      cur_first = __builtin_amdgcn_readfirstlane((int)hd[1]);
+      cur_ngk = __builtin_amdgcn_readfirstlane((int)hd[2]);
+    };
+    if (!active) {
+#pragma unroll
+      for (int k = 0; k < Geo::DMA_PER_WAVE; ++k) dma(t + 1, nxt, k);
+      next_facts();
+      return;
+    }
     const uint16_t* sCK = reinterpret_cast<const uint16_t*>(cur);
     const uint16_t* sCV = reinterpret_cast<const uint16_t*>(cur + G.cv_off);
     const int32_t* sKO = reinterpret_cast<const int32_t*>(cur + G.ko_off);
-    // ---- scores S^T[key][row] = c^K . q~ (fp16 MFMA) ------------------------
-    f32x16 s = zero16();
+    // Operand batches are read into registers well ahead of their MFMAs;
+    // sched_barrier keeps the scheduler from sinking each read next to its
+    // use, which would expose a full LDS round trip per MFMA.
+    auto gather = [&](int kb, f32x16& acc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < RLP / 16; ++ks) {
-      const f16x8 ca = as_f16x8(
-          *reinterpret_cast<const u32x4*>(&sCK[(kh * 32 + (lane & 31)) * G.cks + 16 * ks + 8 * hl]));
-      s = mfma_f16(ca, qtf[ks], s);
-    }
-    // ---- p = 2^(c s + c T - B) ----------------------------------------------
-    u32x4 pk[2];
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 kov = *reinterpret_cast<const u32x4*>(&sKO[kb * 32 + g * 8 + hl * 4]);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const u32x4 kov = *reinterpret_cast<const u32x4*>(&sKO[kh * 32 + g * 8 + hl * 4]);
-      float pv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float tv = *reinterpret_cast<const float*>(sTrow + kov[u]);
-        pv[u] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + u], a.c, tv));
-        lsum += pv[u];
+        for (int u = 0; u < 4; ++u) acc[4 * g + u] = *reinterpret_cast<const float*>(sTrow + kov[u]);
       }
-      pk[g >> 1][(g & 1) * 2] = pack_bf16x2(pv[0], pv[1]);
-      pk[g >> 1][(g & 1) * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
-    }
-    const bf16x8 pb[2] = {as_bf16x8(pk[0]), as_bf16x8(pk[1])};
-    // ---- [acc^T ; M^T][coef|center][row] += [c^V ; onehot(a^V)]^T P^T -------
+    };
+    auto read_k = [&](int kb, f16x8 (&ck)[RLP / 16]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+      for (int ks = 0; ks < RLP / 16; ++ks)
+        ck[ks] = as_f16x8(*reinterpret_cast<const u32x4*>(
+            &sCK[(kb * 32 + (lane & 31)) * G.cks + 16 * ks + 8 * hl]));
+    };
+    auto score = [&](f32x16& acc, const f16x8 (&ck)[RLP / 16]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < RLP / 16; ++ks) acc = mfma_f16(ck[ks], qtf[ks], acc);
+    };
+    auto read_v = [&](int kb, int j, bf16x8 (&vo)[NPB + 2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < NPB + 2; ++db) {
-        const uint16_t* vrow = &sCV[(db * 32 + (lane & 31)) * CVS + kh * 32 + 16 * j + 4 * hl];
+        const uint16_t* vrow = &sCV[(db * 32 + (lane & 31)) * CVS + kb * 32 + 16 * j + 4 * hl];
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        const bf16x8 av = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        if (db < NPB)
-          accT[db] = mfma_bf16(av, pb[j], accT[db]);
-        else
-          accW[db - NPB] = mfma_bf16(av, pb[j], accW[db - NPB]);
+        vo[db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
+    };
+    // p = 2^S for the 16 keys of half hb of a 32-key block, packed to bf16 in
+    // the key order of the B operand
+    auto expo = [&](const f32x16& acc, int hb) __attribute__((always_inline)) {
+      u32x4 pk;
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int g = 2 * hb + g2;
+        float pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          pv[u] = __builtin_amdgcn_exp2f(acc[4 * g + u]);
+          lsum += pv[u];
+        }
+        pk[2 * g2] = pack_bf16x2(pv[0], pv[1]);
+        pk[2 * g2 + 1] = pack_bf16x2(pv[2], pv[3]);
+      }
+      return as_bf16x8(pk);
+    };
+    auto pv = [&](const bf16x8 (&vo)[NPB + 2], bf16x8 p) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < NPB; ++db) accT[db] = mfma_bf16(vo[db], p, accT[db]);
+      accW[0] = mfma_bf16(vo[NPB], p, accW[0]);
+      accW[1] = mfma_bf16(vo[NPB + 1], p, accW[1]);
+    };
+    // wide coefficient rows: one K operand set, reloaded for the second half
+    constexpr bool KDB = RLP <= 96;
+    f32x16 s0, s1;
+    f16x8 ck0[RLP / 16], ck1[KDB ? RLP / 16 : 1];
+    bf16x8 va[NPB + 2], vb[NPB + 2];
+    gather(0, s0);
+    gather(1, s1);
+    read_k(0, ck0);
+    if constexpr (KDB) read_k(1, ck1);
+    dma(t + 1, nxt, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // S^T = T + (c q~) . c^K for both key halves (fp16 MFMA)
+    if constexpr (KDB) {
+      // two independent accumulation chains, interleaved
+#pragma unroll
+      for (int ks = 0; ks < RLP / 16; ++ks) {
+        s0 = mfma_f16(ck0[ks], qtf[ks], s0);
+        s1 = mfma_f16(ck1[ks], qtf[ks], s1);
+      }
+    } else {
+      score(s0, ck0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_k(1, ck0);
+      __builtin_amdgcn_sched_barrier(0);
+      score(s1, ck0);
     }
+    read_v(0, 0, va);
+    dma(t + 1, nxt, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // [acc^T ; M^T][coef|center][row] += [c^V ; onehot(a^V)]^T P^T, 16 keys
+    // per step; each step's MFMAs overlap the exponentials of the next
+    bf16x8 p = expo(s0, 0);
+    read_v(0, 1, vb);
+    dma(t + 1, nxt, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    pv(va, p);
+    p = expo(s0, 1);
+#pragma unroll
+    for (int k = 3; k < Geo::DMA_PER_WAVE; ++k) dma(t + 1, nxt, k);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(1, 0, va);
+    pv(vb, p);
+    p = expo(s1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(1, 1, vb);
+    pv(va, p);
+    p = expo(s1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    pv(vb, p);
+    next_facts();
   };
   for (int t = 0; t < ntiles; t += 2) {
     body(t, sB0, sB1);
@@ -622,44 +737,26 @@ __global__ __launch_bounds__(512, 1) void k_low_main(const MainArgs a) {
   // no row or tile load may still be in flight into LDS when the block ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (prev_gv >= 0) flush(prev_gv);
-  // ---- combine the key halves: coefficient sums (64 dims per pass), ell ------
-#pragma unroll
-  for (int pass = 0; pass < (NPB + 1) / 2; ++pass) {
-    if (kh == 1) {
-#pragma unroll
-      for (int db = 0; db < NPB; ++db)
-        if ((db >> 1) == pass) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            sT[rloc * TS + (db & 1) * 32 + acc_row(e, lane)] = accT[db][e];
-        }
-    }
-    __syncthreads();
-    if (kh == 0 && rok) {
-#pragma unroll
-      for (int db = 0; db < NPB; ++db)
-        if ((db >> 1) == pass) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int dim = db * 32 + acc_row(e, lane);
-            if (dim < a.r_low)
-              a.acc[grow * a.r_low + dim] =
-                  accT[db][e] + sT[rloc * TS + (db & 1) * 32 + acc_row(e, lane)];
-          }
-        }
-    }
-    __syncthreads();
-  }
   lsum += __shfl_xor(lsum, 32, 64);
-  if (kh == 1 && hl == 0) sT[rloc] = lsum;
-  __syncthreads();
-  if (kh == 0 && hl == 0 && rok) a.ell[grow] = lsum + sT[rloc];
+  if (rok) {
+#pragma unroll
+    for (int db = 0; db < NPB; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int dim = db * 32 + e4 * 8 + hl * 4;  // r_low % 16 == 0: whole f32x4 or none
+        if (dim < a.r_low)
+          *reinterpret_cast<f32x4*>(a.acc + grow * a.r_low + dim) =
+              f32x4{accT[db][4 * e4], accT[db][4 * e4 + 1], accT[db][4 * e4 + 2],
+                    accT[db][4 * e4 + 3]};
+      }
+    if (hl == 0) a.ell[grow] = lsum;
+  }
 }
 
 template <int RLP>
 nkv_status launch_main(const MainArgs& m, int64_t Nq, int H, hipStream_t st) {
-  dim3 grid((unsigned)ceil_div(Nq, RB), (unsigned)H);
-  hipLaunchKernelGGL(k_low_main<RLP>, grid, dim3(512), 0, st, m);
+  dim3 grid((unsigned)ceil_div(Nq, RBW), (unsigned)H);
+  hipLaunchKernelGGL(k_low_rows<RLP>, grid, dim3(512), 0, st, m);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }
@@ -820,7 +917,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   {
   ProfScope ps_img("low_prep_images", st);
   hipLaunchKernelGGL(k_build_images, dim3((unsigned)ceil_div(P.max_slots, 256)), dim3(256), 0, st,
-                     kb, vb, r, s->group, r_low, P.g, tile_start, tile_bucket, bcount, P.NB, perm,
+                     kb, vb, r, s->group, r_low, P.g, tile_start, tile_bucket, bcount, P.NB, P.GK, perm,
                      img, misc);
   NKV_LAUNCH_CHECK();
   }

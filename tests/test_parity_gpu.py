@@ -33,6 +33,18 @@ SMALL = {
             n_full_tail=700),
     "S2d": S("C3", H=3, r=96, A=70, n_hist=1500, Nq=150, N_cur=90, chunk=500, r_low=32,
              n_full_tail=333, center_scale=0.05, seed=21),
+    # one case per tuned low-dimensional width (r_low rounded up to 16),
+    # each with a ragged second block of query rows
+    "S4": S("C3", H=2, r=160, A=90, n_hist=1200, Nq=300, N_cur=64, chunk=400, r_low=128,
+            n_full_tail=200, seed=31),
+    "S5": S("C3", H=2, r=128, A=90, n_hist=1200, Nq=300, N_cur=64, chunk=400, r_low=112,
+            n_full_tail=200, seed=32),
+    "S6": S("C3", H=2, r=128, A=90, n_hist=1200, Nq=300, N_cur=64, chunk=400, r_low=80,
+            n_full_tail=200, seed=33),
+    "S7": S("C3", H=2, r=96, A=90, n_hist=1200, Nq=300, N_cur=64, chunk=400, r_low=64,
+            n_full_tail=200, seed=34),
+    "S8": S("C3", H=2, r=64, A=90, n_hist=1200, Nq=300, N_cur=64, chunk=400, r_low=16,
+            n_full_tail=200, seed=35),
     "C0f": S("C0", mode="fast", r_low=4, n_full_tail=32),
     "C0d": S("C0", mode="fast", r_low=4, n_full_tail=32, center_scale=0.05),
 }
@@ -170,7 +182,8 @@ def test_attend_full_small(name):
 
 
 @pytest.mark.parametrize("name,drule", [("C0f", 0.5), ("C0d", 0.1), ("S2", 0.5), ("S3", 0.5),
-                                        ("S2d", 0.1)])
+                                        ("S2d", 0.1), ("S4", 0.5), ("S5", 0.5), ("S6", 0.5),
+                                        ("S7", 0.5), ("S8", 0.5)])
 def test_attend_fast_small(name, drule):
     _check_attend(name, drule=drule)
 
