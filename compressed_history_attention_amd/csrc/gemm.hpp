@@ -3,8 +3,10 @@
 //
 // Block: 256 threads (4 waves) computing a 128 x 128 tile; wave w owns the
 // 64 x 64 quadrant (w / 2, w % 2) as 2 x 2 MFMA 32x32 tiles.  K advances in
-// steps of 32 through a register-staged, double-buffered LDS pipeline.  A
-// problem type P supplies
+// steps of P::BK (32 or 64) through a register-staged, double-buffered LDS
+// pipeline.  A problem type P supplies
+//   static constexpr int BK;                       (32: more blocks per CU,
+//                                                   64: fewer barriers)
 //   int M, N, K;                                   (K % 8 == 0)
 //   __device__ u32x4 load_a(int z, int m, int k) const;  // 8 k values (bf16)
 //   __device__ u32x4 load_b(int z, int n, int k) const;  //   zero if out of range
@@ -17,31 +19,36 @@
 
 namespace nkv {
 
-constexpr int GEMM_BM = 128, GEMM_BN = 128, GEMM_BK = 32;
-constexpr int GEMM_LDS_STRIDE = GEMM_BK + 8;  // bf16 elements per LDS row (80 B)
+constexpr int GEMM_BM = 128, GEMM_BN = 128;
 
 template <class P>
 __global__ __launch_bounds__(256) void k_gemm(const P p) {
+  constexpr int GEMM_BK = P::BK;
+  constexpr int GEMM_LDS_STRIDE = GEMM_BK + 8;  // bf16 elements per LDS row
+  constexpr int GEMM_LD = GEMM_BM * GEMM_BK / 8 / 256;  // 8-value chunks per thread per operand
+  constexpr int TPR = GEMM_BK / 8;                       // threads per tile row
+  static_assert(GEMM_BK == 32 || GEMM_BK == 64, "K step");
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][GEMM_BM * GEMM_LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][GEMM_BN * GEMM_LDS_STRIDE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int z = blockIdx.z;
   const int m_blk = blockIdx.y * GEMM_BM, n_blk = blockIdx.x * GEMM_BN;
-  // global -> register staging: each thread moves 2 chunks of 8 k for A and B
-  const int ld_row0 = tid >> 2, ld_k = (tid & 3) * 8;  // rows ld_row0 and ld_row0 + 64
-  u32x4 ra[2], rb[2];
+  // global -> register staging: each thread moves GEMM_LD chunks of 8 k for A
+  // and for B: rows ld_row0 + (256 / TPR) j, k offset ld_k
+  const int ld_row0 = tid / TPR, ld_k = (tid % TPR) * 8;
+  u32x4 ra[GEMM_LD], rb[GEMM_LD];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      ra[j] = p.load_a(z, m_blk + ld_row0 + 64 * j, k0 + ld_k);
-      rb[j] = p.load_b(z, n_blk + ld_row0 + 64 * j, k0 + ld_k);
+    for (int j = 0; j < GEMM_LD; ++j) {
+      ra[j] = p.load_a(z, m_blk + ld_row0 + (256 / TPR) * j, k0 + ld_k);
+      rb[j] = p.load_b(z, n_blk + ld_row0 + (256 / TPR) * j, k0 + ld_k);
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<u32x4*>(&sA[buf][(ld_row0 + 64 * j) * GEMM_LDS_STRIDE + ld_k]) = ra[j];
-      *reinterpret_cast<u32x4*>(&sB[buf][(ld_row0 + 64 * j) * GEMM_LDS_STRIDE + ld_k]) = rb[j];
+    for (int j = 0; j < GEMM_LD; ++j) {
+      *reinterpret_cast<u32x4*>(&sA[buf][(ld_row0 + (256 / TPR) * j) * GEMM_LDS_STRIDE + ld_k]) = ra[j];
+      *reinterpret_cast<u32x4*>(&sB[buf][(ld_row0 + (256 / TPR) * j) * GEMM_LDS_STRIDE + ld_k]) = rb[j];
     }
   };
   f32x16 acc[2][2];

@@ -233,25 +233,91 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(BranchArgs kb, BranchArg
   }
 }
 
-// one thread per padded slot (key) writes its column of the tile image:
-// dequantised K coefficients (fp16 row), V coefficients and the a^V one-hot
-// (bf16 column), the T-table offset of its a^K; dummies get zeros and the
-// -inf sentinel offset.  Also max |c^K[:r_low]|^2 over real keys.
+// One block per tile writes the tile image with coalesced stores: the keys'
+// tokens, center indices and first r_low INT4 codes / fp16 scales are staged
+// in LDS, then the fp16 K rows (16-byte chunks), the bf16 V and a^V one-hot
+// rows (8-byte chunks), the T-table offsets (-inf sentinel for dummies) and
+// the header.  Also max |c^K[:r_low]|^2 over real keys.
+constexpr int IMG_MAXB = 64;   // code bytes staged per key (r_low <= 128)
+constexpr int IMG_MAXS = 16;   // scales staged per key (r_low / group, group >= 8)
 __global__ __launch_bounds__(256) void k_build_images(
     BranchArgs kb, BranchArgs vb, int r, int group, int r_low, TileGeom g,
     const int32_t* __restrict__ tile_start, const int32_t* __restrict__ tile_bucket,
     const int32_t* __restrict__ bcount, int NB, int GK, const int32_t* __restrict__ perm,
     char* __restrict__ img, uint32_t* __restrict__ cmax2) {
-  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nslots = (int64_t)tile_start[NB] * NT;
-  if (p >= nslots) return;
-  const int64_t tile = p / NT;
-  const int key = (int)(p - tile * NT);
+  __shared__ int64_t stok[NT];
+  __shared__ int sak[NT], sav[NT];
+  __shared__ __attribute__((aligned(16))) uint8_t skc[NT][IMG_MAXB], svc[NT][IMG_MAXB];
+  __shared__ uint16_t sks[NT][IMG_MAXS], svs[NT][IMG_MAXS];
+  const int64_t tile = blockIdx.x;
+  const int64_t ntl = tile_start[NB];
+  if (tile >= ntl) return;
+  const int tid = threadIdx.x;
   const int b = tile_bucket[tile];
-  const bool real = (p - (int64_t)tile_start[b] * NT) < bcount[b];
+  const int nreal = (int)max<int64_t>(0, min<int64_t>(NT, bcount[b] - (tile - tile_start[b]) * NT));
+  const int nb = r_low / 2, ns = (r_low + group - 1) / group;
+  if (tid < NT) {
+    const bool real = tid < nreal;
+    const int64_t t = real ? perm[tile * NT + tid] : -1;
+    stok[tid] = t;
+    sak[tid] = real ? kb.idx[t] : 0;
+    sav[tid] = real ? vb.idx[t] : -1;
+  }
+  __syncthreads();
+  for (int i = tid; i < NT * nb; i += 256) {
+    const int k = i / nb, j = i - k * nb;
+    const int64_t t = stok[k];
+    skc[k][j] = t >= 0 ? kb.codes[t * (r / 2) + j] : uint8_t(0);
+    svc[k][j] = t >= 0 ? vb.codes[t * (r / 2) + j] : uint8_t(0);
+  }
+  for (int i = tid; i < NT * ns; i += 256) {
+    const int k = i / ns, j = i - k * ns;
+    const int64_t t = stok[k];
+    sks[k][j] = t >= 0 ? kb.scales[t * (r / group) + j] : uint16_t(0);
+    svs[k][j] = t >= 0 ? vb.scales[t * (r / group) + j] : uint16_t(0);
+  }
+  __syncthreads();
   char* base = img + tile * g.bytes;
-  if (key == 0) {
-    const int64_t ntl = tile_start[NB];
+  // K rows: key k, coefficients 8c .. 8c + 7 (zero past r_low and for dummies)
+  const int nck = g.cks / 8;
+  for (int i = tid; i < NT * nck; i += 256) {
+    const int k = i / nck, c = i - k * nck;
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = 8 * c + u;
+      v[u] = (j < r_low && k < nreal) ? (float)code_at(skc[k], j) * fp16_bits_to_f32(sks[k][j / group])
+                                      : 0.f;
+    }
+    *reinterpret_cast<u32x4*>(base + (k * g.cks + 8 * c) * 2) =
+        u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
+              pack_f16x2(v[6], v[7])};
+  }
+  // V rows (dims, then the 64 centers of the a^V range): row j, keys 4c .. 4c + 3
+  const int ncv = CVS / 4;
+  for (int i = tid; i < g.cvr * ncv; i += 256) {
+    const int j = i / ncv, c = i - j * ncv;
+    uint16_t h[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = 4 * c + u;
+      uint16_t x = 0;
+      if (k < nreal) {
+        if (j < g.rp)
+          x = j < r_low ? f32_to_bf16_bits((float)code_at(svc[k], j) *
+                                           fp16_bits_to_f32(svs[k][j / group]))
+                        : uint16_t(0);
+        else
+          x = (sav[k] % CR == j - g.rp) ? uint16_t(0x3F80) : uint16_t(0);
+      }
+      h[u] = x;
+    }
+    *reinterpret_cast<u32x2*>(base + g.cv_off + (j * CVS + 4 * c) * 2) =
+        u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+  }
+  if (tid < NT)
+    reinterpret_cast<int32_t*>(base + g.ko_off)[tid] = tid < nreal ? (sak[tid] % CR) * 4 : CR * 4;
+  if (tid == 0) {
     u32x4 hd = {0u, 0u, 0u, 0u};
     if (tile + 1 < ntl) {
       const int bn = tile_bucket[tile + 1];
@@ -261,46 +327,21 @@ __global__ __launch_bounds__(256) void k_build_images(
     }
     *reinterpret_cast<u32x4*>(base + g.hd_off) = hd;
   }
-  uint16_t* ckrow = reinterpret_cast<uint16_t*>(base) + key * g.cks;
-  uint16_t* cvcol = reinterpret_cast<uint16_t*>(base + g.cv_off) + key;
-  int32_t* ko = reinterpret_cast<int32_t*>(base + g.ko_off);
-  if (key < CVS - NT) {  // row padding columns 64..67 of the V/one-hot rows
-    for (int j = 0; j < g.cvr; ++j) cvcol[j * CVS + NT] = 0;
-  }
-  for (int j = g.rlp; j < g.cks; ++j) ckrow[j] = 0;
-  if (!real) {
-    for (int j = 0; j < g.rlp; j += 2) *reinterpret_cast<uint32_t*>(ckrow + j) = 0u;
-    for (int j = 0; j < g.cvr; ++j) cvcol[j * CVS] = 0;
-    ko[key] = CR * 4;
-    return;
-  }
-  const int64_t t = perm[p];
-  const uint8_t* kc = kb.codes + t * (r / 2);
-  const uint16_t* ks = kb.scales + t * (r / group);
-  const uint8_t* vc = vb.codes + t * (r / 2);
-  const uint16_t* vs = vb.scales + t * (r / group);
-  float n2 = 0.f;
-  for (int j = 0; j < g.rlp; j += 2) {
-    float v0 = 0.f, v1 = 0.f;
-    if (j < r_low) {
-      v0 = (float)code_at(kc, j) * fp16_bits_to_f32(ks[j / group]);
-      v1 = (float)code_at(kc, j + 1) * fp16_bits_to_f32(ks[(j + 1) / group]);
+  static_assert(NT == 64, "one wave holds the keys of a tile");
+  if (tid < NT) {
+    float n2 = 0.f;  // fixed order: deterministic bound
+    for (int j = 0; j < r_low; ++j) {
+      const float x = (float)code_at(skc[tid], j) * fp16_bits_to_f32(sks[tid][j / group]);
+      n2 = fmaf(x, x, n2);
     }
-    n2 = fmaf(v0, v0, fmaf(v1, v1, n2));
-    *reinterpret_cast<uint32_t*>(ckrow + j) = pack_f16x2(v0, v1);
+    const float m = wave_max(tid < nreal ? n2 : 0.f);
+    if (tid == 0 && nreal > 0) atomicMax(cmax2, ordered_bits(m));
   }
-  for (int j = 0; j < g.rp; ++j) {
-    const float v = (j < r_low) ? (float)code_at(vc, j) * fp16_bits_to_f32(vs[j / group]) : 0.f;
-    cvcol[j * CVS] = f32_to_bf16_bits(v);
-  }
-  const int av = vb.idx[t] % CR;
-  for (int c = 0; c < CR; ++c) cvcol[(g.rp + c) * CVS] = (c == av) ? uint16_t(0x3F80) : uint16_t(0);
-  ko[key] = (kb.idx[t] % CR) * 4;
-  atomicMax(cmax2, ordered_bits(n2));
 }
 
 // q~ = per-head Q_h D_{K,h}[:, :r_low]  (rows = queries, cols = coefficients)
 struct QtProblem {
+  static constexpr int BK = 64;
   int M, N, K;  // Nq, r_low, 128
   int H;
   const uint16_t* q;
@@ -330,6 +371,7 @@ struct QtProblem {
 // max over centers present in the low set of q_h . mu^K_{a,h}
 // (rows = centers, cols = queries)
 struct TmaxProblem {
+  static constexpr int BK = 64;
   int M, N, K;  // A_k, Nq, 128
   int H;
   const uint16_t* muk;
@@ -363,21 +405,41 @@ struct TmaxProblem {
   }
 };
 
-// per-row bound, fp16 c q~, and the list of rows needing the exact fallback
-__global__ void k_row_bound(const float* __restrict__ qt32, int64_t rows, int r_low, int rlp,
-                            float c, const uint32_t* __restrict__ tmax,
-                            const uint32_t* __restrict__ misc, float* __restrict__ bound,
-                            uint16_t* __restrict__ qt16, int32_t* __restrict__ flags,
-                            int32_t* __restrict__ nflag) {
-  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= rows) return;
-  const float cmax = sqrtf(from_ordered_bits(misc[0]));
-  const float* qr = qt32 + row * r_low;
+// per-row bound, fp16 c q~, and the list of rows needing the exact fallback;
+// 16 lanes per row
+__global__ __launch_bounds__(256) void k_row_bound(const float* __restrict__ qt32, int64_t rows,
+                                                   int r_low, int rlp, float c,
+                                                   const uint32_t* __restrict__ tmax,
+                                                   const uint32_t* __restrict__ misc,
+                                                   float* __restrict__ bound,
+                                                   uint16_t* __restrict__ qt16,
+                                                   int32_t* __restrict__ flags,
+                                                   int32_t* __restrict__ nflag) {
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  const bool ok = row < rows;
+  const float* qr = qt32 + (ok ? row : 0) * r_low;
+  uint16_t* o = qt16 + (ok ? row : 0) * rlp;
   float n2 = 0.f, amax = 0.f;
-  for (int j = 0; j < r_low; ++j) {
-    n2 = fmaf(qr[j], qr[j], n2);
-    amax = fmaxf(amax, fabsf(qr[j]));
+  for (int j = 2 * sub; j < rlp; j += 32) {  // r_low even: a pair is wholly in or out
+    float x0 = 0.f, x1 = 0.f;
+    if (ok && j < r_low) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(qr + j);
+      x0 = v[0];
+      x1 = v[1];
+    }
+    n2 = fmaf(x0, x0, fmaf(x1, x1, n2));
+    amax = fmaxf(amax, fmaxf(fabsf(x0), fabsf(x1)));
+    // fp16 c q~: the main kernel's score MFMA then yields c s directly
+    if (ok) *reinterpret_cast<uint32_t*>(o + j) = pack_f16x2(c * x0, c * x1);
   }
+#pragma unroll
+  for (int m = 8; m > 0; m >>= 1) {
+    n2 += __shfl_xor(n2, m, 16);
+    amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+  }
+  if (!ok || sub != 0) return;
+  const float cmax = sqrtf(from_ordered_bits(misc[0]));
   const float qn = sqrtf(n2);
   const float T = from_ordered_bits(tmax[row]);
   const float B = c * (T + 1e-5f * fabsf(T) + 1.001f * qn * cmax) + 1e-3f;
@@ -385,12 +447,6 @@ __global__ void k_row_bound(const float* __restrict__ qt32, int64_t rows, int r_
   const bool bad = !(2.f * c * qn * cmax <= BOUND_GAP_LIMIT) || !(c * amax < 30000.f) ||
                    !(cmax < 30000.f) || !(fabsf(B) < 1e30f);
   if (bad) flags[atomicAdd(nflag, 1)] = (int32_t)row;
-  // fp16 c q~: the main kernel's score MFMA then yields c s directly
-  uint16_t* o = qt16 + row * rlp;
-  for (int j = 0; j < rlp; j += 2) {
-    const float a = j < r_low ? c * qr[j] : 0.f, b = j + 1 < r_low ? c * qr[j + 1] : 0.f;
-    *reinterpret_cast<uint32_t*>(o + j) = pack_f16x2(a, b);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -558,26 +614,29 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     bf16x8 qv[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qv[ks] = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
+    // two center blocks: independent accumulation chains, interleaved
+    f32x16 tt[2] = {zero16(), zero16()};
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      f32x16 tt = zero16();
-      const int cen = gk * CR + cb * 32 + (lane & 31);
-      const uint16_t* msrc = a.muk + (int64_t)(cen < a.A_k ? cen : 0) * W + h * 128 + 8 * hl;
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int cb = 0; cb < 2; ++cb) {
         bf16x8 m;
-        if constexpr (SM)
+        if constexpr (SM) {
           m = as_bf16x8(lds_row_block(sM, cb * 32 + (lane & 31), 2 * ks + hl));
-        else
-          m = as_bf16x8(ld_u32x4(msrc + 16 * ks));
-        tt = mfma_bf16(m, qv[ks], tt);
+        } else {
+          const int cen = gk * CR + cb * 32 + (lane & 31);
+          m = as_bf16x8(ld_u32x4(a.muk + (int64_t)(cen < a.A_k ? cen : 0) * W + h * 128 +
+                                 8 * hl + 16 * ks));
+        }
+        tt[cb] = mfma_bf16(m, qv[ks], tt[cb]);
       }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int cl = cb * 32 + acc_row(e, lane);
-        sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[e], a.c, -Bq) : -INFINITY;
+        sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[cb][e], a.c, -Bq) : -INFINITY;
       }
-    }
     if (hl == 0) sT[rloc * TS + CR] = -INFINITY;
   };
 
@@ -610,16 +669,15 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       }
     }
     // this tile's header: the bucket facts of tile t + 1
-    auto next_facts = [&]() __attribute__((always_inline)) {
+    {
       const u32x4 hd = *reinterpret_cast<const u32x4*>(cur + G.hd_off);
       cur_b = __builtin_amdgcn_readfirstlane((int)hd[0]);
       cur_first = __builtin_amdgcn_readfirstlane((int)hd[1]);
       cur_ngk = __builtin_amdgcn_readfirstlane((int)hd[2]);
-    };
+    }
     if (!active) {
 #pragma unroll
       for (int k = 0; k < Geo::DMA_PER_WAVE; ++k) dma(t + 1, nxt, k);
-      next_facts();
       return;
     }
     const uint16_t* sCK = reinterpret_cast<const uint16_t*>(cur);
@@ -728,7 +786,6 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     p = expo(s1, 1);
     __builtin_amdgcn_sched_barrier(0);
     pv(vb, p);
-    next_facts();
   };
   for (int t = 0; t < ntiles; t += 2) {
     body(t, sB0, sB1);
@@ -766,6 +823,7 @@ nkv_status launch_main(const MainArgs& m, int64_t Nq, int H, hipStream_t st) {
 // GEMM over K = [acc hi | acc lo | M hi | M lo] (fp32 split into bf16 pairs)
 // ---------------------------------------------------------------------------
 struct RestoreProblem {
+  static constexpr int BK = 64;
   int M, N, K;  // Nq, 128, 2 ra + 2 av
   int H, r, r_low, ra, A_v, av;
   const float* acc;
@@ -916,7 +974,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   }
   {
   ProfScope ps_img("low_prep_images", st);
-  hipLaunchKernelGGL(k_build_images, dim3((unsigned)ceil_div(P.max_slots, 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(k_build_images, dim3((unsigned)P.max_tiles), dim3(256), 0, st,
                      kb, vb, r, s->group, r_low, P.g, tile_start, tile_bucket, bcount, P.NB, P.GK, perm,
                      img, misc);
   NKV_LAUNCH_CHECK();
@@ -928,7 +986,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   if ((e = launch_gemm(qp, H, st))) return e;
   TmaxProblem tp{kb.A, (int)Nq, 128, H, static_cast<const uint16_t*>(kb.centers), q, present, tmax};
   if ((e = launch_gemm(tp, H, st))) return e;
-  hipLaunchKernelGGL(k_row_bound, dim3((unsigned)ceil_div(P.rows, 256)), dim3(256), 0, st, qt32,
+  hipLaunchKernelGGL(k_row_bound, dim3((unsigned)ceil_div(P.rows * 16, 256)), dim3(256), 0, st, qt32,
                      P.rows, r_low, P.rlp, c, tmax, misc, bound, qt16, flags,
                      reinterpret_cast<int32_t*>(misc + 1));
   NKV_LAUNCH_CHECK();

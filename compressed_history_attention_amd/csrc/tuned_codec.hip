@@ -54,6 +54,7 @@ __device__ __forceinline__ u32x4 load8_bf16(const uint16_t* base, int64_t row, i
 // distance GEMM with argmin epilogue: rows = centers, cols = tokens
 // ---------------------------------------------------------------------------
 struct DistProblem {
+  static constexpr int BK = 64;
   int M, N, K;  // M = A centers, N = tokens, K = W
   const uint16_t* mu;
   const uint16_t* x;
@@ -93,6 +94,7 @@ struct DistProblem {
 // projection GEMM: rows = tokens, cols = coefficients, K = 3 W (split terms)
 // ---------------------------------------------------------------------------
 struct ProjProblem {
+  static constexpr int BK = 32;
   int M, N, K;  // M = tokens, N = r, K = 3 W / splits (one split per grid z)
   int W;
   const uint16_t* x;
@@ -148,8 +150,8 @@ struct ProjProblem {
 // split-K factor of the projection (fixed per width, so results are
 // deterministic): the three residual terms, each possibly halved
 inline int proj_splits(int W) {
-  if ((3 * W) % (6 * GEMM_BK) == 0) return 6;
-  if ((3 * W) % (3 * GEMM_BK) == 0) return 3;
+  if ((3 * W) % (6 * ProjProblem::BK) == 0) return 6;
+  if ((3 * W) % (3 * ProjProblem::BK) == 0) return 3;
   return 1;
 }
 
@@ -231,6 +233,7 @@ nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void
 // decoder GEMM: rows = compacted tokens, cols = channels (128 = one head)
 // ---------------------------------------------------------------------------
 struct DecodeProblem {
+  static constexpr int BK = 32;
   int M, N, K;            // M = tokens in the list, N = W, K = r
   int group;
   BranchArgs b;
@@ -298,6 +301,7 @@ struct DecodeProblem {
 // lanes own tokens, so the per-head transposed V^T[h][d][token] stores are
 // contiguous along tokens.
 struct DecodeTProblem {
+  static constexpr int BK = 32;
   int M, N, K;            // M = W channels, N = tokens in the list, K = r
   int group;
   BranchArgs b;
