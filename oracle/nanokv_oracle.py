@@ -308,12 +308,23 @@ def attend_full(q: np.ndarray, kb: Branch, vb: Branch, cur_k: np.ndarray,
     return exact_attention(q, k, v, H, d, tau)
 
 
-def low_attention(q: np.ndarray, kb: Branch, vb: Branch, r_low: int, H: int,
+def head_widths(r_low, H: int) -> list:
+    """Per-head low-dimensional width: one int for every head, or one per head
+    (the deployed configurations of Table 6 mix 32, 64, 96 and 128)."""
+    if np.ndim(r_low) == 0:
+        return [int(r_low)] * H
+    widths = [int(x) for x in r_low]
+    if len(widths) != H:
+        raise ValueError("need one r_low per head")
+    return widths
+
+
+def low_attention(q: np.ndarray, kb: Branch, vb: Branch, r_low, H: int,
                   d: int, tau: float, qblock: int = 256):
     """Low-dimensional read of a history partition (Figure 4(d)).
 
     Per head h, with D_{X,h} the rows h*d..h*d+d-1 of decoder X and [:r_low]
-    the leading coefficients:
+    the leading coefficients (r_low may differ per head, Table 6):
       q~     = D_{K,h}[:, :r_low]^T q_h                  (query reduction)
       s_t    = tau * (q~ . c^K_t[:r_low] + q_h . mu^K_{a^K_t, h})
       p      = softmax_t(s)
@@ -328,14 +339,18 @@ def low_attention(q: np.ndarray, kb: Branch, vb: Branch, r_low: int, H: int,
     lse = np.full((nq, H), -np.inf)
     if nl == 0 or nq == 0:
         return o, lse
-    ck = kb.coefficients()[:, :r_low]
-    cv = vb.coefficients()[:, :r_low]
+    widths = head_widths(r_low, H)
+    ck_all = kb.coefficients()
+    cv_all = vb.coefficients()
     A_v = vb.centers.shape[0]
     onehot_v = sp.csr_matrix((np.ones(nl), (np.arange(nl), vb.idx)), shape=(nl, A_v))
     for h in range(H):
+        rl = widths[h]
+        ck = ck_all[:, :rl]
+        cv = cv_all[:, :rl]
         sl = slice(h * d, (h + 1) * d)
-        dk = kb.decoder[sl, :r_low]
-        dv = vb.decoder[sl, :r_low]
+        dk = kb.decoder[sl, :rl]
+        dv = vb.decoder[sl, :rl]
         muk = kb.centers[:, sl]
         muv = vb.centers[:, sl]
         for s0 in range(0, nq, qblock):
@@ -370,12 +385,13 @@ def route_indices(segments: Sequence[Tuple[int, int, int]], n_hist: int):
     return cat(full), cat(low)
 
 
-def attend_fast(q: np.ndarray, kb: Branch, vb: Branch, segments, r_low: int,
+def attend_fast(q: np.ndarray, kb: Branch, vb: Branch, segments, r_low,
                 cur_k: np.ndarray, cur_v: np.ndarray, H: int, d: int,
                 tau: float):
     """NanoKV-Fast (Figure 4(d)): full-routed history plus the current chunk
     through decode + exact attention, low-routed history through
-    ``low_attention``, then LSE merging of the two parts."""
+    ``low_attention`` (one width for all heads, or one per head as in the
+    deployed configurations of Table 6), then LSE merging of the two parts."""
     n_hist = kb.idx.shape[0]
     full, low = route_indices(segments, n_hist)
     kf = np.concatenate([kb.rows(full).decode(), cur_k], axis=0)

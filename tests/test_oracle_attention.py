@@ -249,6 +249,34 @@ def test_low_read_brute_force():
         np.testing.assert_allclose(l, lb, atol=1e-12)
 
 
+def test_low_read_per_head_widths_brute_force():
+    """Per-head widths (Table 6 deploys heads at different dimensions): each
+    head's columns equal the brute-force low read at that head's width."""
+    q, kb, vb, _, _, H, d = _fast_case(13, H=3, N=10, nq=2)
+    widths = [2, 8, 5]
+    o, l = oracle.low_attention(q, kb, vb, widths, H, d, 0.35)
+    for h, rl in enumerate(widths):
+        ob, lb = _brute_low(q, kb, vb, rl, H, d, 0.35)
+        sl = slice(h * d, (h + 1) * d)
+        np.testing.assert_allclose(o[:, sl], ob[:, sl], atol=1e-12)
+        np.testing.assert_allclose(l[:, h], lb[:, h], atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.low_attention(q, kb, vb, [2, 8], H, d, 0.35)
+
+
+def test_fast_per_head_full_width_head_equals_full_read():
+    """A head read at the full width r equals the full read for that head,
+    while a head at a partial width does not."""
+    q, kb, vb, ck, cv, H, d = _fast_case(14)
+    N = kb.idx.shape[0]
+    segs = [(0, 20, 1), (20, N, 0)]
+    of, lf = oracle.attend_full(q, kb, vb, ck, cv, H, d, 0.35)
+    o, l = oracle.attend_fast(q, kb, vb, segs, [kb.r, 3], ck, cv, H, d, 0.35)
+    np.testing.assert_allclose(o[:, :d], of[:, :d], atol=1e-12)
+    np.testing.assert_allclose(l[:, 0], lf[:, 0], atol=1e-12)
+    assert np.max(np.abs(o[:, d:] - of[:, d:])) > 1e-3
+
+
 def test_low_read_permutation_invariant():
     q, kb, vb, _, _, H, d = _fast_case(12)
     perm = np.random.default_rng(1).permutation(kb.idx.shape[0])
