@@ -128,11 +128,11 @@ static BranchArgs to_args(const nkv_branch* b) {
 // generic-path workspace
 // --------------------------------------------------------------------------
 struct GenericLayout {
-  size_t k, v, o_full, lse_full, o_low, lse_low, total;
+  size_t k, v, o_full, lse_full, o_low, lse_low, rows, total;
 };
 
 static GenericLayout generic_layout(const nkv_shape* s, int64_t n_full, int64_t n_low, int64_t Nq,
-                                    int64_t N_cur) {
+                                    int64_t N_cur, bool per_head = false) {
   GenericLayout L{};
   const int64_t W = (int64_t)s->H * s->d;
   size_t off = 0;
@@ -149,16 +149,51 @@ static GenericLayout generic_layout(const nkv_shape* s, int64_t n_full, int64_t 
     L.lse_full = take(sizeof(float) * Nq * s->H);
     L.o_low = take(sizeof(float) * Nq * W);
     L.lse_low = take(sizeof(float) * Nq * s->H);
+    if (per_head) L.rows = take(sizeof(int32_t) * (Nq * s->H + 1));  // row list + its length
   }
   L.total = off;
   return L;
 }
 
+// widths of a per-head call: each in [1, r]; returns the widest (0 on error)
+static int32_t check_widths(const nkv_shape* s, const int32_t* r_low_h) {
+  if (!r_low_h) {
+    set_error("r_low_h is NULL");
+    return 0;
+  }
+  if (s->H > NKV_MAX_HEADS) {
+    set_error("per-head widths support H <= %d (H=%d)", NKV_MAX_HEADS, s->H);
+    return 0;
+  }
+  int32_t mx = 0;
+  for (int h = 0; h < s->H; ++h) {
+    if (r_low_h[h] < 1 || r_low_h[h] > s->r) {
+      set_error("r_low_h[%d]=%d must be in [1, r=%d]", h, r_low_h[h], s->r);
+      return 0;
+    }
+    mx = std::max(mx, r_low_h[h]);
+  }
+  return mx;
+}
+
+// the tuned kernels serve a call when they serve every width in it
+static bool tuned_applies_all(const nkv_shape* s, int32_t r_low, const int32_t* r_low_h) {
+  if (!tuned_applies(s, r_low)) return false;
+  if (r_low_h)
+    for (int h = 0; h < s->H; ++h)
+      if (!tuned_applies(s, r_low_h[h])) return false;
+  return true;
+}
+
+static size_t workspace_common(const nkv_shape* shape, int32_t A_k, int32_t A_v, int64_t N_hist,
+                               const nkv_segment* route, int32_t n_seg, int32_t r_low,
+                               const int32_t* r_low_h, int64_t Nq, int64_t N_cur);
+
 static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, const nkv_branch* v,
                                 int64_t N_hist, const nkv_segment* route, int32_t n_seg,
-                                int32_t r_low, const void* q, int64_t Nq, const void* cur_k,
-                                const void* cur_v, int64_t N_cur, void* out, float* lse,
-                                void* ws, size_t ws_bytes, void* stream_, bool fast) {
+                                int32_t r_low, const int32_t* r_low_h, const void* q, int64_t Nq,
+                                const void* cur_k, const void* cur_v, int64_t N_cur, void* out,
+                                float* lse, void* ws, size_t ws_bytes, void* stream_, bool fast) {
   nkv_status st = check_shape(shape);
   if (st) return st;
   if ((st = check_branch(k, "K", N_hist)) || (st = check_branch(v, "V", N_hist))) return st;
@@ -169,17 +204,19 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
   if (N_cur > 0 && (!cur_k || !cur_v)) NKV_FAIL(NKV_EINVAL, "NULL current chunk with N_cur>0");
   RangeTable full, low;
   if (fast) {
+    if (r_low_h && !(r_low = check_widths(shape, r_low_h))) return NKV_EUNSUPPORTED;
     if (r_low < 1 || r_low > shape->r)
       NKV_FAIL(NKV_EUNSUPPORTED, "r_low=%d must be in [1, r=%d]", r_low, shape->r);
     if ((st = build_routes(route, n_seg, N_hist, &full, &low))) return st;
   } else {
     if ((st = build_routes(nullptr, 0, N_hist, &full, &low))) return st;
     r_low = 0;
+    r_low_h = nullptr;
   }
-  if (low.total > 0 && r_low > 512 && !tuned_applies(shape, r_low))
+  if (low.total > 0 && r_low > 512 && !tuned_applies_all(shape, r_low, r_low_h))
     NKV_FAIL(NKV_EUNSUPPORTED, "generic low-dimensional read supports r_low <= 512");
-  const size_t need = nkv_attend_workspace_size(shape, k->A, v->A, N_hist, fast ? route : nullptr,
-                                                fast ? n_seg : 0, r_low, Nq, N_cur);
+  const size_t need = workspace_common(shape, k->A, v->A, N_hist, fast ? route : nullptr,
+                                       fast ? n_seg : 0, r_low, r_low_h, Nq, N_cur);
   if (need == SIZE_MAX) return NKV_EINVAL;
   if (Nq == 0) return NKV_OK;
   if (need > 0 && (!ws || ws_bytes < need))
@@ -189,13 +226,13 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
   const int dt = shape->dtype, H = shape->H, d = shape->d, r = shape->r, g = shape->group;
   const BranchArgs kb = to_args(k), vb = to_args(v);
 
-  if (tuned_applies(shape, r_low)) {
-    return tuned_attend(shape, kb, vb, full, low, r_low, tau, q, Nq, cur_k, cur_v, N_cur, out,
-                        lse, static_cast<char*>(ws), ws_bytes, s);
+  if (tuned_applies_all(shape, r_low, low.total > 0 ? r_low_h : nullptr)) {
+    return tuned_attend(shape, kb, vb, full, low, r_low, low.total > 0 ? r_low_h : nullptr, tau, q,
+                        Nq, cur_k, cur_v, N_cur, out, lse, static_cast<char*>(ws), ws_bytes, s);
   }
 
   const int64_t W = (int64_t)H * d;
-  const GenericLayout L = generic_layout(shape, full.total, low.total, Nq, N_cur);
+  const GenericLayout L = generic_layout(shape, full.total, low.total, Nq, N_cur, r_low_h != nullptr);
   char* base = static_cast<char*>(ws);
   float* kw = reinterpret_cast<float*>(base + L.k);
   float* vw = reinterpret_cast<float*>(base + L.v);
@@ -212,10 +249,46 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
   float* ol = reinterpret_cast<float*>(base + L.o_low);
   float* ll = reinterpret_cast<float*>(base + L.lse_low);
   if ((st = launch_attention_generic(dt, true, q, Nq, H, d, tau, kw, vw, nk, of, lf, s))) return st;
-  if ((st = launch_low_generic(dt, q, Nq, H, d, r, g, r_low, tau, kb, vb, low, nullptr, nullptr,
-                               Nq * H, ol, ll, s)))
-    return st;
+  if (!r_low_h) {
+    if ((st = launch_low_generic(dt, q, Nq, H, d, r, g, r_low, tau, kb, vb, low, nullptr, nullptr,
+                                 Nq * H, ol, ll, s)))
+      return st;
+  } else {
+    // one generic launch per width over the rows of its heads
+    int32_t* rows = reinterpret_cast<int32_t*>(base + L.rows);
+    int32_t* nrows = rows + Nq * H;
+    std::vector<int> done(H, 0);
+    for (int h0 = 0; h0 < H; ++h0) {
+      if (done[h0]) continue;
+      HeadSet hs{};
+      for (int h = h0; h < H; ++h)
+        if (!done[h] && r_low_h[h] == r_low_h[h0]) {
+          hs.h[hs.n++] = h;
+          done[h] = 1;
+        }
+      if ((st = launch_head_rows(Nq, H, hs, rows, nrows, s))) return st;
+      if ((st = launch_low_generic(dt, q, Nq, H, d, r, g, r_low_h[h0], tau, kb, vb, low, rows,
+                                   nrows, Nq * hs.n, ol, ll, s)))
+        return st;
+    }
+  }
   return launch_lse_merge(Nq, H, d, of, lf, ol, ll, out, dt, lse, s);
+}
+
+static size_t workspace_common(const nkv_shape* shape, int32_t A_k, int32_t A_v, int64_t N_hist,
+                               const nkv_segment* route, int32_t n_seg, int32_t r_low,
+                               const int32_t* r_low_h, int64_t Nq, int64_t N_cur) {
+  if (check_shape(shape) || A_k < 1 || A_v < 1 || N_hist < 0 || Nq < 0 || N_cur < 0)
+    return SIZE_MAX;
+  RangeTable full, low;
+  if (build_routes(route, n_seg, N_hist, &full, &low)) return SIZE_MAX;
+  if (low.total == 0) {
+    r_low = 0;
+    r_low_h = nullptr;
+  }
+  if (tuned_applies_all(shape, r_low, r_low_h))
+    return tuned_attend_workspace(shape, A_k, A_v, full, low, r_low, Nq, N_cur);
+  return generic_layout(shape, full.total, low.total, Nq, N_cur, r_low_h != nullptr).total;
 }
 
 }  // namespace nkv
@@ -276,14 +349,28 @@ nkv_status nkv_encode(const nkv_shape* shape, const void* x, int64_t N, const vo
 size_t nkv_attend_workspace_size(const nkv_shape* shape, int32_t A_k, int32_t A_v, int64_t N_hist,
                                  const nkv_segment* route, int32_t n_seg, int32_t r_low,
                                  int64_t Nq, int64_t N_cur) {
-  if (check_shape(shape) || A_k < 1 || A_v < 1 || N_hist < 0 || Nq < 0 || N_cur < 0)
-    return SIZE_MAX;
-  RangeTable full, low;
-  if (build_routes(route, n_seg, N_hist, &full, &low)) return SIZE_MAX;
-  if (low.total == 0) r_low = 0;
-  if (tuned_applies(shape, r_low))
-    return tuned_attend_workspace(shape, A_k, A_v, full, low, r_low, Nq, N_cur);
-  return generic_layout(shape, full.total, low.total, Nq, N_cur).total;
+  return workspace_common(shape, A_k, A_v, N_hist, route, n_seg, r_low, nullptr, Nq, N_cur);
+}
+
+size_t nkv_attend_heads_workspace_size(const nkv_shape* shape, int32_t A_k, int32_t A_v,
+                                       int64_t N_hist, const nkv_segment* route, int32_t n_seg,
+                                       const int32_t* r_low_h, int64_t Nq, int64_t N_cur) {
+  if (check_shape(shape)) return SIZE_MAX;
+  const int32_t mx = check_widths(shape, r_low_h);
+  if (!mx) return SIZE_MAX;
+  return workspace_common(shape, A_k, A_v, N_hist, route, n_seg, mx, r_low_h, Nq, N_cur);
+}
+
+nkv_status nkv_attend_fast_heads(const nkv_shape* shape, const nkv_branch* k,
+                                 const nkv_branch* v, int64_t N_hist, const nkv_segment* route,
+                                 int32_t n_seg, const int32_t* r_low_h, const void* q, int64_t Nq,
+                                 const void* cur_k, const void* cur_v, int64_t N_cur, void* out,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!shape) NKV_FAIL(NKV_EINVAL, "shape is NULL");
+  if (!r_low_h) NKV_FAIL(NKV_EINVAL, "r_low_h is NULL");
+  return attend_common(shape, k, v, N_hist, route, n_seg, 0, r_low_h, q, Nq, cur_k, cur_v, N_cur,
+                       out, lse, ws, ws_bytes, stream, true);
 }
 
 nkv_status nkv_attend_full(const nkv_shape* shape, const nkv_branch* k, const nkv_branch* v,
@@ -291,8 +378,8 @@ nkv_status nkv_attend_full(const nkv_shape* shape, const nkv_branch* k, const nk
                            const void* cur_v, int64_t N_cur, void* out, float* lse, void* ws,
                            size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  return attend_common(shape, k, v, N_hist, nullptr, 0, 0, q, Nq, cur_k, cur_v, N_cur, out, lse,
-                       ws, ws_bytes, stream, false);
+  return attend_common(shape, k, v, N_hist, nullptr, 0, 0, nullptr, q, Nq, cur_k, cur_v, N_cur, out,
+                       lse, ws, ws_bytes, stream, false);
 }
 
 nkv_status nkv_attend_fast(const nkv_shape* shape, const nkv_branch* k, const nkv_branch* v,
@@ -301,8 +388,8 @@ nkv_status nkv_attend_fast(const nkv_shape* shape, const nkv_branch* k, const nk
                            int64_t N_cur, void* out, float* lse, void* ws, size_t ws_bytes,
                            void* stream) {
   g_err[0] = 0;
-  return attend_common(shape, k, v, N_hist, route, n_seg, r_low, q, Nq, cur_k, cur_v, N_cur, out,
-                       lse, ws, ws_bytes, stream, true);
+  return attend_common(shape, k, v, N_hist, route, n_seg, r_low, nullptr, q, Nq, cur_k, cur_v,
+                       N_cur, out, lse, ws, ws_bytes, stream, true);
 }
 
 nkv_status nkv_lse_merge(int64_t Nq, int32_t H, int32_t d, const float* o_a, const float* lse_a,

@@ -353,6 +353,23 @@ size_t low_generic_lds_bytes(int A_k, int A_v, int r_low, int d) {
   return (size_t)(A_k + A_v + r_low + d + 64) * sizeof(float) + 64 * sizeof(int);
 }
 
+// rows (query * H + head) of the heads in `hs`, and their count
+__global__ void k_head_rows(int64_t Nq, int H, HeadSet hs, int32_t* __restrict__ rows,
+                            int32_t* __restrict__ nrows) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *nrows = (int32_t)(Nq * hs.n);
+  if (i < Nq * hs.n) rows[i] = (int32_t)((i / hs.n) * H + hs.h[i % hs.n]);
+}
+
+nkv_status launch_head_rows(int64_t Nq, int H, const HeadSet& hs, int32_t* rows, int32_t* nrows,
+                            hipStream_t s) {
+  const int64_t n = std::max<int64_t>(Nq * hs.n, 1);
+  hipLaunchKernelGGL(k_head_rows, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, Nq, H, hs,
+                     rows, nrows);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
 nkv_status launch_low_generic(int dt, const void* q, int64_t Nq, int H, int d, int r, int group,
                               int r_low, float tau, const BranchArgs& kb, const BranchArgs& vb,
                               const RangeTable& low, const int32_t* rows,

@@ -32,6 +32,11 @@ nkv_status launch_low_generic(int dt, const void* q, int64_t Nq, int H, int d, i
                               const int32_t* nrows, int64_t max_rows, float* o_low,
                               float* lse_low, hipStream_t s);
 
+// rows (query * H + head) of the heads in hs and their count, for a
+// per-head generic low-dimensional read
+nkv_status launch_head_rows(int64_t Nq, int H, const HeadSet& hs, int32_t* rows, int32_t* nrows,
+                            hipStream_t s);
+
 // LSE merge (merge.hip)
 nkv_status launch_lse_merge(int64_t Nq, int H, int d, const float* o_a, const float* lse_a,
                             const float* o_b, const float* lse_b, void* out, int out_dt,

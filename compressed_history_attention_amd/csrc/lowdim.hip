@@ -347,15 +347,17 @@ struct QtProblem {
   const uint16_t* q;
   const uint16_t* dkt;  // [r_low, W]
   float* qt32;          // [Nq*H, r_low]
+  HeadSet hs;           // batch z serves head hs.h[z]
   __device__ u32x4 load_a(int z, int m, int k) const {
     if (m >= M) return u32x4{0u, 0u, 0u, 0u};
-    return ld_u32x4(q + (int64_t)m * H * 128 + z * 128 + k);
+    return ld_u32x4(q + (int64_t)m * H * 128 + hs.h[z] * 128 + k);
   }
   __device__ u32x4 load_b(int z, int n, int k) const {
     if (n >= N) return u32x4{0u, 0u, 0u, 0u};
-    return ld_u32x4(dkt + (int64_t)n * H * 128 + z * 128 + k);
+    return ld_u32x4(dkt + (int64_t)n * H * 128 + hs.h[z] * 128 + k);
   }
-  __device__ void epilogue(int z, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+  __device__ void epilogue(int zb, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+    const int z = hs.h[zb];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -378,15 +380,17 @@ struct TmaxProblem {
   const uint16_t* q;
   const uint32_t* present;
   uint32_t* tmax;  // [Nq*H] ordered bits
+  HeadSet hs;      // batch z serves head hs.h[z]
   __device__ u32x4 load_a(int z, int m, int k) const {
     if (m >= M) return u32x4{0u, 0u, 0u, 0u};
-    return ld_u32x4(muk + (int64_t)m * H * 128 + z * 128 + k);
+    return ld_u32x4(muk + (int64_t)m * H * 128 + hs.h[z] * 128 + k);
   }
   __device__ u32x4 load_b(int z, int n, int k) const {
     if (n >= N) return u32x4{0u, 0u, 0u, 0u};
-    return ld_u32x4(q + (int64_t)n * H * 128 + z * 128 + k);
+    return ld_u32x4(q + (int64_t)n * H * 128 + hs.h[z] * 128 + k);
   }
-  __device__ void epilogue(int z, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+  __device__ void epilogue(int zb, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+    const int z = hs.h[zb];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       float best = -INFINITY;
@@ -407,17 +411,18 @@ struct TmaxProblem {
 
 // per-row bound, fp16 c q~, and the list of rows needing the exact fallback;
 // 16 lanes per row
-__global__ __launch_bounds__(256) void k_row_bound(const float* __restrict__ qt32, int64_t rows,
-                                                   int r_low, int rlp, float c,
+__global__ __launch_bounds__(256) void k_row_bound(const float* __restrict__ qt32, int64_t Nq,
+                                                   int H, HeadSet hs, int r_low, int rlp, float c,
                                                    const uint32_t* __restrict__ tmax,
                                                    const uint32_t* __restrict__ misc,
                                                    float* __restrict__ bound,
                                                    uint16_t* __restrict__ qt16,
                                                    int32_t* __restrict__ flags,
                                                    int32_t* __restrict__ nflag) {
-  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int64_t rl = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;  // (query, head of the set)
   const int sub = threadIdx.x & 15;
-  const bool ok = row < rows;
+  const bool ok = rl < Nq * hs.n;
+  const int64_t row = ok ? (rl / hs.n) * H + hs.h[rl % hs.n] : 0;
   const float* qr = qt32 + (ok ? row : 0) * r_low;
   uint16_t* o = qt16 + (ok ? row : 0) * rlp;
   float n2 = 0.f, amax = 0.f;
@@ -466,6 +471,7 @@ struct MainArgs {
   int64_t Nq;
   int H, A_k, A_v, GK, NB, r_low;
   float c;
+  HeadSet hs;  // grid row y serves head hs.h[y]
 };
 
 constexpr int RBW = 256;                // query rows per block: 8 waves x 32 rows
@@ -542,7 +548,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   __shared__ __attribute__((aligned(16))) float sT[RBW * TS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
-  const int h = blockIdx.y;
+  const int h = a.hs.h[blockIdx.y];
   const int W = a.H * 128;
   const int64_t q0 = (int64_t)blockIdx.x * RBW;
   const int rloc = wave * 32 + (lane & 31);
@@ -811,8 +817,8 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
 }
 
 template <int RLP>
-nkv_status launch_main(const MainArgs& m, int64_t Nq, int H, hipStream_t st) {
-  dim3 grid((unsigned)ceil_div(Nq, RBW), (unsigned)H);
+nkv_status launch_main(const MainArgs& m, int64_t Nq, hipStream_t st) {
+  dim3 grid((unsigned)ceil_div(Nq, RBW), (unsigned)m.hs.n);
   hipLaunchKernelGGL(k_low_rows<RLP>, grid, dim3(512), 0, st, m);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
@@ -834,9 +840,10 @@ struct RestoreProblem {
   const float* bound;
   float* o_low;
   float* lse_low;
-  __device__ u32x4 load_a(int z, int m, int k) const {
+  HeadSet hs;  // batch z serves head hs.h[z]
+  __device__ u32x4 load_a(int zb, int m, int k) const {
     if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
-    const int64_t row = (int64_t)m * H + z;
+    const int64_t row = (int64_t)m * H + hs.h[zb];
     float v[8];
     bool lo;
     if (k < 2 * ra) {
@@ -877,9 +884,9 @@ struct RestoreProblem {
     }
     return out;
   }
-  __device__ u32x4 load_b(int z, int n, int k) const {
+  __device__ u32x4 load_b(int zb, int n, int k) const {
     if (n >= N || k >= K) return u32x4{0u, 0u, 0u, 0u};
-    const int64_t ch = (int64_t)z * 128 + n;
+    const int64_t ch = (int64_t)hs.h[zb] * 128 + n;
     if (k < 2 * ra) {
       const int j = k >= ra ? k - ra : k;
       if (j >= r_low) return u32x4{0u, 0u, 0u, 0u};
@@ -889,7 +896,8 @@ struct RestoreProblem {
     const int c = kk >= av ? kk - av : kk;
     return ld_u32x4(mvt + ch * av + c);
   }
-  __device__ void epilogue(int z, int m0, int n0, int lane, const f32x16 (&accv)[2][2]) const {
+  __device__ void epilogue(int zb, int m0, int n0, int lane, const f32x16 (&accv)[2][2]) const {
+    const int z = hs.h[zb];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -920,8 +928,13 @@ size_t low_workspace_bytes(const nkv_shape* s, int32_t A_k, int32_t A_v, const R
 
 nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
                       const RangeTable& low, int32_t r_low, float tau, const uint16_t* q,
-                      int64_t Nq, float* o_low, float* lse_low, char* ws, hipStream_t st) {
-  const Plan P = make_plan(s, kb.A, vb.A, low, r_low, Nq);
+                      int64_t Nq, float* o_low, float* lse_low, char* ws, int32_t r_low_max,
+                      const HeadSet& hs, bool first, hipStream_t st) {
+  // offsets from the widest group's plan, so that every group finds the
+  // shared sort results in the same place; geometry from this group's width
+  const Plan P = make_plan(s, kb.A, vb.A, low, r_low_max, Nq);
+  const int rlp = (int)ceil_div(r_low, 16) * 16, ra = (int)ceil_div(r_low, 32) * 32;
+  const TileGeom geom = tile_geom(rlp);
   const int H = s->H, W = H * s->d, r = s->r;
   const float c = tau * 1.4426950408889634f;
   auto at = [&](size_t off) { return ws + off; };
@@ -948,21 +961,22 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   {
   ProfScope ps_prep("low_prep_tables", st);
 
-  // zero the counters, presence flags and row maxima (kernels: capturable)
+  // zero the counters and row maxima (kernels: capturable)
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(P.rows, 256)), dim3(256), 0, st, tmax, P.rows);
-  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(kb.A, 256)), dim3(256), 0, st, present, (int64_t)kb.A);
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, st, misc, (int64_t)4);
   NKV_LAUNCH_CHECK();
-  // transposed decoder rows for the query reduction, transposed V centers
+  // transposed decoder rows for the query reduction (this width), transposed V centers
   hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(W, 64), (unsigned)ceil_div(r_low, 64)),
                      dim3(256), 0, st, static_cast<const uint16_t*>(kb.decoder), W, r_low, r, dkt, W);
-  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(P.avp, 64), (unsigned)ceil_div(W, 64)),
-                     dim3(256), 0, st, static_cast<const uint16_t*>(vb.centers), vb.A, W, W, mvt,
-                     P.avp);
+  if (first)
+    hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(P.avp, 64), (unsigned)ceil_div(W, 64)),
+                       dim3(256), 0, st, static_cast<const uint16_t*>(vb.centers), vb.A, W, W, mvt,
+                       P.avp);
   NKV_LAUNCH_CHECK();
   }
-  {
+  if (first) {
   ProfScope ps_sort("low_prep_sort", st);
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(kb.A, 256)), dim3(256), 0, st, present, (int64_t)kb.A);
   // bucket sort of the low-routed tokens
   const int nch = (int)P.nchunk;
   hipLaunchKernelGGL(k_bucket_count, dim3(nch), dim3(256), P.NB * sizeof(int), st, kb, vb, low,
@@ -975,19 +989,20 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   {
   ProfScope ps_img("low_prep_images", st);
   hipLaunchKernelGGL(k_build_images, dim3((unsigned)P.max_tiles), dim3(256), 0, st,
-                     kb, vb, r, s->group, r_low, P.g, tile_start, tile_bucket, bcount, P.NB, P.GK, perm,
+                     kb, vb, r, s->group, r_low, geom, tile_start, tile_bucket, bcount, P.NB, P.GK, perm,
                      img, misc);
   NKV_LAUNCH_CHECK();
   }
   {
   ProfScope ps_q("low_prep_query", st);
   // query reduction and per-row score bounds
-  QtProblem qp{(int)Nq, r_low, 128, H, q, dkt, qt32};
-  if ((e = launch_gemm(qp, H, st))) return e;
-  TmaxProblem tp{kb.A, (int)Nq, 128, H, static_cast<const uint16_t*>(kb.centers), q, present, tmax};
-  if ((e = launch_gemm(tp, H, st))) return e;
-  hipLaunchKernelGGL(k_row_bound, dim3((unsigned)ceil_div(P.rows * 16, 256)), dim3(256), 0, st, qt32,
-                     P.rows, r_low, P.rlp, c, tmax, misc, bound, qt16, flags,
+  QtProblem qp{(int)Nq, r_low, 128, H, q, dkt, qt32, hs};
+  if ((e = launch_gemm(qp, hs.n, st))) return e;
+  TmaxProblem tp{kb.A, (int)Nq, 128, H, static_cast<const uint16_t*>(kb.centers), q, present, tmax,
+                 hs};
+  if ((e = launch_gemm(tp, hs.n, st))) return e;
+  hipLaunchKernelGGL(k_row_bound, dim3((unsigned)ceil_div(Nq * hs.n * 16, 256)), dim3(256), 0, st,
+                     qt32, Nq, H, hs, r_low, rlp, c, tmax, misc, bound, qt16, flags,
                      reinterpret_cast<int32_t*>(misc + 1));
   NKV_LAUNCH_CHECK();
   }
@@ -995,16 +1010,16 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   {
   ProfScope ps_main("low_main", st);
   MainArgs m{q, static_cast<const uint16_t*>(kb.centers), qt16, bound, img, tile_start,
-             tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.NB, r_low, c};
-  switch (P.rlp) {
-    case 16: e = launch_main<16>(m, Nq, H, st); break;
-    case 32: e = launch_main<32>(m, Nq, H, st); break;
-    case 48: e = launch_main<48>(m, Nq, H, st); break;
-    case 64: e = launch_main<64>(m, Nq, H, st); break;
-    case 80: e = launch_main<80>(m, Nq, H, st); break;
-    case 96: e = launch_main<96>(m, Nq, H, st); break;
-    case 112: e = launch_main<112>(m, Nq, H, st); break;
-    case 128: e = launch_main<128>(m, Nq, H, st); break;
+             tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.NB, r_low, c, hs};
+  switch (rlp) {
+    case 16: e = launch_main<16>(m, Nq, st); break;
+    case 32: e = launch_main<32>(m, Nq, st); break;
+    case 48: e = launch_main<48>(m, Nq, st); break;
+    case 64: e = launch_main<64>(m, Nq, st); break;
+    case 80: e = launch_main<80>(m, Nq, st); break;
+    case 96: e = launch_main<96>(m, Nq, st); break;
+    case 112: e = launch_main<112>(m, Nq, st); break;
+    case 128: e = launch_main<128>(m, Nq, st); break;
     default: set_error("tuned low-dimensional read supports r_low <= 128"); return NKV_EUNSUPPORTED;
   }
   if (e) return e;
@@ -1012,9 +1027,9 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   // restoration
   {
   ProfScope ps_restore("low_restore", st);
-  RestoreProblem rp{(int)Nq, 128, 2 * P.ra + 2 * P.av, H, r, r_low, P.ra, vb.A, P.av, acc, wmass,
-                    static_cast<const uint16_t*>(vb.decoder), mvt, ell, bound, o_low, lse_low};
-  if ((e = launch_gemm(rp, H, st))) return e;
+  RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, r, r_low, ra, vb.A, P.av, acc, wmass,
+                    static_cast<const uint16_t*>(vb.decoder), mvt, ell, bound, o_low, lse_low, hs};
+  if ((e = launch_gemm(rp, hs.n, st))) return e;
   }
   // rows whose bound may be loose: exact generic recomputation
   ProfScope ps_fallback("low_fallback", st);

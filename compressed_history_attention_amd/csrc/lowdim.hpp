@@ -7,9 +7,14 @@ namespace nkv {
 
 size_t low_workspace_bytes(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& low,
                            int32_t r_low, int64_t Nq);
-// Writes O_low fp32 [Nq, W] and LSE_low [Nq, H] for the low-routed tokens.
+// Writes the columns of O_low fp32 [Nq, W] and LSE_low [Nq, H] of the heads
+// in `hs` for the low-routed tokens, all read at width r_low; the workspace
+// is laid out for the widest group, r_low_max.  `first` runs
+// the width-independent preparation (bucket sort, transposed V centers);
+// further calls on the same workspace for other head groups reuse it.
 nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
                       const RangeTable& low, int32_t r_low, float tau, const uint16_t* q,
-                      int64_t Nq, float* o_low, float* lse_low, char* ws, hipStream_t st);
+                      int64_t Nq, float* o_low, float* lse_low, char* ws, int32_t r_low_max,
+                      const HeadSet& hs, bool first, hipStream_t st);
 
 }  // namespace nkv

@@ -43,6 +43,14 @@ struct RangeTable {
   int64_t prefix[NKV_MAX_SEGMENTS + 1];       // prefix[k] = start in compacted order
 };
 
+// The heads one launch serves (a group of equal low-dimensional width in a
+// per-head call, or every head), passed by value in kernel arguments.
+constexpr int NKV_MAX_HEADS = 128;
+struct HeadSet {
+  int32_t n;
+  int32_t h[NKV_MAX_HEADS];
+};
+
 __device__ __forceinline__ int64_t map_index(const RangeTable& t, int64_t j) {
   int k = 0;
   while (k + 1 < t.n && t.prefix[k + 1] <= j) ++k;

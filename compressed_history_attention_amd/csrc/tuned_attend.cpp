@@ -49,10 +49,10 @@ size_t tuned_attend_workspace(const nkv_shape* s, int32_t A_k, int32_t A_v, cons
 }
 
 nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
-                        const RangeTable& full, const RangeTable& low, int32_t r_low, float tau,
-                        const void* q, int64_t Nq, const void* cur_k, const void* cur_v,
-                        int64_t N_cur, void* out, float* lse, char* ws, size_t ws_bytes,
-                        hipStream_t st) {
+                        const RangeTable& full, const RangeTable& low, int32_t r_low,
+                        const int32_t* r_low_h, float tau, const void* q, int64_t Nq,
+                        const void* cur_k, const void* cur_v, int64_t N_cur, void* out,
+                        float* lse, char* ws, size_t ws_bytes, hipStream_t st) {
   const Layout L = make_layout(s, kb.A, vb.A, full, low, r_low, Nq, N_cur);
   const int H = s->H, W = H * s->d;
   uint16_t* kall = reinterpret_cast<uint16_t*>(ws + L.kall);
@@ -83,7 +83,26 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
     ProfScope ps("flash", st);
     if ((e = launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, st))) return e;
   }
-  if ((e = launch_low(s, kb, vb, low, r_low, tau, qb, Nq, ol, ll, ws + L.low, st))) return e;
+  // heads grouped by width (one group when every head shares r_low), in the
+  // order their widths first appear; r_low is the widest
+  int widths[NKV_MAX_HEADS];
+  HeadSet groups[NKV_MAX_HEADS];
+  int ng = 0;
+  for (int h = 0; h < H; ++h) {
+    const int w = r_low_h ? r_low_h[h] : r_low;
+    int g = 0;
+    while (g < ng && widths[g] != w) ++g;
+    if (g == ng) {
+      widths[ng] = w;
+      groups[ng].n = 0;
+      ++ng;
+    }
+    groups[g].h[groups[g].n++] = h;
+  }
+  for (int g = 0; g < ng; ++g)
+    if ((e = launch_low(s, kb, vb, low, widths[g], tau, qb, Nq, ol, ll, ws + L.low, r_low,
+                        groups[g], g == 0, st)))
+      return e;
   ProfScope ps("merge", st);
   return launch_lse_merge(Nq, H, s->d, of, lf, ol, ll, out, NKV_BF16, lse, st);
 }

@@ -16,6 +16,7 @@ import os
 from dataclasses import dataclass
 from typing import Optional, Sequence, Tuple
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,10 @@ def load() -> ctypes.CDLL:
         "nkv_attend_full": (ctypes.c_int, [SH, BR, BR, I64, P, I64, P, P, I64, P, P, P, SZ, P]),
         "nkv_attend_fast": (ctypes.c_int, [SH, BR, BR, I64, SG, I32, I32, P, I64, P, P, I64, P,
                                            P, P, SZ, P]),
+        "nkv_attend_heads_workspace_size": (SZ, [SH, I32, I32, I64, SG, I32, ctypes.POINTER(I32),
+                                                 I64, I64]),
+        "nkv_attend_fast_heads": (ctypes.c_int, [SH, BR, BR, I64, SG, I32, ctypes.POINTER(I32), P,
+                                                 I64, P, P, I64, P, P, P, SZ, P]),
         "nkv_lse_merge": (ctypes.c_int, [I64, I32, I32, P, P, P, P, P, I32, P, P]),
         "nkv_profile_enable": (None, [ctypes.c_int]),
         "nkv_profile_read": (ctypes.c_int, [ctypes.POINTER(nkv_prof_entry), I32]),
@@ -94,8 +99,8 @@ def load() -> ctypes.CDLL:
 
 EXPORTS = ("nkv_version", "nkv_last_error", "nkv_status_string", "nkv_force_generic",
            "nkv_encode_workspace_size", "nkv_encode", "nkv_attend_workspace_size",
-           "nkv_attend_full", "nkv_attend_fast", "nkv_lse_merge", "nkv_profile_enable",
-           "nkv_profile_read")
+           "nkv_attend_full", "nkv_attend_fast", "nkv_attend_heads_workspace_size",
+           "nkv_attend_fast_heads", "nkv_lse_merge", "nkv_profile_enable", "nkv_profile_read")
 
 
 def _check(status: int):
@@ -218,6 +223,35 @@ def nkv_attend_workspace_size(shape: Shape, A_k: int, A_v: int, N_hist: int, rou
     return res
 
 
+def _widths(shape: Shape, r_low_h):
+    arr = (ctypes.c_int32 * shape.H)(*[int(x) for x in r_low_h])
+    if len(r_low_h) != shape.H:
+        raise ValueError(f"need {shape.H} per-head widths, got {len(r_low_h)}")
+    return arr
+
+
+def nkv_attend_heads_workspace_size(shape: Shape, A_k: int, A_v: int, N_hist: int, route,
+                                    r_low_h, Nq: int, N_cur: int) -> int:
+    segs, n = _segments(route)
+    res = load().nkv_attend_heads_workspace_size(ctypes.byref(shape.c()), A_k, A_v, N_hist, segs,
+                                                 n, _widths(shape, r_low_h), Nq, N_cur)
+    if res == SIZE_MAX:
+        raise NkvError(1, load().nkv_last_error().decode() or "invalid attend arguments")
+    return res
+
+
+def nkv_attend_fast_heads(shape: Shape, k: Branch, v: Branch, N_hist: int, route, r_low_h, q,
+                          cur_k, cur_v, out, lse, ws=None, stream=None):
+    N_cur = 0 if cur_k is None else int(cur_k.shape[0])
+    segs, n = _segments(route)
+    _check(load().nkv_attend_fast_heads(ctypes.byref(shape.c()), ctypes.byref(k.c()),
+                                        ctypes.byref(v.c()), N_hist, segs, n,
+                                        _widths(shape, r_low_h), _ptr(q), int(q.shape[0]),
+                                        _ptr(cur_k), _ptr(cur_v), N_cur, _ptr(out), _ptr(lse),
+                                        _ptr(ws), 0 if ws is None else ws.numel(),
+                                        _stream(stream)))
+
+
 def nkv_attend_full(shape: Shape, k: Branch, v: Branch, N_hist: int, q, cur_k, cur_v, out, lse,
                     ws=None, stream=None):
     N_cur = 0 if cur_k is None else int(cur_k.shape[0])
@@ -280,12 +314,21 @@ def attend_full(shape: Shape, k: Branch, v: Branch, N_hist: int, q, cur_k=None, 
     return out, lse
 
 
-def attend_fast(shape: Shape, k: Branch, v: Branch, N_hist: int, route, r_low: int, q,
+def attend_fast(shape: Shape, k: Branch, v: Branch, N_hist: int, route, r_low, q,
                 cur_k=None, cur_v=None, ws=None, stream=None):
+    """r_low: one width for every head, or a sequence of one width per head
+    (nkv_attend_fast_heads)."""
     Nq = int(q.shape[0])
     N_cur = 0 if cur_k is None else int(cur_k.shape[0])
     out = torch.empty((Nq, shape.W), dtype=shape.torch_dtype, device=q.device)
     lse = torch.empty((Nq, shape.H), dtype=torch.float32, device=q.device)
+    if not isinstance(r_low, (int, np.integer)):
+        if ws is None:
+            ws = _workspace(nkv_attend_heads_workspace_size(shape, k.A, v.A, N_hist, route, r_low,
+                                                            Nq, N_cur), q.device)
+        nkv_attend_fast_heads(shape, k, v, N_hist, route, r_low, q, cur_k, cur_v, out, lse,
+                              ws=ws, stream=stream)
+        return out, lse
     if ws is None:
         ws = _workspace(nkv_attend_workspace_size(shape, k.A, v.A, N_hist, route, r_low, Nq,
                                                   N_cur), q.device)

@@ -160,6 +160,33 @@ nkv_status nkv_attend_fast(const nkv_shape* shape, const nkv_branch* k,
                            int64_t N_cur, void* out, float* lse, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Workspace bytes for nkv_attend_fast_heads with the same arguments;
+ * SIZE_MAX if the arguments are invalid. */
+size_t nkv_attend_heads_workspace_size(const nkv_shape* shape, int32_t A_k,
+                                       int32_t A_v, int64_t N_hist,
+                                       const nkv_segment* route, int32_t n_seg,
+                                       const int32_t* r_low_h, int64_t Nq,
+                                       int64_t N_cur);
+
+/*
+ * NanoKV-Fast with a low-dimensional width per head (the deployed
+ * configurations mix heads read at 32, 64, 96 and 128 dimensions; Table 6 of
+ * the NanoKV page): identical to nkv_attend_fast except that head h reads
+ * the NKV_LOW segments with the leading r_low_h[h] coefficients.  r_low_h is
+ * a host array of H ints, each in [1, r], read before the call returns; H
+ * may be at most 128 (NKV_EUNSUPPORTED otherwise, or for a width outside
+ * [1, r]).  Heads of equal width share one pass of the low-dimensional
+ * kernels.
+ */
+nkv_status nkv_attend_fast_heads(const nkv_shape* shape, const nkv_branch* k,
+                                 const nkv_branch* v, int64_t N_hist,
+                                 const nkv_segment* route, int32_t n_seg,
+                                 const int32_t* r_low_h, const void* q,
+                                 int64_t Nq, const void* cur_k,
+                                 const void* cur_v, int64_t N_cur, void* out,
+                                 float* lse, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /*
  * LSE merge of two partial attentions over disjoint key sets (Figure 4(d)):
  *   L = log(exp(L_a) + exp(L_b)),  O = exp(L_a - L) O_a + exp(L_b - L) O_b.

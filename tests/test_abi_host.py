@@ -100,6 +100,36 @@ def test_attend_validation():
     assert _attend_fast(sh, ok_route, Nq=0, ws=FAKE, wsb=need) == 0
 
 
+def _attend_heads(shape, widths, route=((0, 6, 1), (6, 10, 0)), Nq=4, ws=None, wsb=0):
+    L = lib.load()
+    segs, n = lib._segments(list(route))
+    arr = None if widths is None else (ctypes.c_int32 * len(widths))(*widths)
+    return L.nkv_attend_fast_heads(ctypes.byref(shape), ctypes.byref(_branch()),
+                                   ctypes.byref(_branch()), 10, segs, n, arr, FAKE, Nq, FAKE,
+                                   FAKE, 2, FAKE, FAKE, ws, wsb, None)
+
+
+def test_attend_heads_validation():
+    L = lib.load()
+    sh = _shape(H=2)
+    assert _attend_heads(sh, None) == EINVAL                   # no widths
+    assert _attend_heads(sh, [16, 0]) == EUNSUP                # width below 1
+    assert _attend_heads(sh, [16, 65]) == EUNSUP               # width above r
+    assert _attend_heads(sh, [16, 32]) == EWS                  # valid, workspace missing
+    assert _attend_heads(_shape(H=129, d=16, r=64, group=32), [16] * 129) == EUNSUP
+    segs, n = lib._segments([(0, 6, 1), (6, 10, 0)])
+    w = (ctypes.c_int32 * 2)(16, 48)
+    need = L.nkv_attend_heads_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, w, 4, 2)
+    assert need != lib.SIZE_MAX and need > 0
+    bad = (ctypes.c_int32 * 2)(16, 99)
+    assert L.nkv_attend_heads_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, bad, 4, 2) \
+        == lib.SIZE_MAX
+    # the widest head sizes the workspace: never smaller than the uniform call at that width
+    uni = L.nkv_attend_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, 48, 4, 2)
+    assert need >= uni
+    assert _attend_heads(sh, [16, 48], Nq=0, ws=FAKE, wsb=need) == 0
+
+
 def test_attend_full_validation():
     L = lib.load()
     sh = _shape()

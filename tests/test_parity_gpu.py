@@ -45,6 +45,11 @@ SMALL = {
             n_full_tail=200, seed=34),
     "S8": S("C3", H=2, r=64, A=90, n_hist=1200, Nq=300, N_cur=64, chunk=400, r_low=16,
             n_full_tail=200, seed=35),
+    # per-head widths and Table 7-style routing (anchors + recent frames)
+    "S9": S("C3", H=4, r=160, A=90, n_hist=1200, Nq=300, N_cur=64, chunk=400, r_low=128,
+            n_full_tail=200, seed=36),
+    "S10": S("C3", H=4, r=128, A=90, n_hist=2000, Nq=260, N_cur=100, chunk=100, r_low=64,
+             n_full_tail=400, seed=37),
     "C0f": S("C0", mode="fast", r_low=4, n_full_tail=32),
     "C0d": S("C0", mode="fast", r_low=4, n_full_tail=32, center_scale=0.05),
 }
@@ -186,6 +191,43 @@ def test_attend_full_small(name):
                                         ("S7", 0.5), ("S8", 0.5)])
 def test_attend_fast_small(name, drule):
     _check_attend(name, drule=drule)
+
+
+# The deployed Fast configurations read heads at different dimensions
+# (NanoKV page, Table 6: 32 / 64 / 96 / 128); a width that is not a multiple
+# of 16 sends the whole call through the generic kernels.
+@pytest.mark.parametrize("widths", [[32, 64, 96, 128], [128, 32, 32, 80], [24, 64, 96, 40]])
+def test_attend_fast_per_head_widths(widths):
+    _check_attend("S9", r_low=widths, drule=0.5)
+
+
+def test_per_head_equal_widths_match_uniform():
+    case = get_case(_cfg("S9"))
+    out_u, lse_u, _ = _run_attend(case, r_low=64)
+    out_h, lse_h, _ = _run_attend(case, r_low=[64] * 4)
+    assert np.array_equal(out_u, out_h) and np.array_equal(lse_u, lse_h)
+
+
+def _anchor_route(n_chunks, chunk, recent=4, every=16):
+    """Table 7-style routing: the last `recent` frames and one anchor frame
+    per `every` older frames are read at full dimension, the rest low."""
+    modes = [0 if (c >= n_chunks - recent or c % every == 0) else 1 for c in range(n_chunks)]
+    segs, start = [], 0
+    for c in range(1, n_chunks + 1):
+        if c == n_chunks or modes[c] != modes[start]:
+            segs.append((start * chunk, c * chunk, modes[start]))
+            start = c
+    return segs
+
+
+def test_attend_fast_anchor_routing_per_head():
+    route = _anchor_route(20, 100, recent=4, every=8)
+    assert sum(m == 0 for _, _, m in route) >= 3   # anchors split the low history
+    _check_attend("S10", route=route, r_low=[32, 96, 64, 128], drule=0.5)
+
+
+def test_attend_fast_C3_table6_widths():
+    _check_attend("C3", sample=40, r_low=[32, 64, 96, 128] * 6, drule=0.5)
 
 
 def test_attend_full_C1():
