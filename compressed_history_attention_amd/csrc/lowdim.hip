@@ -40,24 +40,30 @@ constexpr int CHUNK = 1024;   // tokens per counting chunk
 constexpr float BOUND_GAP_LIMIT = 60.f;  // log2 units
 
 // Tile image: the exact LDS layout the main kernel consumes, so a tile moves
-// from HBM/L2 to LDS with plain 1 KiB direct-to-LDS loads.
-//   [0, ck_bytes)        K coefficients, 64 keys x (rlp + 8) fp16 (padded rows)
-//   [cv_off, +cv_bytes)  V coefficients then the a^V one-hot, (rp + 64) x 68 bf16
+// from HBM/L2 to LDS with plain 1 KiB direct-to-LDS loads.  Both operand
+// regions are fragment-major: every MFMA operand fragment is one 1 KiB chunk
+// in which lane l's 16 bytes sit at l * 16 (one conflict-free ds_read_b128).
+//   [0, ck_bytes)        K coefficients (fp16): chunk (kb, ks) holds key
+//                        kb*32 + l%32, coefficients 16 ks + 8 (l/32) .. +7
+//   [cv_off, +cv_bytes)  V coefficients, then the a^V one-hot over the 64
+//                        centers of the range (bf16): chunk (kb, j, db) holds
+//                        row db*32 + l%32 (a coefficient, or a center for
+//                        db >= rp/32) for keys kb*32 + 16 j + 4 (l/32) + {0..3}
+//                        and the same + 8 (the key order of P in registers)
 //   [ko_off, +256)       per key: byte offset of its a^K slot in the T table row
 //   [hd_off, +16)        header: the facts of the FOLLOWING tile (its bucket,
 //                        whether it opens that bucket, the a^K range of the
 //                        bucket after it or -1), so a kernel learns them while
 //                        it works on this tile; zero after the last tile
 struct TileGeom {
-  int rlp, rp, cks, cvr, ck_bytes, cv_off, cv_bytes, ko_off, hd_off, bytes;
+  int rlp, rp, nks, nvb, ck_bytes, cv_off, cv_bytes, ko_off, hd_off, bytes;
 };
-constexpr int CVS = 68;
 __host__ __device__ constexpr TileGeom tile_geom(int rlp) {
   const int rp = (rlp + 31) / 32 * 32;
-  const int cks = rlp + 8, cvr = rp + CR;
-  const int ck_bytes = NT * cks * 2, cv_bytes = cvr * CVS * 2;
+  const int nks = rlp / 16, nvb = rp / 32 + CR / 32;  // K steps; V + one-hot row blocks
+  const int ck_bytes = (NT / 32) * nks * 1024, cv_bytes = (NT / 32) * 2 * nvb * 1024;
   const int ko_off = ck_bytes + cv_bytes, hd_off = ko_off + NT * 4;
-  return TileGeom{rlp, rp, cks, cvr, ck_bytes, ck_bytes, cv_bytes, ko_off, hd_off,
+  return TileGeom{rlp, rp, nks, nvb, ck_bytes, ck_bytes, cv_bytes, ko_off, hd_off,
                   (hd_off + 16 + 1023) / 1024 * 1024};
 }
 
@@ -278,42 +284,49 @@ __global__ __launch_bounds__(256) void k_build_images(
   }
   __syncthreads();
   char* base = img + tile * g.bytes;
-  // K rows: key k, coefficients 8c .. 8c + 7 (zero past r_low and for dummies)
-  const int nck = g.cks / 8;
-  for (int i = tid; i < NT * nck; i += 256) {
-    const int k = i / nck, c = i - k * nck;
+  // K fragments: chunk (kb, ks), lane l -> key kb*32 + l%32, coefficients
+  // 16 ks + 8 (l/32) .. + 7 (zero past r_low and for dummies)
+  for (int i = tid; i < (NT / 32) * g.nks * 64; i += 256) {
+    const int ch = i >> 6, l = i & 63;
+    const int kb = ch / g.nks, ks = ch - kb * g.nks;
+    const int k = kb * 32 + (l & 31), j0 = 16 * ks + 8 * (l >> 5);
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int j = 8 * c + u;
+      const int j = j0 + u;
       v[u] = (j < r_low && k < nreal) ? (float)code_at(skc[k], j) * fp16_bits_to_f32(sks[k][j / group])
                                       : 0.f;
     }
-    *reinterpret_cast<u32x4*>(base + (k * g.cks + 8 * c) * 2) =
+    *reinterpret_cast<u32x4*>(base + ch * 1024 + l * 16) =
         u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
               pack_f16x2(v[6], v[7])};
   }
-  // V rows (dims, then the 64 centers of the a^V range): row j, keys 4c .. 4c + 3
-  const int ncv = CVS / 4;
-  for (int i = tid; i < g.cvr * ncv; i += 256) {
-    const int j = i / ncv, c = i - j * ncv;
-    uint16_t h[4];
+  // V fragments: chunk (kb, j, db), lane l -> row db*32 + l%32 (coefficient,
+  // or center of the range for db >= rp/32), keys kb*32 + 16 j + 4 (l/32) +
+  // {0..3} and + 8 + {0..3}
+  for (int i = tid; i < (NT / 32) * 2 * g.nvb * 64; i += 256) {
+    const int ch = i >> 6, l = i & 63;
+    const int kbj = ch / g.nvb, db = ch - kbj * g.nvb;
+    const int row = db * 32 + (l & 31);
+    const int kq = (kbj >> 1) * 32 + 16 * (kbj & 1) + 4 * (l >> 5);
+    uint16_t hv[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = 4 * c + u;
+    for (int u = 0; u < 8; ++u) {
+      const int k = kq + (u & 3) + 8 * (u >> 2);
       uint16_t x = 0;
       if (k < nreal) {
-        if (j < g.rp)
-          x = j < r_low ? f32_to_bf16_bits((float)code_at(svc[k], j) *
-                                           fp16_bits_to_f32(svs[k][j / group]))
-                        : uint16_t(0);
+        if (row < g.rp)
+          x = row < r_low ? f32_to_bf16_bits((float)code_at(svc[k], row) *
+                                             fp16_bits_to_f32(svs[k][row / group]))
+                          : uint16_t(0);
         else
-          x = (sav[k] % CR == j - g.rp) ? uint16_t(0x3F80) : uint16_t(0);
+          x = (sav[k] % CR == row - g.rp) ? uint16_t(0x3F80) : uint16_t(0);
       }
-      h[u] = x;
+      hv[u] = x;
     }
-    *reinterpret_cast<u32x2*>(base + g.cv_off + (j * CVS + 4 * c) * 2) =
-        u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+    *reinterpret_cast<u32x4*>(base + g.cv_off + ch * 1024 + l * 16) =
+        u32x4{uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16),
+              uint32_t(hv[4]) | (uint32_t(hv[5]) << 16), uint32_t(hv[6]) | (uint32_t(hv[7]) << 16)};
   }
   if (tid < NT)
     reinterpret_cast<int32_t*>(base + g.ko_off)[tid] = tid < nreal ? (sak[tid] % CR) * 4 : CR * 4;
@@ -686,8 +699,6 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       for (int k = 0; k < Geo::DMA_PER_WAVE; ++k) dma(t + 1, nxt, k);
       return;
     }
-    const uint16_t* sCK = reinterpret_cast<const uint16_t*>(cur);
-    const uint16_t* sCV = reinterpret_cast<const uint16_t*>(cur + G.cv_off);
     const int32_t* sKO = reinterpret_cast<const int32_t*>(cur + G.ko_off);
     // Operand batches are read into registers well ahead of their MFMAs;
     // sched_barrier keeps the scheduler from sinking each read next to its
@@ -704,7 +715,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
 #pragma unroll
       for (int ks = 0; ks < RLP / 16; ++ks)
         ck[ks] = as_f16x8(*reinterpret_cast<const u32x4*>(
-            &sCK[(kb * 32 + (lane & 31)) * G.cks + 16 * ks + 8 * hl]));
+            cur + (kb * G.nks + ks) * 1024 + lane * 16));
     };
     auto score = [&](f32x16& acc, const f16x8 (&ck)[RLP / 16]) __attribute__((always_inline)) {
 #pragma unroll
@@ -712,12 +723,9 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     };
     auto read_v = [&](int kb, int j, bf16x8 (&vo)[NPB + 2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < NPB + 2; ++db) {
-        const uint16_t* vrow = &sCV[(db * 32 + (lane & 31)) * CVS + kb * 32 + 16 * j + 4 * hl];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        vo[db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-      }
+      for (int db = 0; db < NPB + 2; ++db)
+        vo[db] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            cur + G.cv_off + ((kb * 2 + j) * G.nvb + db) * 1024 + lane * 16));
     };
     // p = 2^S for the 16 keys of half hb of a 32-key block, packed to bf16 in
     // the key order of the B operand
