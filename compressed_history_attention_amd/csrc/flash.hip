@@ -78,17 +78,44 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
   for (int64_t tile = 0; tile < ntiles; ++tile) {
     const int buf = (int)(tile & 1);
     if (tile + 1 < ntiles) fetch((tile + 1) * FA_KT);
-    // ---- S^T = K Q^T ------------------------------------------------------
+    // ---- S^T = K Q^T: K fragments read four k-steps ahead of their MFMAs ----
+    // (sched_barrier keeps each batch of reads ahead of the MFMAs using it)
     f32x16 s[2] = {zero16(), zero16()};
+    auto read_k4 = [&](int ks0, bf16x8 (&kf)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            &sK[buf][(kb * 32 + (lane & 31)) * FA_KS + 16 * ks + 8 * hl]));
-        s[kb] = mfma_bf16(a, qf[ks], s[kb]);
+        for (int u = 0; u < 4; ++u)
+          kf[kb][u] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              &sK[buf][(kb * 32 + (lane & 31)) * FA_KS + 16 * (ks0 + u) + 8 * hl]));
+    };
+    auto read_v4 = [&](int j, bf16x8 (&vf)[4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint16_t* vrow = &sV[buf][(db * 32 + (lane & 31)) * FA_VS + 16 * j + 4 * hl];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+        vf[db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
+    };
+    {
+      bf16x8 k0[2][4], k1[2][4];
+      read_k4(0, k0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_k4(4, k1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(k0[kb][u], qf[u], s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(k1[kb][u], qf[4 + u], s[kb]);
     }
+    bf16x8 va[4], vb[4];
+    read_v4(0, va);
+    __builtin_amdgcn_sched_barrier(0);
     if ((tile + 1) * FA_KT > Nk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -112,34 +139,41 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       m_run = mt;
     }
-    bf16x8 pb[4];
+    // P for 16 keys (step j: key block j/2, half j%2), packed to bf16 in the
+    // key order of the B operand
+    auto probs = [&](int j) __attribute__((always_inline)) {
+      const int kb = j >> 1, half = j & 1;
+      u32x4 pk;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 pk;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * u], c, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * u + 1], c, -m_run));
-          l_part += p0 + p1;
-          pk[u] = pack_bf16x2(p0, p1);
-        }
-        pb[2 * kb + half] = as_bf16x8(pk);
+      for (int u = 0; u < 4; ++u) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * u], c, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * u + 1], c, -m_run));
+        l_part += p0 + p1;
+        pk[u] = pack_bf16x2(p0, p1);
       }
-    }
-    // ---- O^T += V^T P^T ---------------------------------------------------
+      return as_bf16x8(pk);
+    };
+    // ---- O^T += V^T P^T: V fragments one 16-key step ahead, each step's
+    // MFMAs overlapping the exponentials of the next ----------------------
+    bf16x8 p = probs(0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v4(1, vb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(va[db], p, o[db]);
+    p = probs(1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v4(2, va);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint16_t* vrow = &sV[buf][(db * 32 + (lane & 31)) * FA_VS + 16 * j + 4 * hl];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        o[db] = mfma_bf16(a, pb[j], o[db]);
-      }
-    }
+    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(vb[db], p, o[db]);
+    p = probs(2);
+    __builtin_amdgcn_sched_barrier(0);
+    read_v4(3, vb);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(va[db], p, o[db]);
+    p = probs(3);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(vb[db], p, o[db]);
     if (tile + 1 < ntiles) {
       stash(buf ^ 1);
       __syncthreads();

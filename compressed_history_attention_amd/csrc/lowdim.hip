@@ -560,7 +560,10 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   __shared__ __attribute__((aligned(1024))) char sM[SM ? Geo::M_BYTES : 16];
   __shared__ __attribute__((aligned(16))) float sT[RBW * TS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+  // wave index and tile count in scalar registers: tile addresses and the
+  // LDS destinations of the tile loads are then computed on the scalar unit
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = a.hs.h[blockIdx.y];
   const int W = a.H * 128;
   const int64_t q0 = (int64_t)blockIdx.x * RBW;
@@ -583,7 +586,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   accW[1] = zero16();
   float lsum = 0.f;
 
-  const int ntiles = a.tile_start[a.NB];
+  const int ntiles = __builtin_amdgcn_readfirstlane(a.tile_start[a.NB]);
   const char* sTrow = reinterpret_cast<const char*>(sT + rloc * TS);
   const uint16_t* qsrc = a.q + (rok ? qrow : q0) * W + h * 128 + 8 * hl;
 
@@ -596,10 +599,12 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   // the k-th of this wave's 1 KiB chunks of tile tt into `dst`
   auto dma = [&](int tt, char* dst, int k) __attribute__((always_inline)) {
     const int c = wave + 8 * k;
-    if (c < Geo::CHUNKS && tt < ntiles)
-      __builtin_amdgcn_global_load_lds(a.img + (int64_t)tt * G.bytes + c * 1024 + lane * 16,
+    if (c < Geo::CHUNKS && tt < ntiles) {
+      const char* chunk = a.img + ((int64_t)tt * G.bytes + c * 1024);  // wave-uniform
+      __builtin_amdgcn_global_load_lds(chunk + (uint32_t)(lane * 16),
                                        (__attribute__((address_space(3))) void*)(dst + c * 1024),
                                        16, 0, 0);
+    }
   };
 
   // masses of a finished a^V range straight from the accumulators
