@@ -52,6 +52,31 @@ class nkv_segment(ctypes.Structure):
     _fields_ = [("begin", ctypes.c_int64), ("end", ctypes.c_int64), ("mode", ctypes.c_int32)]
 
 
+class nkv_route_policy(ctypes.Structure):
+    _fields_ = [("frame_tokens", ctypes.c_int64), ("recent_frames", ctypes.c_int32),
+                ("sink_frames", ctypes.c_int32), ("anchor_every", ctypes.c_int32),
+                ("all_full_frames", ctypes.c_int32), ("layer_full", ctypes.c_int32)]
+
+
+class nkv_storage(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("idx", "codes", "scales", "cached", "centers",
+                                               "encoders", "decoders", "resident", "total",
+                                               "original")] + \
+               [(n, ctypes.c_double) for n in ("cr_effective", "cr_cached", "cr_nominal")]
+
+
+class nkv_cache_branch(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("centers", ctypes.c_void_p),
+                ("encoder", ctypes.c_void_p), ("decoder", ctypes.c_void_p),
+                ("A", ctypes.c_int32)]
+
+
+class nkv_layer_cache(ctypes.Structure):
+    _fields_ = [("k", nkv_cache_branch), ("v", nkv_cache_branch),
+                ("n_hist", ctypes.c_int64), ("capacity", ctypes.c_int64)]
+
+
 class nkv_prof_entry(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("ms", ctypes.c_double), ("count", ctypes.c_int32)]
 
@@ -70,6 +95,7 @@ def load() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     SH, BR, SG = ctypes.POINTER(nkv_shape), ctypes.POINTER(nkv_branch), ctypes.POINTER(nkv_segment)
+    LC, RP = ctypes.POINTER(nkv_layer_cache), ctypes.POINTER(nkv_route_policy)
     sig = {
         "nkv_version": (ctypes.c_int, []),
         "nkv_last_error": (ctypes.c_char_p, []),
@@ -86,6 +112,14 @@ def load() -> ctypes.CDLL:
         "nkv_attend_fast_heads": (ctypes.c_int, [SH, BR, BR, I64, SG, I32, ctypes.POINTER(I32), P,
                                                  I64, P, P, I64, P, P, P, SZ, P]),
         "nkv_lse_merge": (ctypes.c_int, [I64, I32, I32, P, P, P, P, P, I32, P, P]),
+        "nkv_route_segments": (ctypes.c_int, [ctypes.POINTER(nkv_route_policy), I64, SG, I32,
+                                              ctypes.POINTER(I32)]),
+        "nkv_storage_account": (ctypes.c_int, [SH, I32, I32, I64, ctypes.POINTER(nkv_storage)]),
+        "nkv_layer_attend_workspace_size": (SZ, [SH, LC, RP, ctypes.POINTER(I32), I64, I64]),
+        "nkv_layer_attend": (ctypes.c_int, [SH, LC, RP, ctypes.POINTER(I32), P, I64, P, P, I64,
+                                            P, P, P, SZ, P]),
+        "nkv_layer_append_workspace_size": (SZ, [SH, LC, I64]),
+        "nkv_layer_append": (ctypes.c_int, [SH, LC, P, P, I64, P, SZ, P]),
         "nkv_profile_enable": (None, [ctypes.c_int]),
         "nkv_profile_read": (ctypes.c_int, [ctypes.POINTER(nkv_prof_entry), I32]),
     }
@@ -100,7 +134,9 @@ def load() -> ctypes.CDLL:
 EXPORTS = ("nkv_version", "nkv_last_error", "nkv_status_string", "nkv_force_generic",
            "nkv_encode_workspace_size", "nkv_encode", "nkv_attend_workspace_size",
            "nkv_attend_full", "nkv_attend_fast", "nkv_attend_heads_workspace_size",
-           "nkv_attend_fast_heads", "nkv_lse_merge", "nkv_profile_enable", "nkv_profile_read")
+           "nkv_attend_fast_heads", "nkv_lse_merge", "nkv_route_segments", "nkv_storage_account",
+           "nkv_layer_attend_workspace_size", "nkv_layer_attend", "nkv_layer_append_workspace_size",
+           "nkv_layer_append", "nkv_profile_enable", "nkv_profile_read")
 
 
 def _check(status: int):
@@ -276,6 +312,118 @@ def nkv_lse_merge(H: int, d: int, o_a, lse_a, o_b, lse_b, out, lse_out, stream=N
     dt = NKV_F32 if out.dtype == torch.float32 else NKV_BF16
     _check(load().nkv_lse_merge(int(o_a.shape[0]), H, d, _ptr(o_a), _ptr(lse_a), _ptr(o_b),
                                 _ptr(lse_b), _ptr(out), dt, _ptr(lse_out), _stream(stream)))
+
+
+@dataclass(frozen=True)
+class RoutePolicy:
+    """Per-layer full-dimensional routing policy (mirrors nkv_route_policy)."""
+    frame_tokens: int
+    recent_frames: int = 0
+    sink_frames: int = 0
+    anchor_every: int = 0
+    all_full_frames: int = 0
+    layer_full: bool = False
+
+    def c(self) -> nkv_route_policy:
+        return nkv_route_policy(int(self.frame_tokens), int(self.recent_frames),
+                                int(self.sink_frames), int(self.anchor_every),
+                                int(self.all_full_frames), 1 if self.layer_full else 0)
+
+
+def nkv_route_segments(policy: RoutePolicy, n_hist: int):
+    """[(begin, end, mode)] of the policy over n_hist history tokens."""
+    L, pol, n = load(), policy.c(), ctypes.c_int32(0)
+    st = L.nkv_route_segments(ctypes.byref(pol), n_hist, None, 0, ctypes.byref(n))
+    if st != 0 and n.value == 0 and n_hist > 0:
+        _check(st)
+    buf = (nkv_segment * max(1, n.value))()
+    _check(L.nkv_route_segments(ctypes.byref(pol), n_hist, buf, n.value, ctypes.byref(n)))
+    return [(buf[i].begin, buf[i].end, buf[i].mode) for i in range(n.value)]
+
+
+def nkv_storage_account(shape: Shape, A_k: int, A_v: int, n_hist: int) -> dict:
+    out = nkv_storage()
+    _check(load().nkv_storage_account(ctypes.byref(shape.c()), A_k, A_v, n_hist,
+                                      ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in nkv_storage._fields_}
+
+
+class LayerCache:
+    """One layer's compressed history on the GPU (both branches) with room
+    for ``capacity`` tokens, plus the layer's codecs.  ``n_hist`` lives in
+    the C descriptor that nkv_layer_append advances."""
+
+    def __init__(self, shape: Shape, capacity: int, centers, encoders, decoders, device):
+        self.shape = shape
+        dev = torch.device(device)
+        self.codec = (tuple(centers), tuple(encoders), tuple(decoders))
+        self.idx = [torch.empty(capacity, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.codes = [torch.empty((capacity, shape.r // 2), dtype=torch.uint8, device=dev)
+                      for _ in range(2)]
+        self.scales = [torch.empty((capacity, shape.r // shape.group), dtype=torch.int16,
+                                   device=dev) for _ in range(2)]
+        br = [nkv_cache_branch(_ptr(self.idx[b]), _ptr(self.codes[b]), _ptr(self.scales[b]),
+                               _ptr(centers[b]), _ptr(encoders[b]), _ptr(decoders[b]),
+                               int(centers[b].shape[0])) for b in range(2)]
+        self.desc = nkv_layer_cache(br[0], br[1], 0, int(capacity))
+
+    @property
+    def n_hist(self) -> int:
+        return int(self.desc.n_hist)
+
+    @property
+    def capacity(self) -> int:
+        return int(self.desc.capacity)
+
+    def branch(self, b: int) -> Branch:
+        """The stored history of branch b (0 = K, 1 = V) as a Branch view."""
+        n = self.n_hist
+        return Branch(self.idx[b][:n], self.codes[b][:n], self.scales[b][:n],
+                      self.codec[0][b], self.codec[2][b])
+
+    def history_bytes(self) -> int:
+        """Bytes of the stored records (both branches) at the current length."""
+        n = self.n_hist
+        return sum(t[:n].numel() * t.element_size()
+                   for t in (*self.idx, *self.codes, *self.scales))
+
+
+def nkv_layer_attend_workspace_size(shape: Shape, cache: LayerCache, policy: RoutePolicy,
+                                    r_low_h, Nq: int, N_cur: int) -> int:
+    w = None if r_low_h is None else _widths(shape, r_low_h)
+    res = load().nkv_layer_attend_workspace_size(ctypes.byref(shape.c()),
+                                                 ctypes.byref(cache.desc),
+                                                 ctypes.byref(policy.c()), w, Nq, N_cur)
+    if res == SIZE_MAX:
+        raise NkvError(1, load().nkv_last_error().decode() or "invalid layer attend arguments")
+    return res
+
+
+def nkv_layer_attend(shape: Shape, cache: LayerCache, policy: RoutePolicy, r_low_h, q, cur_k,
+                     cur_v, out, lse, ws=None, stream=None):
+    N_cur = 0 if cur_k is None else int(cur_k.shape[0])
+    w = None if r_low_h is None else _widths(shape, r_low_h)
+    _check(load().nkv_layer_attend(ctypes.byref(shape.c()), ctypes.byref(cache.desc),
+                                   ctypes.byref(policy.c()), w, _ptr(q), int(q.shape[0]),
+                                   _ptr(cur_k), _ptr(cur_v), N_cur, _ptr(out), _ptr(lse),
+                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def nkv_layer_append_workspace_size(shape: Shape, cache: LayerCache, N: int) -> int:
+    res = load().nkv_layer_append_workspace_size(ctypes.byref(shape.c()),
+                                                 ctypes.byref(cache.desc), N)
+    if res == SIZE_MAX:
+        raise NkvError(1, load().nkv_last_error().decode() or "invalid append arguments")
+    return res
+
+
+def nkv_layer_append(shape: Shape, cache: LayerCache, k_new, v_new, ws=None, stream=None):
+    N = int(k_new.shape[0])
+    if int(v_new.shape[0]) != N:
+        raise ValueError("k_new and v_new need the same number of rows")
+    _check(load().nkv_layer_append(ctypes.byref(shape.c()), ctypes.byref(cache.desc),
+                                   _ptr(k_new), _ptr(v_new), N, _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

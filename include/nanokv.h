@@ -199,6 +199,125 @@ nkv_status nkv_lse_merge(int64_t Nq, int32_t H, int32_t d, const float* o_a,
                          const float* lse_b, void* out, int32_t out_dtype,
                          float* lse_out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Rollout support: per-layer routing policy, per-layer compressed cache and
+ * storage accounting.  Every chunk of an autoregressive rollout attends, at
+ * every layer, to that layer's history plus its own keys/values; once the
+ * chunk is final its K and V are encoded and appended to the history
+ * (Figure 4(a)/(b)).
+ * ------------------------------------------------------------------------ */
+
+/* Full-dimensional routing policy of one layer (Table 7 of the NanoKV page:
+ * recent latent frames, one anchor per F older frames, sink frames, all of a
+ * short history, full-layer fallback).  History positions form latent frames
+ * of frame_tokens consecutive tokens, oldest first; a ragged last frame is a
+ * frame.  With n_frames frames in the history, frame f is read NKV_FULL when
+ *   layer_full != 0, or n_frames <= all_full_frames, or f < sink_frames,
+ *   or f >= n_frames - recent_frames,
+ *   or anchor_every > 0 and f % anchor_every == 0,
+ * and NKV_LOW otherwise.  Counts are non-negative; frame_tokens > 0. */
+typedef struct {
+  int64_t frame_tokens;
+  int32_t recent_frames;
+  int32_t sink_frames;
+  int32_t anchor_every;     /* 0: no anchors */
+  int32_t all_full_frames;  /* 0: none */
+  int32_t layer_full;       /* non-zero: the whole layer is read full */
+} nkv_route_policy;
+
+/* Segments of `policy` for a history of n_hist tokens, oldest first,
+ * adjacent frames of one mode joined into one segment (n_hist == 0 gives no
+ * segment).  Host-only: writes *n_out and, if *n_out <= max_out, the
+ * segments to out (host memory).  NKV_EINVAL for a malformed policy, or when
+ * more than max_out segments are needed (*n_out then holds the number
+ * needed). */
+nkv_status nkv_route_segments(const nkv_route_policy* policy, int64_t n_hist,
+                              nkv_segment* out, int32_t max_out,
+                              int32_t* n_out);
+
+/* Persistent bytes of one layer's compressed history (Figure 8 of the NanoKV
+ * page splits storage into cached data and resident operators; Table 1
+ * reports the effective compression ratio against the uncompressed cache).
+ *   cached    = idx (4 B) + codes (r/2 B) + scales (2 r/group B) per token,
+ *               for both branches;
+ *   resident  = centers [A_k + A_v, W] + encoders 2 x [r, W]
+ *               + decoders 2 x [W, r] at the element size of shape->dtype;
+ *   original  = K and V of the same tokens in bf16 (2 B per value). */
+typedef struct {
+  int64_t idx, codes, scales, cached;
+  int64_t centers, encoders, decoders, resident;
+  int64_t total;          /* cached + resident */
+  int64_t original;
+  double cr_effective;    /* original / total (0 when total == 0) */
+  double cr_cached;       /* original / cached (0 when cached == 0) */
+  double cr_nominal;      /* (W x 16 bit) / (r x 4 bit) */
+} nkv_storage;
+
+/* Host-only; NKV_EINVAL for a NULL or invalid argument. */
+nkv_status nkv_storage_account(const nkv_shape* shape, int32_t A_k,
+                               int32_t A_v, int64_t n_hist, nkv_storage* out);
+
+/* One branch of a layer cache: history arrays with room for `capacity`
+ * tokens (layout as for nkv_encode) and the branch's codec. */
+typedef struct {
+  int32_t* idx;            /* [capacity]                                  */
+  uint8_t* codes;          /* [capacity, r/2]                             */
+  uint16_t* scales;        /* [capacity, r/group]                         */
+  const void* centers;     /* [A, W]                                      */
+  const void* encoder;     /* [r, W]                                      */
+  const void* decoder;     /* [W, r]                                      */
+  int32_t A;
+} nkv_cache_branch;
+
+/* The compressed history of one layer.  Device arrays are the caller's;
+ * n_hist is maintained by nkv_layer_append (host field, advanced when the
+ * encode work is enqueued, so stream order keeps later reads consistent). */
+typedef struct {
+  nkv_cache_branch k, v;
+  int64_t n_hist;
+  int64_t capacity;
+} nkv_layer_cache;
+
+/* Workspace bytes for nkv_layer_attend with the same arguments; SIZE_MAX if
+ * they are invalid. */
+size_t nkv_layer_attend_workspace_size(const nkv_shape* shape,
+                                       const nkv_layer_cache* cache,
+                                       const nkv_route_policy* policy,
+                                       const int32_t* r_low_h, int64_t Nq,
+                                       int64_t N_cur);
+
+/*
+ * Attention of one layer for one chunk: the chunk's queries q [Nq, W] over
+ * the layer's history routed by `policy` (nkv_route_segments) plus the
+ * chunk's own cur_k/cur_v [N_cur, W].  When every history frame is routed
+ * full this is nkv_attend_full, otherwise nkv_attend_fast_heads with the
+ * per-head widths r_low_h (host array of H ints; may be NULL only when the
+ * policy routes the whole current history full).  Outputs as nkv_attend_full.
+ */
+nkv_status nkv_layer_attend(const nkv_shape* shape,
+                            const nkv_layer_cache* cache,
+                            const nkv_route_policy* policy,
+                            const int32_t* r_low_h, const void* q, int64_t Nq,
+                            const void* cur_k, const void* cur_v,
+                            int64_t N_cur, void* out, float* lse, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Workspace bytes for nkv_layer_append of N tokens; SIZE_MAX if invalid. */
+size_t nkv_layer_append_workspace_size(const nkv_shape* shape,
+                                       const nkv_layer_cache* cache,
+                                       int64_t N);
+
+/*
+ * Encode a finished chunk's K and V rows (k_new, v_new [N, W]) with the
+ * layer's codecs (as nkv_encode) into positions [n_hist, n_hist + N) of the
+ * cache, then advance cache->n_hist by N.  NKV_EINVAL, with nothing
+ * enqueued and n_hist unchanged, if the arrays lack room
+ * (n_hist + N > capacity).
+ */
+nkv_status nkv_layer_append(const nkv_shape* shape, nkv_layer_cache* cache,
+                            const void* k_new, const void* v_new, int64_t N,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* nkv_status_string(nkv_status s);
 /* Detail of the last failure on the calling thread ("" if none). */
