@@ -320,7 +320,7 @@ def head_widths(r_low, H: int) -> list:
 
 
 def low_attention(q: np.ndarray, kb: Branch, vb: Branch, r_low, H: int,
-                  d: int, tau: float, qblock: int = 256):
+                  d: int, tau: float, qblock: int = 256, maps=None):
     """Low-dimensional read of a history partition (Figure 4(d)).
 
     Per head h, with D_{X,h} the rows h*d..h*d+d-1 of decoder X and [:r_low]
@@ -332,6 +332,11 @@ def low_attention(q: np.ndarray, kb: Branch, vb: Branch, r_low, H: int,
                + sum_t p_t mu^V_{a^V_t, h}                 (output restoration)
       LSE_h  = logsumexp_t(s)
     With r_low = r this equals decoding followed by exact attention.
+
+    ``maps`` = (Q, O), float64 [W, ld] each, replaces D_K in the query
+    reduction and D_V in the restoration by other maps (Table 8 compares the
+    analytical decoder maps with adapted ones); the scores still use the
+    stored K coefficients and centers.
     """
     nq = q.shape[0]
     nl = kb.idx.shape[0]
@@ -349,8 +354,8 @@ def low_attention(q: np.ndarray, kb: Branch, vb: Branch, r_low, H: int,
         ck = ck_all[:, :rl]
         cv = cv_all[:, :rl]
         sl = slice(h * d, (h + 1) * d)
-        dk = kb.decoder[sl, :rl]
-        dv = vb.decoder[sl, :rl]
+        dk = (kb.decoder if maps is None else maps[0])[sl, :rl]
+        dv = (vb.decoder if maps is None else maps[1])[sl, :rl]
         muk = kb.centers[:, sl]
         muv = vb.centers[:, sl]
         for s0 in range(0, nq, qblock):
@@ -387,15 +392,16 @@ def route_indices(segments: Sequence[Tuple[int, int, int]], n_hist: int):
 
 def attend_fast(q: np.ndarray, kb: Branch, vb: Branch, segments, r_low,
                 cur_k: np.ndarray, cur_v: np.ndarray, H: int, d: int,
-                tau: float):
+                tau: float, maps=None):
     """NanoKV-Fast (Figure 4(d)): full-routed history plus the current chunk
     through decode + exact attention, low-routed history through
     ``low_attention`` (one width for all heads, or one per head as in the
-    deployed configurations of Table 6), then LSE merging of the two parts."""
+    deployed configurations of Table 6; optional query-reduction and
+    restoration maps, Table 8), then LSE merging of the two parts."""
     n_hist = kb.idx.shape[0]
     full, low = route_indices(segments, n_hist)
     kf = np.concatenate([kb.rows(full).decode(), cur_k], axis=0)
     vf = np.concatenate([vb.rows(full).decode(), cur_v], axis=0)
     part_full = exact_attention(q, kf, vf, H, d, tau)
-    part_low = low_attention(q, kb.rows(low), vb.rows(low), r_low, H, d, tau)
+    part_low = low_attention(q, kb.rows(low), vb.rows(low), r_low, H, d, tau, maps=maps)
     return lse_merge([part_full, part_low], H, d)

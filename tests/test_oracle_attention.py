@@ -213,7 +213,9 @@ def test_low_read_with_zero_rank_is_attention_over_centers():
     np.testing.assert_allclose(l, ls, atol=1e-12)
 
 
-def _brute_low(q, kb, vb, r_low, H, d, tau):
+def _brute_low(q, kb, vb, r_low, H, d, tau, qmap=None, omap=None):
+    qmap = kb.decoder if qmap is None else qmap
+    omap = vb.decoder if omap is None else omap
     ck, cv = kb.coefficients(), vb.coefficients()
     nq, N = q.shape[0], ck.shape[0]
     o = np.zeros((nq, H * d))
@@ -221,7 +223,7 @@ def _brute_low(q, kb, vb, r_low, H, d, tau):
     for i in range(nq):
         for h in range(H):
             rows = range(h * d, (h + 1) * d)
-            qt = [sum(kb.decoder[w, j] * q[i, w] for w in rows) for j in range(r_low)]
+            qt = [sum(qmap[w, j] * q[i, w] for w in rows) for j in range(r_low)]
             s = []
             for t in range(N):
                 a = kb.idx[t]
@@ -233,7 +235,7 @@ def _brute_low(q, kb, vb, r_low, H, d, tau):
             for jj, w in enumerate(rows):
                 val = 0.0
                 for t in range(N):
-                    coef = sum(vb.decoder[w, j] * cv[t, j] for j in range(r_low))
+                    coef = sum(omap[w, j] * cv[t, j] for j in range(r_low))
                     val += p[t] * (coef + vb.centers[vb.idx[t], w])
                 o[i, w] = val / tot
             lse[i, h] = m + math.log(tot)
@@ -275,6 +277,39 @@ def test_fast_per_head_full_width_head_equals_full_read():
     np.testing.assert_allclose(o[:, :d], of[:, :d], atol=1e-12)
     np.testing.assert_allclose(l[:, 0], lf[:, 0], atol=1e-12)
     assert np.max(np.abs(o[:, d:] - of[:, d:])) > 1e-3
+
+
+def test_low_read_arbitrary_maps_brute_force():
+    """Caller-given query-reduction / restoration maps (Table 8: adapted maps
+    replace the analytical ones) with more columns than any width."""
+    q, kb, vb, _, _, H, d = _fast_case(15, N=9, nq=2)
+    rng = np.random.default_rng(3)
+    W = H * d
+    qmap = rng.standard_normal((W, kb.r + 3))
+    omap = rng.standard_normal((W, kb.r + 3))
+    widths = [3, kb.r]
+    o, l = oracle.low_attention(q, kb, vb, widths, H, d, 0.35, maps=(qmap, omap))
+    for h, rl in enumerate(widths):
+        ob, lb = _brute_low(q, kb, vb, rl, H, d, 0.35, qmap, omap)
+        sl = slice(h * d, (h + 1) * d)
+        np.testing.assert_allclose(o[:, sl], ob[:, sl], atol=1e-12)
+        np.testing.assert_allclose(l[:, h], lb[:, h], atol=1e-12)
+    # the analytical maps are the decoders
+    o1, l1 = oracle.low_attention(q, kb, vb, widths, H, d, 0.35, maps=(kb.decoder, vb.decoder))
+    o2, l2 = oracle.low_attention(q, kb, vb, widths, H, d, 0.35)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_zero_maps_reduce_to_attention_over_centers():
+    """Zero maps remove the coefficient terms from scores and outputs: the
+    read is then exact attention over the tokens' centers (library sdpa)."""
+    q, kb, vb, _, _, H, d = _fast_case(16)
+    z = np.zeros((H * d, kb.r))
+    o, l = oracle.low_attention(q, kb, vb, kb.r, H, d, 0.35, maps=(z, z))
+    os_, ls = _sdpa(q, kb.centers[kb.idx], vb.centers[vb.idx], H, d, 0.35)
+    np.testing.assert_allclose(o, os_, atol=1e-12)
+    np.testing.assert_allclose(l, ls, atol=1e-12)
 
 
 def test_low_read_permutation_invariant():
