@@ -187,13 +187,15 @@ static bool tuned_applies_all(const nkv_shape* s, int32_t r_low, const int32_t* 
 
 static size_t workspace_common(const nkv_shape* shape, int32_t A_k, int32_t A_v, int64_t N_hist,
                                const nkv_segment* route, int32_t n_seg, int32_t r_low,
-                               const int32_t* r_low_h, int64_t Nq, int64_t N_cur);
+                               const int32_t* r_low_h, int64_t Nq, int64_t N_cur,
+                               bool tuned_maps = true);
 
 static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, const nkv_branch* v,
                                 int64_t N_hist, const nkv_segment* route, int32_t n_seg,
-                                int32_t r_low, const int32_t* r_low_h, const void* q, int64_t Nq,
-                                const void* cur_k, const void* cur_v, int64_t N_cur, void* out,
-                                float* lse, void* ws, size_t ws_bytes, void* stream_, bool fast) {
+                                int32_t r_low, const int32_t* r_low_h, const nkv_low_maps* maps,
+                                const void* q, int64_t Nq, const void* cur_k, const void* cur_v,
+                                int64_t N_cur, void* out, float* lse, void* ws, size_t ws_bytes,
+                                void* stream_, bool fast) {
   nkv_status st = check_shape(shape);
   if (st) return st;
   if ((st = check_branch(k, "K", N_hist)) || (st = check_branch(v, "V", N_hist))) return st;
@@ -213,10 +215,22 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
     r_low = 0;
     r_low_h = nullptr;
   }
-  if (low.total > 0 && r_low > 512 && !tuned_applies_all(shape, r_low, r_low_h))
+  // query-reduction / restoration maps: the decoders unless the caller gives others
+  LowMaps mp{k->decoder, v->decoder, shape->r};
+  if (maps) {
+    if (!maps->q_map || !maps->o_map) NKV_FAIL(NKV_EINVAL, "maps: NULL q_map/o_map");
+    if (maps->ld < r_low)
+      NKV_FAIL(NKV_EINVAL, "maps: ld=%d below the widest r_low=%d", maps->ld, r_low);
+    mp = LowMaps{maps->q_map, maps->o_map, maps->ld};
+  }
+  const bool tuned_maps = mp.ld % 8 == 0 && (reinterpret_cast<uintptr_t>(mp.qmap) & 15) == 0 &&
+                          (reinterpret_cast<uintptr_t>(mp.omap) & 15) == 0;
+  const bool tuned = tuned_applies_all(shape, r_low, low.total > 0 ? r_low_h : nullptr) &&
+                     (low.total == 0 || tuned_maps);
+  if (low.total > 0 && r_low > 512 && !tuned)
     NKV_FAIL(NKV_EUNSUPPORTED, "generic low-dimensional read supports r_low <= 512");
   const size_t need = workspace_common(shape, k->A, v->A, N_hist, fast ? route : nullptr,
-                                       fast ? n_seg : 0, r_low, r_low_h, Nq, N_cur);
+                                       fast ? n_seg : 0, r_low, r_low_h, Nq, N_cur, tuned_maps);
   if (need == SIZE_MAX) return NKV_EINVAL;
   if (Nq == 0) return NKV_OK;
   if (need > 0 && (!ws || ws_bytes < need))
@@ -226,8 +240,8 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
   const int dt = shape->dtype, H = shape->H, d = shape->d, r = shape->r, g = shape->group;
   const BranchArgs kb = to_args(k), vb = to_args(v);
 
-  if (tuned_applies_all(shape, r_low, low.total > 0 ? r_low_h : nullptr)) {
-    return tuned_attend(shape, kb, vb, full, low, r_low, low.total > 0 ? r_low_h : nullptr, tau, q,
+  if (tuned) {
+    return tuned_attend(shape, kb, vb, mp, full, low, r_low, low.total > 0 ? r_low_h : nullptr, tau, q,
                         Nq, cur_k, cur_v, N_cur, out, lse, static_cast<char*>(ws), ws_bytes, s);
   }
 
@@ -250,7 +264,7 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
   float* ll = reinterpret_cast<float*>(base + L.lse_low);
   if ((st = launch_attention_generic(dt, true, q, Nq, H, d, tau, kw, vw, nk, of, lf, s))) return st;
   if (!r_low_h) {
-    if ((st = launch_low_generic(dt, q, Nq, H, d, r, g, r_low, tau, kb, vb, low, nullptr, nullptr,
+    if ((st = launch_low_generic(dt, q, Nq, H, d, r, g, r_low, tau, kb, vb, mp, low, nullptr, nullptr,
                                  Nq * H, ol, ll, s)))
       return st;
   } else {
@@ -267,7 +281,7 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
           done[h] = 1;
         }
       if ((st = launch_head_rows(Nq, H, hs, rows, nrows, s))) return st;
-      if ((st = launch_low_generic(dt, q, Nq, H, d, r, g, r_low_h[h0], tau, kb, vb, low, rows,
+      if ((st = launch_low_generic(dt, q, Nq, H, d, r, g, r_low_h[h0], tau, kb, vb, mp, low, rows,
                                    nrows, Nq * hs.n, ol, ll, s)))
         return st;
     }
@@ -277,7 +291,8 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
 
 static size_t workspace_common(const nkv_shape* shape, int32_t A_k, int32_t A_v, int64_t N_hist,
                                const nkv_segment* route, int32_t n_seg, int32_t r_low,
-                               const int32_t* r_low_h, int64_t Nq, int64_t N_cur) {
+                               const int32_t* r_low_h, int64_t Nq, int64_t N_cur,
+                               bool tuned_maps) {
   if (check_shape(shape) || A_k < 1 || A_v < 1 || N_hist < 0 || Nq < 0 || N_cur < 0)
     return SIZE_MAX;
   RangeTable full, low;
@@ -286,7 +301,7 @@ static size_t workspace_common(const nkv_shape* shape, int32_t A_k, int32_t A_v,
     r_low = 0;
     r_low_h = nullptr;
   }
-  if (tuned_applies_all(shape, r_low, r_low_h))
+  if (tuned_applies_all(shape, r_low, r_low_h) && (low.total == 0 || tuned_maps))
     return tuned_attend_workspace(shape, A_k, A_v, full, low, r_low, Nq, N_cur);
   return generic_layout(shape, full.total, low.total, Nq, N_cur, r_low_h != nullptr).total;
 }
@@ -369,8 +384,34 @@ nkv_status nkv_attend_fast_heads(const nkv_shape* shape, const nkv_branch* k,
   g_err[0] = 0;
   if (!shape) NKV_FAIL(NKV_EINVAL, "shape is NULL");
   if (!r_low_h) NKV_FAIL(NKV_EINVAL, "r_low_h is NULL");
-  return attend_common(shape, k, v, N_hist, route, n_seg, 0, r_low_h, q, Nq, cur_k, cur_v, N_cur,
-                       out, lse, ws, ws_bytes, stream, true);
+  return attend_common(shape, k, v, N_hist, route, n_seg, 0, r_low_h, nullptr, q, Nq, cur_k, cur_v,
+                       N_cur, out, lse, ws, ws_bytes, stream, true);
+}
+
+nkv_status nkv_attend_fast_maps(const nkv_shape* shape, const nkv_branch* k,
+                                const nkv_branch* v, int64_t N_hist, const nkv_segment* route,
+                                int32_t n_seg, const int32_t* r_low_h, const nkv_low_maps* maps,
+                                const void* q, int64_t Nq, const void* cur_k, const void* cur_v,
+                                int64_t N_cur, void* out, float* lse, void* ws, size_t ws_bytes,
+                                void* stream) {
+  g_err[0] = 0;
+  if (!shape) NKV_FAIL(NKV_EINVAL, "shape is NULL");
+  if (!r_low_h) NKV_FAIL(NKV_EINVAL, "r_low_h is NULL");
+  if (!maps) NKV_FAIL(NKV_EINVAL, "maps is NULL");
+  return attend_common(shape, k, v, N_hist, route, n_seg, 0, r_low_h, maps, q, Nq, cur_k, cur_v,
+                       N_cur, out, lse, ws, ws_bytes, stream, true);
+}
+
+size_t nkv_attend_maps_workspace_size(const nkv_shape* shape, int32_t A_k, int32_t A_v,
+                                      int64_t N_hist, const nkv_segment* route, int32_t n_seg,
+                                      const int32_t* r_low_h, const nkv_low_maps* maps,
+                                      int64_t Nq, int64_t N_cur) {
+  if (check_shape(shape) || !maps) return SIZE_MAX;
+  const int32_t mx = check_widths(shape, r_low_h);
+  if (!mx || maps->ld < mx) return SIZE_MAX;
+  const bool tm = maps->ld % 8 == 0 && (reinterpret_cast<uintptr_t>(maps->q_map) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(maps->o_map) & 15) == 0;
+  return workspace_common(shape, A_k, A_v, N_hist, route, n_seg, mx, r_low_h, Nq, N_cur, tm);
 }
 
 nkv_status nkv_attend_full(const nkv_shape* shape, const nkv_branch* k, const nkv_branch* v,
@@ -378,8 +419,8 @@ nkv_status nkv_attend_full(const nkv_shape* shape, const nkv_branch* k, const nk
                            const void* cur_v, int64_t N_cur, void* out, float* lse, void* ws,
                            size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  return attend_common(shape, k, v, N_hist, nullptr, 0, 0, nullptr, q, Nq, cur_k, cur_v, N_cur, out,
-                       lse, ws, ws_bytes, stream, false);
+  return attend_common(shape, k, v, N_hist, nullptr, 0, 0, nullptr, nullptr, q, Nq, cur_k, cur_v,
+                       N_cur, out, lse, ws, ws_bytes, stream, false);
 }
 
 nkv_status nkv_attend_fast(const nkv_shape* shape, const nkv_branch* k, const nkv_branch* v,
@@ -388,8 +429,8 @@ nkv_status nkv_attend_fast(const nkv_shape* shape, const nkv_branch* k, const nk
                            int64_t N_cur, void* out, float* lse, void* ws, size_t ws_bytes,
                            void* stream) {
   g_err[0] = 0;
-  return attend_common(shape, k, v, N_hist, route, n_seg, r_low, nullptr, q, Nq, cur_k, cur_v,
-                       N_cur, out, lse, ws, ws_bytes, stream, true);
+  return attend_common(shape, k, v, N_hist, route, n_seg, r_low, nullptr, nullptr, q, Nq, cur_k,
+                       cur_v, N_cur, out, lse, ws, ws_bytes, stream, true);
 }
 
 nkv_status nkv_lse_merge(int64_t Nq, int32_t H, int32_t d, const float* o_a, const float* lse_a,

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void k_attention_generic(
 template <int DT>
 __global__ __launch_bounds__(64) void k_low_generic(
     const void* __restrict__ q, int64_t Nq, int H, int d, int r, int group, int r_low,
-    float tau, BranchArgs kb, BranchArgs vb, RangeTable low,
+    float tau, BranchArgs kb, BranchArgs vb, LowMaps mp, RangeTable low,
     const int32_t* __restrict__ rows, const int32_t* __restrict__ nrows,
     float* __restrict__ o_low, float* __restrict__ lse_low) {
   extern __shared__ float smem[];
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64) void k_low_generic(
   __builtin_amdgcn_wave_barrier();
   for (int j = lane; j < r_low; j += 64) {
     float acc = 0.f;
-    for (int i = 0; i < d; ++i) acc = fmaf(qh[i], ld<DT>(kb.decoder, (int64_t)(h * d + i) * r + j), acc);
+    for (int i = 0; i < d; ++i) acc = fmaf(qh[i], ld<DT>(mp.qmap, (int64_t)(h * d + i) * mp.ld + j), acc);
     qt[j] = acc;
   }
   for (int a = lane; a < kb.A; a += 64) {
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(64) void k_low_generic(
   const float inv = (l > 0.f) ? 1.f / l : 0.f;
   for (int i = lane; i < d; i += 64) {
     float val = 0.f;
-    for (int c = 0; c < r_low; ++c) val = fmaf(ld<DT>(vb.decoder, (int64_t)(h * d + i) * r + c), qt[c], val);
+    for (int c = 0; c < r_low; ++c) val = fmaf(ld<DT>(mp.omap, (int64_t)(h * d + i) * mp.ld + c), qt[c], val);
     for (int a = 0; a < vb.A; ++a) val = fmaf(Wm[a], ld<DT>(vb.centers, (int64_t)a * W + h * d + i), val);
     o_low[qi * W + h * d + i] = val * inv;
   }
@@ -372,7 +372,7 @@ nkv_status launch_head_rows(int64_t Nq, int H, const HeadSet& hs, int32_t* rows,
 
 nkv_status launch_low_generic(int dt, const void* q, int64_t Nq, int H, int d, int r, int group,
                               int r_low, float tau, const BranchArgs& kb, const BranchArgs& vb,
-                              const RangeTable& low, const int32_t* rows,
+                              const LowMaps& mp, const RangeTable& low, const int32_t* rows,
                               const int32_t* nrows, int64_t max_rows, float* o_low,
                               float* lse_low, hipStream_t s) {
   if (max_rows == 0) return NKV_OK;
@@ -383,7 +383,7 @@ nkv_status launch_low_generic(int dt, const void* q, int64_t Nq, int H, int d, i
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     const unsigned grid = (unsigned)std::min<int64_t>(max_rows, rows ? 4096 : max_rows);
     hipLaunchKernelGGL(k_low_generic<DT>, dim3(grid), dim3(64), lds, s, q, Nq, H,
-                       d, r, group, r_low, tau, kb, vb, low, rows, nrows, o_low, lse_low);
+                       d, r, group, r_low, tau, kb, vb, mp, low, rows, nrows, o_low, lse_low);
     NKV_LAUNCH_CHECK();
   });
   return NKV_OK;

@@ -15,6 +15,16 @@ struct BranchArgs {
   int32_t A;
 };
 
+// Query-reduction and output-restoration maps of the low-dimensional read:
+// head h reduces with rows h*d..h*d+d-1, columns 0..r_low-1 of qmap [W, ld]
+// and restores with the same block of omap [W, ld].  The analytical maps are
+// the decoders themselves (qmap = D_K, omap = D_V, ld = r).
+struct LowMaps {
+  const void* qmap;
+  const void* omap;
+  int32_t ld;
+};
+
 // generic kernels (generic.hip)
 nkv_status launch_encode_generic(int dt, const void* x, int64_t N, int W, const void* centers,
                                  int A, const void* enc, int r, int group, int32_t* idx,
@@ -28,7 +38,7 @@ nkv_status launch_attention_generic(int dt, bool out_f32, const void* q, int64_t
 size_t low_generic_lds_bytes(int A_k, int A_v, int r_low, int d);
 nkv_status launch_low_generic(int dt, const void* q, int64_t Nq, int H, int d, int r, int group,
                               int r_low, float tau, const BranchArgs& kb, const BranchArgs& vb,
-                              const RangeTable& low, const int32_t* rows,
+                              const LowMaps& mp, const RangeTable& low, const int32_t* rows,
                               const int32_t* nrows, int64_t max_rows, float* o_low,
                               float* lse_low, hipStream_t s);
 

@@ -844,10 +844,10 @@ nkv_status launch_main(const MainArgs& m, int64_t Nq, hipStream_t st) {
 struct RestoreProblem {
   static constexpr int BK = 64;
   int M, N, K;  // Nq, 128, 2 ra + 2 av
-  int H, r, r_low, ra, A_v, av;
+  int H, ldv, r_low, ra, A_v, av;
   const float* acc;
   const float* wmass;
-  const uint16_t* dv;    // [W, r]
+  const uint16_t* dv;    // restoration map [W, ldv]
   const uint16_t* mvt;   // [W, av]
   const float* ell;
   const float* bound;
@@ -903,7 +903,7 @@ struct RestoreProblem {
     if (k < 2 * ra) {
       const int j = k >= ra ? k - ra : k;
       if (j >= r_low) return u32x4{0u, 0u, 0u, 0u};
-      return ld_u32x4(dv + ch * r + j);
+      return ld_u32x4(dv + ch * ldv + j);
     }
     const int kk = k - 2 * ra;
     const int c = kk >= av ? kk - av : kk;
@@ -940,7 +940,8 @@ size_t low_workspace_bytes(const nkv_shape* s, int32_t A_k, int32_t A_v, const R
 }
 
 nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
-                      const RangeTable& low, int32_t r_low, float tau, const uint16_t* q,
+                      const LowMaps& mp, const RangeTable& low, int32_t r_low, float tau,
+                      const uint16_t* q,
                       int64_t Nq, float* o_low, float* lse_low, char* ws, int32_t r_low_max,
                       const HeadSet& hs, bool first, hipStream_t st) {
   // offsets from the widest group's plan, so that every group finds the
@@ -978,9 +979,10 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(P.rows, 256)), dim3(256), 0, st, tmax, P.rows);
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, st, misc, (int64_t)4);
   NKV_LAUNCH_CHECK();
-  // transposed decoder rows for the query reduction (this width), transposed V centers
+  // transposed query-reduction map (this width), transposed V centers
   hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(W, 64), (unsigned)ceil_div(r_low, 64)),
-                     dim3(256), 0, st, static_cast<const uint16_t*>(kb.decoder), W, r_low, r, dkt, W);
+                     dim3(256), 0, st, static_cast<const uint16_t*>(mp.qmap), W, r_low, mp.ld, dkt,
+                     W);
   if (first)
     hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(P.avp, 64), (unsigned)ceil_div(W, 64)),
                        dim3(256), 0, st, static_cast<const uint16_t*>(vb.centers), vb.A, W, W, mvt,
@@ -1040,13 +1042,13 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   // restoration
   {
   ProfScope ps_restore("low_restore", st);
-  RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, r, r_low, ra, vb.A, P.av, acc, wmass,
-                    static_cast<const uint16_t*>(vb.decoder), mvt, ell, bound, o_low, lse_low, hs};
+  RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, mp.ld, r_low, ra, vb.A, P.av, acc, wmass,
+                    static_cast<const uint16_t*>(mp.omap), mvt, ell, bound, o_low, lse_low, hs};
   if ((e = launch_gemm(rp, hs.n, st))) return e;
   }
   // rows whose bound may be loose: exact generic recomputation
   ProfScope ps_fallback("low_fallback", st);
-  return launch_low_generic(NKV_BF16, q, Nq, H, s->d, r, s->group, r_low, tau, kb, vb, low, flags,
+  return launch_low_generic(NKV_BF16, q, Nq, H, s->d, r, s->group, r_low, tau, kb, vb, mp, low, flags,
                             reinterpret_cast<int32_t*>(misc + 1), P.rows, o_low, lse_low, st);
 }
 

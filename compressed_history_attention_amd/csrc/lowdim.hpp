@@ -12,8 +12,10 @@ size_t low_workspace_bytes(const nkv_shape* s, int32_t A_k, int32_t A_v, const R
 // is laid out for the widest group, r_low_max.  `first` runs
 // the width-independent preparation (bucket sort, transposed V centers);
 // further calls on the same workspace for other head groups reuse it.
+// `mp` holds the query-reduction and restoration maps (bf16, ld % 8 == 0).
 nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
-                      const RangeTable& low, int32_t r_low, float tau, const uint16_t* q,
+                      const LowMaps& mp, const RangeTable& low, int32_t r_low, float tau,
+                      const uint16_t* q,
                       int64_t Nq, float* o_low, float* lse_low, char* ws, int32_t r_low_max,
                       const HeadSet& hs, bool first, hipStream_t st);
 

@@ -49,7 +49,7 @@ size_t tuned_attend_workspace(const nkv_shape* s, int32_t A_k, int32_t A_v, cons
 }
 
 nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
-                        const RangeTable& full, const RangeTable& low, int32_t r_low,
+                        const LowMaps& mp, const RangeTable& full, const RangeTable& low, int32_t r_low,
                         const int32_t* r_low_h, float tau, const void* q, int64_t Nq,
                         const void* cur_k, const void* cur_v, int64_t N_cur, void* out,
                         float* lse, char* ws, size_t ws_bytes, hipStream_t st) {
@@ -100,7 +100,7 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
     groups[g].h[groups[g].n++] = h;
   }
   for (int g = 0; g < ng; ++g)
-    if ((e = launch_low(s, kb, vb, low, widths[g], tau, qb, Nq, ol, ll, ws + L.low, r_low,
+    if ((e = launch_low(s, kb, vb, mp, low, widths[g], tau, qb, Nq, ol, ll, ws + L.low, r_low,
                         groups[g], g == 0, st)))
       return e;
   ProfScope ps("merge", st);

@@ -52,6 +52,10 @@ class nkv_segment(ctypes.Structure):
     _fields_ = [("begin", ctypes.c_int64), ("end", ctypes.c_int64), ("mode", ctypes.c_int32)]
 
 
+class nkv_low_maps(ctypes.Structure):
+    _fields_ = [("q_map", ctypes.c_void_p), ("o_map", ctypes.c_void_p), ("ld", ctypes.c_int32)]
+
+
 class nkv_route_policy(ctypes.Structure):
     _fields_ = [("frame_tokens", ctypes.c_int64), ("recent_frames", ctypes.c_int32),
                 ("sink_frames", ctypes.c_int32), ("anchor_every", ctypes.c_int32),
@@ -96,6 +100,7 @@ def load() -> ctypes.CDLL:
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     SH, BR, SG = ctypes.POINTER(nkv_shape), ctypes.POINTER(nkv_branch), ctypes.POINTER(nkv_segment)
     LC, RP = ctypes.POINTER(nkv_layer_cache), ctypes.POINTER(nkv_route_policy)
+    MP = ctypes.POINTER(nkv_low_maps)
     sig = {
         "nkv_version": (ctypes.c_int, []),
         "nkv_last_error": (ctypes.c_char_p, []),
@@ -111,6 +116,10 @@ def load() -> ctypes.CDLL:
                                                  I64, I64]),
         "nkv_attend_fast_heads": (ctypes.c_int, [SH, BR, BR, I64, SG, I32, ctypes.POINTER(I32), P,
                                                  I64, P, P, I64, P, P, P, SZ, P]),
+        "nkv_attend_maps_workspace_size": (SZ, [SH, I32, I32, I64, SG, I32, ctypes.POINTER(I32),
+                                                MP, I64, I64]),
+        "nkv_attend_fast_maps": (ctypes.c_int, [SH, BR, BR, I64, SG, I32, ctypes.POINTER(I32), MP,
+                                                P, I64, P, P, I64, P, P, P, SZ, P]),
         "nkv_lse_merge": (ctypes.c_int, [I64, I32, I32, P, P, P, P, P, I32, P, P]),
         "nkv_route_segments": (ctypes.c_int, [ctypes.POINTER(nkv_route_policy), I64, SG, I32,
                                               ctypes.POINTER(I32)]),
@@ -134,7 +143,8 @@ def load() -> ctypes.CDLL:
 EXPORTS = ("nkv_version", "nkv_last_error", "nkv_status_string", "nkv_force_generic",
            "nkv_encode_workspace_size", "nkv_encode", "nkv_attend_workspace_size",
            "nkv_attend_full", "nkv_attend_fast", "nkv_attend_heads_workspace_size",
-           "nkv_attend_fast_heads", "nkv_lse_merge", "nkv_route_segments", "nkv_storage_account",
+           "nkv_attend_fast_heads", "nkv_attend_maps_workspace_size", "nkv_attend_fast_maps",
+           "nkv_lse_merge", "nkv_route_segments", "nkv_storage_account",
            "nkv_layer_attend_workspace_size", "nkv_layer_attend", "nkv_layer_append_workspace_size",
            "nkv_layer_append", "nkv_profile_enable", "nkv_profile_read")
 
@@ -286,6 +296,36 @@ def nkv_attend_fast_heads(shape: Shape, k: Branch, v: Branch, N_hist: int, route
                                         _ptr(cur_k), _ptr(cur_v), N_cur, _ptr(out), _ptr(lse),
                                         _ptr(ws), 0 if ws is None else ws.numel(),
                                         _stream(stream)))
+
+
+def _maps(q_map, o_map) -> nkv_low_maps:
+    if q_map.shape != o_map.shape or q_map.dim() != 2:
+        raise ValueError("q_map and o_map must both be [W, ld]")
+    return nkv_low_maps(_ptr(q_map), _ptr(o_map), int(q_map.shape[1]))
+
+
+def nkv_attend_maps_workspace_size(shape: Shape, A_k: int, A_v: int, N_hist: int, route, r_low_h,
+                                   q_map, o_map, Nq: int, N_cur: int) -> int:
+    segs, n = _segments(route)
+    res = load().nkv_attend_maps_workspace_size(ctypes.byref(shape.c()), A_k, A_v, N_hist, segs,
+                                                n, _widths(shape, r_low_h),
+                                                ctypes.byref(_maps(q_map, o_map)), Nq, N_cur)
+    if res == SIZE_MAX:
+        raise NkvError(1, load().nkv_last_error().decode() or "invalid attend arguments")
+    return res
+
+
+def nkv_attend_fast_maps(shape: Shape, k: Branch, v: Branch, N_hist: int, route, r_low_h, q_map,
+                         o_map, q, cur_k, cur_v, out, lse, ws=None, stream=None):
+    N_cur = 0 if cur_k is None else int(cur_k.shape[0])
+    segs, n = _segments(route)
+    _check(load().nkv_attend_fast_maps(ctypes.byref(shape.c()), ctypes.byref(k.c()),
+                                       ctypes.byref(v.c()), N_hist, segs, n,
+                                       _widths(shape, r_low_h),
+                                       ctypes.byref(_maps(q_map, o_map)), _ptr(q),
+                                       int(q.shape[0]), _ptr(cur_k), _ptr(cur_v), N_cur,
+                                       _ptr(out), _ptr(lse), _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def nkv_attend_full(shape: Shape, k: Branch, v: Branch, N_hist: int, q, cur_k, cur_v, out, lse,
@@ -463,13 +503,23 @@ def attend_full(shape: Shape, k: Branch, v: Branch, N_hist: int, q, cur_k=None, 
 
 
 def attend_fast(shape: Shape, k: Branch, v: Branch, N_hist: int, route, r_low, q,
-                cur_k=None, cur_v=None, ws=None, stream=None):
+                cur_k=None, cur_v=None, ws=None, stream=None, maps=None):
     """r_low: one width for every head, or a sequence of one width per head
-    (nkv_attend_fast_heads)."""
+    (nkv_attend_fast_heads).  maps: optional (q_map, o_map), both [W, ld],
+    replacing the decoders in the query reduction and output restoration
+    (nkv_attend_fast_maps)."""
     Nq = int(q.shape[0])
     N_cur = 0 if cur_k is None else int(cur_k.shape[0])
     out = torch.empty((Nq, shape.W), dtype=shape.torch_dtype, device=q.device)
     lse = torch.empty((Nq, shape.H), dtype=torch.float32, device=q.device)
+    if maps is not None:
+        widths = [int(r_low)] * shape.H if isinstance(r_low, (int, np.integer)) else r_low
+        if ws is None:
+            ws = _workspace(nkv_attend_maps_workspace_size(shape, k.A, v.A, N_hist, route, widths,
+                                                           maps[0], maps[1], Nq, N_cur), q.device)
+        nkv_attend_fast_maps(shape, k, v, N_hist, route, widths, maps[0], maps[1], q, cur_k, cur_v,
+                             out, lse, ws=ws, stream=stream)
+        return out, lse
     if not isinstance(r_low, (int, np.integer)):
         if ws is None:
             ws = _workspace(nkv_attend_heads_workspace_size(shape, k.A, v.A, N_hist, route, r_low,

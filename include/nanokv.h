@@ -187,6 +187,50 @@ nkv_status nkv_attend_fast_heads(const nkv_shape* shape, const nkv_branch* k,
                                  float* lse, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Query-reduction and output-restoration maps of the low-dimensional read
+ * (Figure 4(d) reduces the queries and restores the output dimension;
+ * Table 8 of the NanoKV page compares the analytical maps with adapted
+ * ones).  Both are [W, ld] device arrays of the shape's dtype, row-major;
+ * head h uses rows h*d..h*d+d-1 and the leading r_low_h[h] columns.  The
+ * analytical maps are the decoders: q_map = D_K, o_map = D_V, ld = r. */
+typedef struct {
+  const void* q_map;
+  const void* o_map;
+  int32_t ld;              /* columns of both maps, >= every r_low_h[h] */
+} nkv_low_maps;
+
+/* Workspace bytes for nkv_attend_fast_maps with the same arguments;
+ * SIZE_MAX if they are invalid. */
+size_t nkv_attend_maps_workspace_size(const nkv_shape* shape, int32_t A_k,
+                                      int32_t A_v, int64_t N_hist,
+                                      const nkv_segment* route, int32_t n_seg,
+                                      const int32_t* r_low_h,
+                                      const nkv_low_maps* maps, int64_t Nq,
+                                      int64_t N_cur);
+
+/*
+ * NanoKV-Fast with per-head widths and caller-given low-dimensional maps:
+ * identical to nkv_attend_fast_heads except that, for head h with width
+ * w = r_low_h[h] and M_X,h the block rows h*d..h*d+d-1, columns 0..w-1 of
+ * map X,
+ *   q~_h  = M_{q,h}^T q_h
+ *   O_low = (M_{o,h} sum_t p_t c^V_t[:w] + sum_t p_t centers_V[a^V_t, h])
+ *           / sum_t p_t.
+ * The scores still use the stored K coefficients and centers.  With the
+ * analytical maps the result equals nkv_attend_fast_heads.  The tuned
+ * kernels need ld % 8 == 0 and 16-byte aligned maps; other maps run on the
+ * generic kernels.
+ */
+nkv_status nkv_attend_fast_maps(const nkv_shape* shape, const nkv_branch* k,
+                                const nkv_branch* v, int64_t N_hist,
+                                const nkv_segment* route, int32_t n_seg,
+                                const int32_t* r_low_h,
+                                const nkv_low_maps* maps, const void* q,
+                                int64_t Nq, const void* cur_k,
+                                const void* cur_v, int64_t N_cur, void* out,
+                                float* lse, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /*
  * LSE merge of two partial attentions over disjoint key sets (Figure 4(d)):
  *   L = log(exp(L_a) + exp(L_b)),  O = exp(L_a - L) O_a + exp(L_b - L) O_b.

@@ -129,7 +129,7 @@ def test_encode_deterministic_and_offset_append():
 # attention
 # --------------------------------------------------------------------------
 
-def _run_attend(case, rows_sample=None, route=None, r_low=None, fast=None):
+def _run_attend(case, rows_sample=None, route=None, r_low=None, fast=None, maps=None):
     cfg = case.cfg
     fast = (cfg.mode == "fast") if fast is None else fast
     route = cfg.segments() if route is None else route
@@ -143,7 +143,8 @@ def _run_attend(case, rows_sample=None, route=None, r_low=None, fast=None):
     log(f"attend {cfg.name} fast={fast} Nq={cfg.Nq} N_hist={n_hist} N_cur={cfg.N_cur} "
         f"r_low={r_low} route={route}")
     if fast:
-        out, lse = lib.attend_fast(shape, kb, vb, n_hist, route, r_low, q, ck, cv)
+        dmaps = None if maps is None else tuple(to_dev(m, cfg.dtype) for m in maps)
+        out, lse = lib.attend_fast(shape, kb, vb, n_hist, route, r_low, q, ck, cv, maps=dmaps)
     else:
         out, lse = lib.attend_full(shape, kb, vb, n_hist, q, ck, cv)
     torch.cuda.synchronize()
@@ -151,13 +152,14 @@ def _run_attend(case, rows_sample=None, route=None, r_low=None, fast=None):
     return from_dev(out)[rows], from_dev(lse)[rows], rows
 
 
-def _oracle_attend(case, rows, fast, route, r_low):
+def _oracle_attend(case, rows, fast, route, r_low, maps=None):
     cfg = case.cfg
     q, ck, cv = oracle_inputs(case, rows)
     kb, vb = oracle_branch(case, 0), oracle_branch(case, 1)
     if not fast:
         return oracle_full_chunked(q, kb, vb, ck, cv, cfg)
-    return oracle.attend_fast(q, kb, vb, route, r_low, ck, cv, cfg.H, cfg.d, cfg.tau)
+    omaps = None if maps is None else tuple(oracle.as_f64(m, cfg.dtype) for m in maps)
+    return oracle.attend_fast(q, kb, vb, route, r_low, ck, cv, cfg.H, cfg.d, cfg.tau, maps=omaps)
 
 
 def _check_attend(name, sample=None, route=None, r_low=None, drule=None):
@@ -228,6 +230,65 @@ def test_attend_fast_anchor_routing_per_head():
 
 def test_attend_fast_C3_table6_widths():
     _check_attend("C3", sample=40, r_low=[32, 64, 96, 128] * 6, drule=0.5)
+
+
+def _adapted_maps(cfg, ld, eps=1.0, seed=5):
+    """Seeded stand-ins for adapted low-dimensional maps (Table 8): each
+    decoder padded to ld columns plus a perturbation of relative size eps."""
+    w = synth.workload(cfg)
+    rng = np.random.default_rng(seed)
+    out = []
+    for b in range(2):
+        D = np.zeros((cfg.W, ld))
+        D[:, :cfg.r] = oracle.as_f64(w.decoder(b), cfg.dtype)[:, :ld]
+        out.append(synth.store(D + eps * rng.standard_normal((cfg.W, ld)) / np.sqrt(cfg.W),
+                               cfg.dtype))
+    return tuple(out)
+
+
+def _check_maps(name, widths, ld, sample=None):
+    """Fast read with caller-given maps against the oracle with the same
+    maps; it must also sit closer to that than to the analytical-map read."""
+    cfg = _cfg(name)
+    case = get_case(cfg)
+    maps = _adapted_maps(cfg, ld)
+    route = cfg.segments()
+    out, lse, rows = _run_attend(case, sample, route, widths, maps=maps)
+    ro, rl = _oracle_attend(case, rows, True, route, widths, maps)
+    rel, lerr = attention_errors(out, lse, ro, rl)
+    ra, _ = _oracle_attend(case, rows, True, route, widths)
+    gap = float(np.max(np.abs(ra - ro)))
+    err = float(np.max(np.abs(out - ro)))
+    log(f"  {name} maps ld={ld}: rel={rel:.3e} dLSE={lerr:.3e} gap to analytical={gap:.3e} "
+        f"err={err:.3e}")
+    assert rel <= OUT_TOL and lerr <= LSE_TOL
+    assert err <= 0.5 * gap
+
+
+def test_attend_fast_maps_tuned():
+    # ld % 8 == 0: the tuned kernels
+    _check_maps("S9", [32, 64, 96, 128], ld=160)
+
+
+def test_attend_fast_maps_generic_ld():
+    # ld = r + 3 is not a multiple of 8: the same call on the generic kernels
+    _check_maps("S9", [32, 64, 96, 128], ld=163)
+
+
+def test_attend_fast_maps_f32():
+    _check_maps("C0f", [4, 6], ld=10)
+
+
+def test_analytical_maps_equal_heads_call():
+    """Passing the decoders themselves as maps reproduces the per-head call
+    bit for bit."""
+    cfg = _cfg("S9")
+    case = get_case(cfg)
+    w = synth.workload(cfg)
+    widths = [32, 64, 96, 128]
+    out_h, lse_h, _ = _run_attend(case, r_low=widths)
+    out_m, lse_m, _ = _run_attend(case, r_low=widths, maps=(w.decoder(0), w.decoder(1)))
+    assert np.array_equal(out_h, out_m) and np.array_equal(lse_h, lse_m)
 
 
 def test_attend_full_C1():
