@@ -433,6 +433,63 @@ nkv_status nkv_attend_fast(const nkv_shape* shape, const nkv_branch* k, const nk
                        cur_v, N_cur, out, lse, ws, ws_bytes, stream, true);
 }
 
+size_t nkv_fit_workspace_size(const nkv_shape* shape, int64_t N, int32_t A) {
+  g_err[0] = 0;
+  if (check_shape(shape) || N < 0 || A < 1) return SIZE_MAX;
+  const int64_t W = (int64_t)shape->H * shape->d;
+  size_t off = tuned_applies(shape, 0) ? tuned_assign_workspace(N, A) : 0;
+  off = align_up(off + sizeof(int32_t) * (size_t)N, 256);        // assignment
+  off = align_up(off + sizeof(int32_t) * (size_t)N, 256);        // rows sorted by center
+  off = align_up(off + sizeof(int32_t) * (3 * (size_t)A + 1), 256);  // counts, offsets, cursor
+  return off;
+}
+
+nkv_status nkv_fit_centers(const nkv_shape* shape, const void* x, int64_t N, void* centers,
+                           int32_t A, int32_t iters, int32_t* idx, int32_t* counts, void* ws,
+                           size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  nkv_status st = check_shape(shape);
+  if (st) return st;
+  if (N < 0 || iters < 0) NKV_FAIL(NKV_EINVAL, "N and iters must be non-negative");
+  if (N > (int64_t)1 << 31) NKV_FAIL(NKV_EUNSUPPORTED, "N above 2^31");
+  if (A < 1) NKV_FAIL(NKV_EINVAL, "A=%d must be positive", A);
+  if (A > 65536) NKV_FAIL(NKV_EUNSUPPORTED, "A above 65536");
+  if (!centers) NKV_FAIL(NKV_EINVAL, "centers is NULL");
+  if (N > 0 && !x) NKV_FAIL(NKV_EINVAL, "x is NULL with N>0");
+  if (reinterpret_cast<uintptr_t>(x) & 15) NKV_FAIL(NKV_EINVAL, "x must be 16-byte aligned");
+  const size_t need = nkv_fit_workspace_size(shape, N, A);
+  if (!ws || ws_bytes < need)
+    NKV_FAIL(NKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int W = shape->H * shape->d;
+  const bool tuned = tuned_applies(shape, 0);
+  char* base = static_cast<char*>(ws);
+  const size_t a_bytes = tuned ? tuned_assign_workspace(N, A) : 0;
+  int32_t* lab = reinterpret_cast<int32_t*>(base + a_bytes);
+  size_t off = align_up(a_bytes + sizeof(int32_t) * (size_t)N, 256);
+  int32_t* perm = reinterpret_cast<int32_t*>(base + off);
+  off = align_up(off + sizeof(int32_t) * (size_t)N, 256);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + off);
+  int32_t* offs = cnt + A;
+  int32_t* cursor = offs + A + 1;
+  auto assign = [&](int32_t* out) -> nkv_status {
+    if (N == 0) return NKV_OK;
+    if (tuned) return tuned_assign(shape, x, N, centers, A, out, base, s);
+    return launch_assign_generic(shape->dtype, x, N, W, centers, A, out, s);
+  };
+  for (int it = 0; it < iters; ++it) {
+    if ((st = assign(lab))) return st;
+    if ((st = launch_fit_update(shape->dtype, x, N, W, lab, A, cnt, offs, cursor, perm, centers, s)))
+      return st;
+  }
+  if (idx || counts) {
+    int32_t* out = idx ? idx : lab;
+    if ((st = assign(out))) return st;
+    if (counts && (st = launch_fit_counts(out, N, A, counts, s))) return st;
+  }
+  return NKV_OK;
+}
+
 nkv_status nkv_lse_merge(int64_t Nq, int32_t H, int32_t d, const float* o_a, const float* lse_a,
                          const float* o_b, const float* lse_b, void* out, int32_t out_dtype,
                          float* lse_out, void* stream) {

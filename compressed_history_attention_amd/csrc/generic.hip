@@ -311,6 +311,17 @@ nkv_status launch_encode_generic(int dt, const void* x, int64_t N, int W, const 
   return NKV_OK;
 }
 
+nkv_status launch_assign_generic(int dt, const void* x, int64_t N, int W, const void* centers,
+                                 int A, int32_t* idx, hipStream_t s) {
+  if (N == 0) return NKV_OK;
+  NKV_DT_DISPATCH(dt, {
+    hipLaunchKernelGGL(k_assign_generic<DT>, dim3((unsigned)N), dim3(256), W * sizeof(float), s,
+                       x, N, W, centers, A, idx);
+    NKV_LAUNCH_CHECK();
+  });
+  return NKV_OK;
+}
+
 nkv_status launch_decode_generic(int dt, const BranchArgs& b, int W, int r, int group,
                                  const RangeTable& rows, float* out, hipStream_t s) {
   if (rows.total == 0) return NKV_OK;

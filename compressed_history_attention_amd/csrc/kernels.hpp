@@ -29,6 +29,8 @@ struct LowMaps {
 nkv_status launch_encode_generic(int dt, const void* x, int64_t N, int W, const void* centers,
                                  int A, const void* enc, int r, int group, int32_t* idx,
                                  uint8_t* codes, uint16_t* scales, hipStream_t s);
+nkv_status launch_assign_generic(int dt, const void* x, int64_t N, int W, const void* centers,
+                                 int A, int32_t* idx, hipStream_t s);
 nkv_status launch_decode_generic(int dt, const BranchArgs& b, int W, int r, int group,
                                  const RangeTable& rows, float* out, hipStream_t s);
 nkv_status launch_rows_to_f32(int dt, const void* src, int64_t n, float* dst, hipStream_t s);
@@ -46,6 +48,15 @@ nkv_status launch_low_generic(int dt, const void* q, int64_t Nq, int H, int d, i
 // per-head generic low-dimensional read
 nkv_status launch_head_rows(int64_t Nq, int H, const HeadSet& hs, int32_t* rows, int32_t* nrows,
                             hipStream_t s);
+
+// center fitting (fit.hip): rows sorted by center (counts, offsets, cursor,
+// perm), then per center the fp64 mean of its rows stored in the codec dtype
+// (empty centers kept)
+nkv_status launch_fit_update(int dt, const void* x, int64_t N, int W, const int32_t* idx, int A,
+                             int32_t* counts, int32_t* offs, int32_t* cursor, int32_t* perm,
+                             void* centers, hipStream_t s);
+nkv_status launch_fit_counts(const int32_t* idx, int64_t N, int A, int32_t* counts,
+                             hipStream_t s);
 
 // LSE merge (merge.hip)
 nkv_status launch_lse_merge(int64_t Nq, int H, int d, const float* o_a, const float* lse_a,

@@ -6,6 +6,10 @@
 namespace nkv {
 
 size_t tuned_encode_workspace(const nkv_shape* s, int64_t N, int32_t A);
+// nearest center per token only (the encoder's first stage)
+size_t tuned_assign_workspace(int64_t N, int32_t A);
+nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void* centers,
+                        int32_t A, int32_t* idx, char* ws, hipStream_t st);
 nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void* centers,
                         int32_t A, const void* enc, int32_t* idx, uint8_t* codes,
                         uint16_t* scales, char* ws, size_t ws_bytes, hipStream_t st);

@@ -184,10 +184,32 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
   if (j % group == 0) scales[t * (r / group) + j / group] = __half_as_ushort(sh);
 }
 
+size_t tuned_assign_workspace(int64_t N, int32_t A) {
+  return align_up(sizeof(float) * A, 256) + align_up(sizeof(uint64_t) * N, 256);
+}
+
+nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void* centers,
+                        int32_t A, int32_t* idx, char* ws, hipStream_t st) {
+  const int W = s->H * s->d;
+  float* mu2 = reinterpret_cast<float*>(ws);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(ws + align_up(sizeof(float) * A, 256));
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* mub = static_cast<const uint16_t*>(centers);
+  hipLaunchKernelGGL(k_center_norms, dim3(A), dim3(64), 0, st, mub, A, W, mu2);
+  NKV_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N,
+                     ~0ull);
+  NKV_LAUNCH_CHECK();
+  DistProblem dp{A, (int)N, W, mub, xb, mu2, keys};
+  nkv_status e;
+  if ((e = launch_gemm(dp, 1, st))) return e;
+  hipLaunchKernelGGL(k_unpack_idx, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N, idx);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
 size_t tuned_encode_workspace(const nkv_shape* s, int64_t N, int32_t A) {
-  size_t off = 0;
-  off = align_up(off + sizeof(float) * A, 256);
-  off = align_up(off + sizeof(uint64_t) * N, 256);
+  size_t off = tuned_assign_workspace(N, A);
   off = align_up(off + sizeof(float) * N * s->r * proj_splits(s->H * s->d), 256);
   return off;
 }
@@ -196,26 +218,14 @@ nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void
                         int32_t A, const void* enc, int32_t* idx, uint8_t* codes,
                         uint16_t* scales, char* ws, size_t ws_bytes, hipStream_t st) {
   const int W = s->H * s->d, r = s->r;
-  float* mu2 = reinterpret_cast<float*>(ws);
-  size_t off = align_up(sizeof(float) * A, 256);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(ws + off);
-  off = align_up(off + sizeof(uint64_t) * N, 256);
-  float* z = reinterpret_cast<float*>(ws + off);
+  float* z = reinterpret_cast<float*>(ws + tuned_assign_workspace(N, A));
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* mub = static_cast<const uint16_t*>(centers);
   nkv_status e;
   const int splits = proj_splits(W);
   {
   ProfScope ps("encode_assign", st);
-  hipLaunchKernelGGL(k_center_norms, dim3(A), dim3(64), 0, st, mub, A, W, mu2);
-  NKV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N,
-                     ~0ull);
-  NKV_LAUNCH_CHECK();
-  DistProblem dp{A, (int)N, W, mub, xb, mu2, keys};
-  if ((e = launch_gemm(dp, 1, st))) return e;
-  hipLaunchKernelGGL(k_unpack_idx, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N, idx);
-  NKV_LAUNCH_CHECK();
+  if ((e = tuned_assign(s, x, N, centers, A, idx, ws, st))) return e;
   }
   {
   ProfScope ps("encode_project", st);

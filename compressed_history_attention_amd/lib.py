@@ -121,6 +121,8 @@ def load() -> ctypes.CDLL:
         "nkv_attend_fast_maps": (ctypes.c_int, [SH, BR, BR, I64, SG, I32, ctypes.POINTER(I32), MP,
                                                 P, I64, P, P, I64, P, P, P, SZ, P]),
         "nkv_lse_merge": (ctypes.c_int, [I64, I32, I32, P, P, P, P, P, I32, P, P]),
+        "nkv_fit_workspace_size": (SZ, [SH, I64, I32]),
+        "nkv_fit_centers": (ctypes.c_int, [SH, P, I64, P, I32, I32, P, P, P, SZ, P]),
         "nkv_route_segments": (ctypes.c_int, [ctypes.POINTER(nkv_route_policy), I64, SG, I32,
                                               ctypes.POINTER(I32)]),
         "nkv_storage_account": (ctypes.c_int, [SH, I32, I32, I64, ctypes.POINTER(nkv_storage)]),
@@ -144,7 +146,7 @@ EXPORTS = ("nkv_version", "nkv_last_error", "nkv_status_string", "nkv_force_gene
            "nkv_encode_workspace_size", "nkv_encode", "nkv_attend_workspace_size",
            "nkv_attend_full", "nkv_attend_fast", "nkv_attend_heads_workspace_size",
            "nkv_attend_fast_heads", "nkv_attend_maps_workspace_size", "nkv_attend_fast_maps",
-           "nkv_lse_merge", "nkv_route_segments", "nkv_storage_account",
+           "nkv_lse_merge", "nkv_fit_workspace_size", "nkv_fit_centers", "nkv_route_segments", "nkv_storage_account",
            "nkv_layer_attend_workspace_size", "nkv_layer_attend", "nkv_layer_append_workspace_size",
            "nkv_layer_append", "nkv_profile_enable", "nkv_profile_read")
 
@@ -352,6 +354,32 @@ def nkv_lse_merge(H: int, d: int, o_a, lse_a, o_b, lse_b, out, lse_out, stream=N
     dt = NKV_F32 if out.dtype == torch.float32 else NKV_BF16
     _check(load().nkv_lse_merge(int(o_a.shape[0]), H, d, _ptr(o_a), _ptr(lse_a), _ptr(o_b),
                                 _ptr(lse_b), _ptr(out), dt, _ptr(lse_out), _stream(stream)))
+
+
+def nkv_fit_workspace_size(shape: Shape, N: int, A: int) -> int:
+    n = load().nkv_fit_workspace_size(ctypes.byref(shape.c()), N, A)
+    if n == SIZE_MAX:
+        raise NkvError(1, "invalid fit arguments")
+    return n
+
+
+def nkv_fit_centers(shape: Shape, x, centers, iters: int, idx=None, counts=None, ws=None,
+                    stream=None):
+    N = int(x.shape[0])
+    _check(load().nkv_fit_centers(ctypes.byref(shape.c()), _ptr(x), N, _ptr(centers),
+                                  int(centers.shape[0]), int(iters), _ptr(idx), _ptr(counts),
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def fit_centers(shape: Shape, x, centers, iters: int, stream=None):
+    """Lloyd iterations in place on ``centers``; returns (centers, idx, counts)
+    with idx/counts the assignment to the returned centers."""
+    N, A = int(x.shape[0]), int(centers.shape[0])
+    idx = torch.empty(N, dtype=torch.int32, device=centers.device)
+    counts = torch.empty(A, dtype=torch.int32, device=centers.device)
+    ws = _workspace(nkv_fit_workspace_size(shape, N, A), centers.device)
+    nkv_fit_centers(shape, x, centers, iters, idx if N else None, counts, ws=ws, stream=stream)
+    return centers, idx, counts
 
 
 @dataclass(frozen=True)

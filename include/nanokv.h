@@ -243,6 +243,29 @@ nkv_status nkv_lse_merge(int64_t Nq, int32_t H, int32_t d, const float* o_a,
                          const float* lse_b, void* out, int32_t out_dtype,
                          float* lse_out, void* stream);
 
+/* Workspace bytes for nkv_fit_centers (never 0); SIZE_MAX if invalid. */
+size_t nkv_fit_workspace_size(const nkv_shape* shape, int64_t N, int32_t A);
+
+/*
+ * Center fitting for one branch (the NanoKV page fits K and V centers
+ * separately, Table 5 caption, without printing how; this is Lloyd's
+ * k-means).  `centers` [A, W] holds the initial centers and receives the
+ * fitted ones.  Each of `iters` iterations assigns every row of x [N, W] to
+ * its nearest center exactly as nkv_encode does (squared L2, ties to the
+ * lowest index), then replaces every center that received rows by their
+ * mean, rounded once (half to even) to the shape dtype; a center that
+ * received none keeps its value.  Optional outputs (NULL to skip): idx [N]
+ * int32, each row's nearest center among the returned centers; counts [A]
+ * int32, rows per returned center under that assignment.  iters == 0 only
+ * assigns.  x must be 16-byte aligned (NKV_EINVAL otherwise).  Means are
+ * summed in fp64 (see the implementation for when the sum is
+ * order-independent).
+ */
+nkv_status nkv_fit_centers(const nkv_shape* shape, const void* x, int64_t N,
+                           void* centers, int32_t A, int32_t iters,
+                           int32_t* idx, int32_t* counts, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Rollout support: per-layer routing policy, per-layer compressed cache and
  * storage accounting.  Every chunk of an autoregressive rollout attends, at

@@ -161,3 +161,27 @@ def test_status_strings():
     L = lib.load()
     assert L.nkv_status_string(0) == b"ok"
     assert L.nkv_status_string(3) == b"workspace too small"
+
+
+def test_fit_validation():
+    L = lib.load()
+    sh = _shape()
+
+    def call(shape=sh, x=FAKE, N=8, c=FAKE, A=4, iters=1, ws=FAKE, wsb=1 << 30):
+        return L.nkv_fit_centers(None if shape is None else ctypes.byref(shape), x, N, c, A, iters,
+                                 None, None, ws, wsb, None)
+
+    assert call(shape=None) == EINVAL
+    assert call(iters=-1) == EINVAL
+    assert call(N=-1) == EINVAL
+    assert call(A=0) == EINVAL
+    assert call(A=70000) == EUNSUP
+    assert call(c=None) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(x=FAKE + 4) == EINVAL        # x must be 16-byte aligned
+    assert call(ws=None) == EWS
+    assert call(wsb=16) == EWS
+    assert call(shape=_shape(d=100)) == EUNSUP
+    assert L.nkv_fit_workspace_size(ctypes.byref(sh), -1, 4) == lib.SIZE_MAX
+    assert L.nkv_fit_workspace_size(ctypes.byref(sh), 8, 0) == lib.SIZE_MAX
+    assert L.nkv_fit_workspace_size(ctypes.byref(sh), 8, 4) > 0
