@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "prof.hpp"
 #include "tuned.hpp"
 
 namespace nkv {
@@ -478,7 +479,11 @@ nkv_status nkv_fit_centers(const nkv_shape* shape, const void* x, int64_t N, voi
     return launch_assign_generic(shape->dtype, x, N, W, centers, A, out, s);
   };
   for (int it = 0; it < iters; ++it) {
-    if ((st = assign(lab))) return st;
+    {
+      ProfScope ps("fit_assign", s);
+      if ((st = assign(lab))) return st;
+    }
+    ProfScope ps("fit_update", s);
     if ((st = launch_fit_update(shape->dtype, x, N, W, lab, A, cnt, offs, cursor, perm, centers, s)))
       return st;
   }
