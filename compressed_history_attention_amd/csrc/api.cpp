@@ -303,7 +303,7 @@ static size_t workspace_common(const nkv_shape* shape, int32_t A_k, int32_t A_v,
     r_low_h = nullptr;
   }
   if (tuned_applies_all(shape, r_low, r_low_h) && (low.total == 0 || tuned_maps))
-    return tuned_attend_workspace(shape, A_k, A_v, full, low, r_low, Nq, N_cur);
+    return tuned_attend_workspace(shape, A_k, A_v, full, low, r_low, r_low_h, Nq, N_cur);
   return generic_layout(shape, full.total, low.total, Nq, N_cur, r_low_h != nullptr).total;
 }
 

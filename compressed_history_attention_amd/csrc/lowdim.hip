@@ -25,6 +25,7 @@
 //    sums from any split simply add.  Rows whose bound could be loose by
 //    more than 2^60 are recomputed exactly by the generic kernel.
 #include <algorithm>
+#include <vector>
 
 #include "lowdim.hpp"
 #include "prof.hpp"
@@ -77,7 +78,7 @@ struct Plan {
 };
 
 Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& low, int32_t r_low,
-               int64_t Nq) {
+               int64_t Nq, int64_t part_units) {
   Plan P;
   const int64_t W = (int64_t)s->H * s->d;
   P.n_low = low.total;
@@ -116,9 +117,11 @@ Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& l
   P.tile_bucket = take(sizeof(int32_t) * P.max_tiles);
   P.perm = take(sizeof(int32_t) * P.max_slots);
   P.img = take((size_t)P.max_tiles * P.g.bytes);
-  P.acc = take(sizeof(float) * P.rows * r_low);
-  P.wmass = take(sizeof(float) * P.rows * A_v);
-  P.ell = take(sizeof(float) * P.rows);
+  // partial sums of the main pass: (split, query, head of the group) rows
+  const int64_t prows = Nq * part_units;
+  P.acc = take(sizeof(float) * prows * r_low);
+  P.wmass = take(sizeof(float) * prows * A_v);
+  P.ell = take(sizeof(float) * prows);
   P.total = off;
   return P;
 }
@@ -482,9 +485,9 @@ struct MainArgs {
   float* wmass;
   float* ell;
   int64_t Nq;
-  int H, A_k, A_v, GK, NB, r_low;
+  int H, A_k, A_v, GK, GV, NB, r_low;
   float c;
-  HeadSet hs;  // grid row y serves head hs.h[y]
+  HeadSet hs;  // grid row y serves head hs.h[y]; grid z = key-range split
 };
 
 constexpr int RBW = 256;                // query rows per block: 8 waves x 32 rows
@@ -565,6 +568,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = a.hs.h[blockIdx.y];
+  const int split = blockIdx.z, nsplit = gridDim.z;
   const int W = a.H * 128;
   const int64_t q0 = (int64_t)blockIdx.x * RBW;
   const int rloc = wave * 32 + (lane & 31);
@@ -572,6 +576,8 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   const bool rok = qrow < a.Nq;
   const bool active = q0 + wave * 32 < a.Nq;  // the wave owns at least one row
   const int64_t grow = (rok ? qrow : q0) * a.H + h;
+  // partial-sum row of this (key-range split, query, head of the group)
+  const int64_t prow = ((int64_t)split * a.Nq + (rok ? qrow : q0)) * a.hs.n + blockIdx.y;
 
   f16x8 qtf[RLP / 16];
 #pragma unroll
@@ -586,7 +592,10 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   accW[1] = zero16();
   float lsum = 0.f;
 
+  // this split's tiles [ts, te) of the bucket-sorted sequence
   const int ntiles = __builtin_amdgcn_readfirstlane(a.tile_start[a.NB]);
+  const int ts = __builtin_amdgcn_readfirstlane((int)((int64_t)ntiles * split / nsplit));
+  const int te = __builtin_amdgcn_readfirstlane((int)((int64_t)ntiles * (split + 1) / nsplit));
   const char* sTrow = reinterpret_cast<const char*>(sT + rloc * TS);
   const uint16_t* qsrc = a.q + (rok ? qrow : q0) * W + h * 128 + 8 * hl;
 
@@ -599,7 +608,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   // the k-th of this wave's 1 KiB chunks of tile tt into `dst`
   auto dma = [&](int tt, char* dst, int k) __attribute__((always_inline)) {
     const int c = wave + 8 * k;
-    if (c < Geo::CHUNKS && tt < ntiles) {
+    if (c < Geo::CHUNKS && tt < te) {
       const char* chunk = a.img + ((int64_t)tt * G.bytes + c * 1024);  // wave-uniform
       __builtin_amdgcn_global_load_lds(chunk + (uint32_t)(lane * 16),
                                        (__attribute__((address_space(3))) void*)(dst + c * 1024),
@@ -607,10 +616,10 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     }
   };
 
-  // masses of a finished a^V range straight from the accumulators
-  auto flush = [&](int gv) __attribute__((always_inline)) {
+  // masses of the a^V range gv from the accumulators
+  auto put_mass = [&](int gv) __attribute__((always_inline)) {
     if (rok) {
-      float* dst = a.wmass + grow * a.A_v + gv * CR;
+      float* dst = a.wmass + prow * a.A_v + gv * CR;
       const int lim = a.A_v - gv * CR;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
@@ -628,9 +637,25 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
           }
         }
     }
+  };
+  // zeros for the a^V ranges [g0, g1) this split never visits (the
+  // restoration reads every range)
+  auto zero_mass = [&](int g0, int g1) __attribute__((always_inline)) {
+    if (!rok) return;
+    for (int gv = g0; gv < g1; ++gv) {
+      float* dst = a.wmass + prow * a.A_v + gv * CR;
+      const int lim = min(CR, a.A_v - gv * CR);
+      for (int c = hl; c < lim; c += 2) dst[c] = 0.f;
+    }
+  };
+  int zgv = 0;  // first a^V range of this split's rows not yet written
+  auto flush = [&](int gv) __attribute__((always_inline)) {
+    if (zgv < gv) zero_mass(zgv, gv);
+    put_mass(gv);
+    zgv = gv + 1;
     accW[0] = zero16();
     accW[1] = zero16();
-    };
+  };
 
   // T[row][center] = c mu^K_{center,h} . q_h - B for the wave's rows
   // (exact bf16 products, fp32 sums) into the wave's own rows of sT
@@ -667,13 +692,13 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   // bucket facts of the tile about to be processed: tile 0's from the tables,
   // every later tile's from the header of the tile before it
   int cur_b = 0, cur_first = 0, cur_ngk = -1;
-  if (ntiles > 0) {
-    cur_b = a.tile_bucket[0];
-    cur_first = 1;
+  if (ts < te) {
+    cur_b = a.tile_bucket[ts];
+    cur_first = 1;  // a split may start inside a bucket: its T slice is still needed
     const int tn = a.tile_start[cur_b + 1];
     cur_ngk = tn < ntiles ? a.tile_bucket[tn] % a.GK : -1;
     if constexpr (SM) load_mu(cur_b % a.GK);
-    load_tile<RLP>(a.img, sB0, wave, lane);
+    load_tile<RLP>(a.img + (int64_t)ts * G.bytes, sB0, wave, lane);
   }
 
   int prev_gv = -1;
@@ -806,13 +831,14 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     pv(vb, p);
   };
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = ts; t < te; t += 2) {
     body(t, sB0, sB1);
-    if (t + 1 < ntiles) body(t + 1, sB1, sB0);
+    if (t + 1 < te) body(t + 1, sB1, sB0);
   }
   // no row or tile load may still be in flight into LDS when the block ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (prev_gv >= 0) flush(prev_gv);
+  if (zgv < a.GV) zero_mass(zgv, a.GV);
   lsum += __shfl_xor(lsum, 32, 64);
   if (rok) {
 #pragma unroll
@@ -821,17 +847,17 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       for (int e4 = 0; e4 < 4; ++e4) {
         const int dim = db * 32 + e4 * 8 + hl * 4;  // r_low % 16 == 0: whole f32x4 or none
         if (dim < a.r_low)
-          *reinterpret_cast<f32x4*>(a.acc + grow * a.r_low + dim) =
+          *reinterpret_cast<f32x4*>(a.acc + prow * a.r_low + dim) =
               f32x4{accT[db][4 * e4], accT[db][4 * e4 + 1], accT[db][4 * e4 + 2],
                     accT[db][4 * e4 + 3]};
       }
-    if (hl == 0) a.ell[grow] = lsum;
+    if (hl == 0) a.ell[prow] = lsum;
   }
 }
 
 template <int RLP>
-nkv_status launch_main(const MainArgs& m, int64_t Nq, hipStream_t st) {
-  dim3 grid((unsigned)ceil_div(Nq, RBW), (unsigned)m.hs.n);
+nkv_status launch_main(const MainArgs& m, int64_t Nq, int nsplit, hipStream_t st) {
+  dim3 grid((unsigned)ceil_div(Nq, RBW), (unsigned)m.hs.n, (unsigned)nsplit);
   hipLaunchKernelGGL(k_low_rows<RLP>, grid, dim3(512), 0, st, m);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
@@ -845,44 +871,53 @@ struct RestoreProblem {
   static constexpr int BK = 64;
   int M, N, K;  // Nq, 128, 2 ra + 2 av
   int H, ldv, r_low, ra, A_v, av;
-  const float* acc;
-  const float* wmass;
+  int nsplit;   // key-range splits of the main pass: their partial sums add
+  const float* acc;    // partials [nsplit][Nq][hs.n][r_low]
+  const float* wmass;  // partials [nsplit][Nq][hs.n][A_v]
   const uint16_t* dv;    // restoration map [W, ldv]
   const uint16_t* mvt;   // [W, av]
-  const float* ell;
+  const float* ell;     // partials [nsplit][Nq][hs.n]
   const float* bound;
   float* o_low;
   float* lse_low;
   HeadSet hs;  // batch z serves head hs.h[z]
+  // partial row of split s for query m and group head zb
+  __device__ int64_t prow(int s, int m, int zb) const {
+    return ((int64_t)s * M + m) * hs.n + zb;
+  }
   __device__ u32x4 load_a(int zb, int m, int k) const {
     if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
-    const int64_t row = (int64_t)m * H + hs.h[zb];
     float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
     bool lo;
     if (k < 2 * ra) {
       lo = k >= ra;
       const int j = lo ? k - ra : k;
       if (j + 8 <= r_low) {  // r_low % 16 == 0: 32-byte aligned row chunk
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(acc + row * r_low + j);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(acc + row * r_low + j + 4);
+        for (int s = 0; s < nsplit; ++s) {
+          const float* src = acc + prow(s, m, zb) * r_low + j;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { v[i] = x0[i]; v[4 + i] = x1[i]; }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+          for (int i = 0; i < 4; ++i) { v[i] += x0[i]; v[4 + i] += x1[i]; }
+        }
       }
     } else {
       const int kk = k - 2 * ra;
       lo = kk >= av;
       const int c = lo ? kk - av : kk;
-      if ((A_v & 3) == 0 && c + 8 <= A_v) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(wmass + row * A_v + c);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(wmass + row * A_v + c + 4);
+      for (int s = 0; s < nsplit; ++s) {
+        const float* src = wmass + prow(s, m, zb) * A_v + c;
+        if ((A_v & 3) == 0 && c + 8 <= A_v) {
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { v[i] = x0[i]; v[4 + i] = x1[i]; }
-      } else {
+          for (int i = 0; i < 4; ++i) { v[i] += x0[i]; v[4 + i] += x1[i]; }
+        } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (c + i < A_v) ? wmass[row * A_v + c + i] : 0.f;
+          for (int i = 0; i < 8; ++i) v[i] += (c + i < A_v) ? src[i] : 0.f;
+        }
       }
     }
     u32x4 out;
@@ -918,7 +953,8 @@ struct RestoreProblem {
         const int m = m0 + 32 * i + acc_row(e, lane);
         if (m >= M) continue;
         const int64_t row = (int64_t)m * H + z;
-        const float l = ell[row];
+        float l = 0.f;
+        for (int s = 0; s < nsplit; ++s) l += ell[prow(s, m, zb)];
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -934,19 +970,46 @@ struct RestoreProblem {
 
 }  // namespace
 
+int low_splits(int64_t Nq, int n_heads, int64_t n_low) {
+  const int64_t blocks = ceil_div(Nq, RBW) * n_heads;
+  int64_t S = std::max<int64_t>(1, 512 / std::max<int64_t>(blocks, 1));  // ~2 blocks per CU
+  S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(n_low, NT) / 8));  // >= 8 tiles each
+  return (int)std::min<int64_t>(S, 16);
+}
+
+int64_t low_part_units(int64_t Nq, int H, int32_t r_low, const int32_t* r_low_h, int64_t n_low) {
+  int64_t best = 0;
+  std::vector<int> done(H, 0);
+  for (int h0 = 0; h0 < H; ++h0) {
+    if (done[h0]) continue;
+    int n = 0;
+    for (int h = h0; h < H; ++h) {
+      const int w0 = r_low_h ? r_low_h[h0] : r_low, w = r_low_h ? r_low_h[h] : r_low;
+      if (!done[h] && w == w0) {
+        done[h] = 1;
+        ++n;
+      }
+    }
+    best = std::max<int64_t>(best, (int64_t)n * low_splits(Nq, n, n_low));
+  }
+  return best;
+}
+
 size_t low_workspace_bytes(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& low,
-                           int32_t r_low, int64_t Nq) {
-  return make_plan(s, A_k, A_v, low, r_low, Nq).total;
+                           int32_t r_low, const int32_t* r_low_h, int64_t Nq) {
+  const int64_t units = low_part_units(Nq, s->H, r_low, r_low_h, low.total);
+  return make_plan(s, A_k, A_v, low, r_low, Nq, units).total;
 }
 
 nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
                       const LowMaps& mp, const RangeTable& low, int32_t r_low, float tau,
                       const uint16_t* q,
                       int64_t Nq, float* o_low, float* lse_low, char* ws, int32_t r_low_max,
-                      const HeadSet& hs, bool first, hipStream_t st) {
+                      int64_t part_units, const HeadSet& hs, bool first, hipStream_t st) {
   // offsets from the widest group's plan, so that every group finds the
   // shared sort results in the same place; geometry from this group's width
-  const Plan P = make_plan(s, kb.A, vb.A, low, r_low_max, Nq);
+  const Plan P = make_plan(s, kb.A, vb.A, low, r_low_max, Nq, part_units);
+  const int nsplit = low_splits(Nq, hs.n, low.total);
   const int rlp = (int)ceil_div(r_low, 16) * 16, ra = (int)ceil_div(r_low, 32) * 32;
   const TileGeom geom = tile_geom(rlp);
   const int H = s->H, W = H * s->d, r = s->r;
@@ -1025,16 +1088,16 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   {
   ProfScope ps_main("low_main", st);
   MainArgs m{q, static_cast<const uint16_t*>(kb.centers), qt16, bound, img, tile_start,
-             tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.NB, r_low, c, hs};
+             tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.GV, P.NB, r_low, c, hs};
   switch (rlp) {
-    case 16: e = launch_main<16>(m, Nq, st); break;
-    case 32: e = launch_main<32>(m, Nq, st); break;
-    case 48: e = launch_main<48>(m, Nq, st); break;
-    case 64: e = launch_main<64>(m, Nq, st); break;
-    case 80: e = launch_main<80>(m, Nq, st); break;
-    case 96: e = launch_main<96>(m, Nq, st); break;
-    case 112: e = launch_main<112>(m, Nq, st); break;
-    case 128: e = launch_main<128>(m, Nq, st); break;
+    case 16: e = launch_main<16>(m, Nq, nsplit, st); break;
+    case 32: e = launch_main<32>(m, Nq, nsplit, st); break;
+    case 48: e = launch_main<48>(m, Nq, nsplit, st); break;
+    case 64: e = launch_main<64>(m, Nq, nsplit, st); break;
+    case 80: e = launch_main<80>(m, Nq, nsplit, st); break;
+    case 96: e = launch_main<96>(m, Nq, nsplit, st); break;
+    case 112: e = launch_main<112>(m, Nq, nsplit, st); break;
+    case 128: e = launch_main<128>(m, Nq, nsplit, st); break;
     default: set_error("tuned low-dimensional read supports r_low <= 128"); return NKV_EUNSUPPORTED;
   }
   if (e) return e;
@@ -1042,7 +1105,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   // restoration
   {
   ProfScope ps_restore("low_restore", st);
-  RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, mp.ld, r_low, ra, vb.A, P.av, acc, wmass,
+  RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, mp.ld, r_low, ra, vb.A, P.av, nsplit, acc, wmass,
                     static_cast<const uint16_t*>(mp.omap), mvt, ell, bound, o_low, lse_low, hs};
   if ((e = launch_gemm(rp, hs.n, st))) return e;
   }

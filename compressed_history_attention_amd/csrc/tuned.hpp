@@ -15,7 +15,8 @@ nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void
                         uint16_t* scales, char* ws, size_t ws_bytes, hipStream_t st);
 
 size_t tuned_attend_workspace(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& full,
-                              const RangeTable& low, int32_t r_low, int64_t Nq, int64_t N_cur);
+                              const RangeTable& low, int32_t r_low, const int32_t* r_low_h,
+                              int64_t Nq, int64_t N_cur);
 // r_low_h: NULL, or one width per head (r_low is then the widest); mp: the
 // low-dimensional maps
 nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,

@@ -17,7 +17,8 @@ struct Layout {
 };
 
 Layout make_layout(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& full,
-                   const RangeTable& low, int32_t r_low, int64_t Nq, int64_t N_cur) {
+                   const RangeTable& low, int32_t r_low, const int32_t* r_low_h, int64_t Nq,
+                   int64_t N_cur) {
   Layout L;
   const int64_t W = (int64_t)s->H * s->d;
   size_t off = 0;
@@ -35,7 +36,7 @@ Layout make_layout(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTabl
     L.lse_full = take(sizeof(float) * Nq * s->H);
     L.o_low = take(sizeof(float) * Nq * W);
     L.lse_low = take(sizeof(float) * Nq * s->H);
-    L.low = take(low_workspace_bytes(s, A_k, A_v, low, r_low, Nq));
+    L.low = take(low_workspace_bytes(s, A_k, A_v, low, r_low, r_low_h, Nq));
   }
   L.total = off;
   return L;
@@ -44,8 +45,9 @@ Layout make_layout(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTabl
 }  // namespace
 
 size_t tuned_attend_workspace(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& full,
-                              const RangeTable& low, int32_t r_low, int64_t Nq, int64_t N_cur) {
-  return make_layout(s, A_k, A_v, full, low, r_low, Nq, N_cur).total;
+                              const RangeTable& low, int32_t r_low, const int32_t* r_low_h,
+                              int64_t Nq, int64_t N_cur) {
+  return make_layout(s, A_k, A_v, full, low, r_low, r_low_h, Nq, N_cur).total;
 }
 
 nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchArgs& vb,
@@ -53,7 +55,7 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
                         const int32_t* r_low_h, float tau, const void* q, int64_t Nq,
                         const void* cur_k, const void* cur_v, int64_t N_cur, void* out,
                         float* lse, char* ws, size_t ws_bytes, hipStream_t st) {
-  const Layout L = make_layout(s, kb.A, vb.A, full, low, r_low, Nq, N_cur);
+  const Layout L = make_layout(s, kb.A, vb.A, full, low, r_low, r_low_h, Nq, N_cur);
   const int H = s->H, W = H * s->d;
   uint16_t* kall = reinterpret_cast<uint16_t*>(ws + L.kall);
   uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
@@ -99,9 +101,10 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
     }
     groups[g].h[groups[g].n++] = h;
   }
+  const int64_t units = low_part_units(Nq, H, r_low, r_low_h, low.total);
   for (int g = 0; g < ng; ++g)
     if ((e = launch_low(s, kb, vb, mp, low, widths[g], tau, qb, Nq, ol, ll, ws + L.low, r_low,
-                        groups[g], g == 0, st)))
+                        units, groups[g], g == 0, st)))
       return e;
   ProfScope ps("merge", st);
   return launch_lse_merge(Nq, H, s->d, of, lf, ol, ll, out, NKV_BF16, lse, st);

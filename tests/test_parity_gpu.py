@@ -291,6 +291,36 @@ def test_analytical_maps_equal_heads_call():
     assert np.array_equal(out_h, out_m) and np.array_equal(lse_h, lse_m)
 
 
+def test_low_read_with_few_tokens_ignores_stale_workspace():
+    """A handful of low-routed tokens touch few of the 16 V-center ranges;
+    the rest of the center masses must be written as zeros, not read from
+    whatever the workspace held (here: NaN bytes)."""
+    cfg = S("C3", H=2, r=128, A=1024, n_hist=600, Nq=100, N_cur=30, chunk=600, r_low=64,
+            n_full_tail=590, seed=41)
+    case = get_case(cfg)
+    shape = shape_of(cfg)
+    kb, vb = device_branch(case, 0), device_branch(case, 1)
+    q = to_dev(case.w.queries(), cfg.dtype)
+    ck, cv = to_dev(case.w.current(0), cfg.dtype), to_dev(case.w.current(1), cfg.dtype)
+    route = cfg.segments()
+    for widths in (64, [64, 32]):
+        if isinstance(widths, int):
+            n = lib.nkv_attend_workspace_size(shape, cfg.A, cfg.A, cfg.n_attend, route, widths,
+                                              cfg.Nq, cfg.N_cur)
+        else:
+            n = lib.nkv_attend_heads_workspace_size(shape, cfg.A, cfg.A, cfg.n_attend, route,
+                                                    widths, cfg.Nq, cfg.N_cur)
+        ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+        log(f"few low tokens: route={route} widths={widths}")
+        out, lse = lib.attend_fast(shape, kb, vb, cfg.n_attend, route, widths, q, ck, cv, ws=ws)
+        torch.cuda.synchronize()
+        rows = q_rows(cfg, None)
+        ro, rl = _oracle_attend(case, rows, True, route, widths)
+        rel, lerr = attention_errors(from_dev(out), from_dev(lse), ro, rl)
+        log(f"  rel={rel:.3e} dLSE={lerr:.3e}")
+        assert rel <= OUT_TOL and lerr <= LSE_TOL
+
+
 def test_attend_full_C1():
     _check_attend("C1", sample=48)
 
