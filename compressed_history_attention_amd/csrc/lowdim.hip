@@ -652,6 +652,10 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   auto flush = [&](int gv) __attribute__((always_inline)) {
     if (zgv < gv) zero_mass(zgv, gv);
     put_mass(gv);
+    // the softmax denominator is the sum of the center masses: every key's
+    // p lands in exactly one center (padding keys have p = 0)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lsum += accW[0][e] + accW[1][e];
     zgv = gv + 1;
     accW[0] = zero16();
     accW[1] = zero16();
@@ -766,10 +770,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
         const int g = 2 * hb + g2;
         float pv[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          pv[u] = __builtin_amdgcn_exp2f(acc[4 * g + u]);
-          lsum += pv[u];
-        }
+        for (int u = 0; u < 4; ++u) pv[u] = __builtin_amdgcn_exp2f(acc[4 * g + u]);
         pk[2 * g2] = pack_bf16x2(pv[0], pv[1]);
         pk[2 * g2 + 1] = pack_bf16x2(pv[2], pv[3]);
       }
