@@ -386,44 +386,98 @@ struct QtProblem {
   }
 };
 
-// max over centers present in the low set of q_h . mu^K_{a,h}
-// (rows = centers, cols = queries)
-struct TmaxProblem {
-  static constexpr int BK = 64;
-  int M, N, K;  // A_k, Nq, 128
-  int H;
-  const uint16_t* muk;
-  const uint16_t* q;
-  const uint32_t* present;
-  uint32_t* tmax;  // [Nq*H] ordered bits
-  HeadSet hs;      // batch z serves head hs.h[z]
-  __device__ u32x4 load_a(int z, int m, int k) const {
-    if (m >= M) return u32x4{0u, 0u, 0u, 0u};
-    return ld_u32x4(muk + (int64_t)m * H * 128 + hs.h[z] * 128 + k);
-  }
-  __device__ u32x4 load_b(int z, int n, int k) const {
-    if (n >= N) return u32x4{0u, 0u, 0u, 0u};
-    return ld_u32x4(q + (int64_t)n * H * 128 + hs.h[z] * 128 + k);
-  }
-  __device__ void epilogue(int zb, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
-    const int z = hs.h[zb];
+// 16-byte block j of row r of 256-byte rows stored with block j of row r at
+// block j ^ (r & 15) (conflict-free when 32 lanes read one block of 32 rows)
+__device__ __forceinline__ u32x4 lds_row_block(const char* lds, int r, int j) {
+  return *reinterpret_cast<const u32x4*>(lds + r * 256 + ((j ^ (r & 15)) << 4));
+}
+
+// max over centers present in the low set of q_h . mu^K_{a,h}, per row of
+// the heads in hs.  One block = 128 queries of one head: 4 waves of 32
+// queries keep their q fragments in registers while the head's center rows
+// stream through LDS 64 at a time (double buffered, rows swizzled so that the
+// MFMA operand reads are conflict-free); each lane folds its centers into a
+// running max and one store per row replaces the atomics of a GEMM epilogue.
+// Products are exact (bf16), sums fp32 in k order: the same values as a
+// GEMM over k.
+constexpr int CM_Q = 128, CM_C = 64;
+__global__ __launch_bounds__(256) void k_center_max(const uint16_t* __restrict__ q,
+                                                    const uint16_t* __restrict__ muk,
+                                                    const uint32_t* __restrict__ present,
+                                                    int64_t Nq, int H, int A_k, HeadSet hs,
+                                                    uint32_t* __restrict__ tmax) {
+  __shared__ __attribute__((aligned(1024))) char sMu0[CM_C * 256];
+  __shared__ __attribute__((aligned(1024))) char sMu1[CM_C * 256];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = hs.h[blockIdx.y];
+  const int64_t W = (int64_t)H * 128;
+  const int64_t qrow = (int64_t)blockIdx.x * CM_Q + wave * 32 + (lane & 31);
+  const bool rok = qrow < Nq;
+  bf16x8 qv[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float best = -INFINITY;
+  for (int ks = 0; ks < 8; ++ks)
+    qv[ks] = rok ? as_bf16x8(ld_u32x4(q + qrow * W + h * 128 + 16 * ks + 8 * hl))
+                 : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  // 64 center rows (16 KiB): 16 direct-to-LDS loads of 1 KiB, 4 per wave;
+  // row r's 16-byte block j lands at block j ^ (r & 15)
+  auto load = [&](int blk, char* dst) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int k = 0; k < CM_C / 16; ++k) {
+      const int c = wave + 4 * k;
+      const int r = 4 * c + (lane >> 4), jp = lane & 15;
+      const int j = jp ^ (r & 15);
+      const int cen = min(blk * CM_C + r, A_k - 1);  // rows past A_k are masked below
+      __builtin_amdgcn_global_load_lds(muk + (int64_t)cen * W + h * 128 + j * 8,
+                                       (__attribute__((address_space(3))) void*)(dst + c * 1024),
+                                       16, 0, 0);
+    }
+  };
+  float best = -INFINITY;
+  const int nblk = (A_k + CM_C - 1) / CM_C;
+  auto block = [&](int blk, const char* cur) __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + 32 * i + acc_row(e, lane);
-          if (m < M && present[m]) best = fmaxf(best, acc[i][j][e]);
+    for (int cb = 0; cb < 2; ++cb) {
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        acc = mfma_bf16(as_bf16x8(lds_row_block(cur, cb * 32 + (lane & 31), 2 * ks + hl)),
+                        qv[ks], acc);
+      const int c0 = blk * CM_C + cb * 32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cg = c0 + g * 8 + hl * 4;  // the 4 consecutive centers of elements 4g..4g+3
+        u32x4 pr;
+        if (cg + 4 <= A_k) {
+          pr = *reinterpret_cast<const u32x4*>(present + cg);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) pr[u] = cg + u < A_k ? present[cg + u] : 0u;
         }
-      best = fmaxf(best, __shfl_xor(best, 32, 64));
-      const int n = n0 + 32 * j + (lane & 31);
-      if (lane < 32 && n < N && best > -INFINITY)
-        atomicMax(tmax + (int64_t)n * H + z, ordered_bits(best));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (pr[u]) best = fmaxf(best, acc[4 * g + u]);
+      }
+    }
+  };
+  load(0, sMu0);
+  for (int blk = 0; blk < nblk; blk += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (blk + 1 < nblk) load(blk + 1, sMu1);
+    block(blk, sMu0);
+    if (blk + 1 < nblk) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (blk + 2 < nblk) load(blk + 2, sMu0);
+      block(blk + 1, sMu1);
     }
   }
-};
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  best = fmaxf(best, __shfl_xor(best, 32, 64));
+  // the encoding of "no present center" is the cleared value 0
+  if (lane < 32 && rok) tmax[qrow * H + h] = best > -INFINITY ? ordered_bits(best) : 0u;
+}
 
 // per-row bound, fp16 c q~, and the list of rows needing the exact fallback;
 // 16 lanes per row
@@ -533,9 +587,6 @@ __device__ __forceinline__ void load_rows_swizzled(const uint16_t* __restrict__ 
   }
 }
 
-__device__ __forceinline__ u32x4 lds_row_block(const char* lds, int r, int j) {
-  return *reinterpret_cast<const u32x4*>(lds + r * 256 + ((j ^ (r & 15)) << 4));
-}
 
 // ---------------------------------------------------------------------------
 // Main kernel.  One block = 256 query rows of one head; wave w owns rows
@@ -1077,9 +1128,10 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   // query reduction and per-row score bounds
   QtProblem qp{(int)Nq, r_low, 128, H, q, dkt, qt32, hs};
   if ((e = launch_gemm(qp, hs.n, st))) return e;
-  TmaxProblem tp{kb.A, (int)Nq, 128, H, static_cast<const uint16_t*>(kb.centers), q, present, tmax,
-                 hs};
-  if ((e = launch_gemm(tp, hs.n, st))) return e;
+  hipLaunchKernelGGL(k_center_max, dim3((unsigned)ceil_div(Nq, CM_Q), (unsigned)hs.n), dim3(256),
+                     0, st, q, static_cast<const uint16_t*>(kb.centers), present, Nq, H, kb.A, hs,
+                     tmax);
+  NKV_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_row_bound, dim3((unsigned)ceil_div(Nq * hs.n * 16, 256)), dim3(256), 0, st,
                      qt32, Nq, H, hs, r_low, rlp, c, tmax, misc, bound, qt16, flags,
                      reinterpret_cast<int32_t*>(misc + 1));
