@@ -355,10 +355,182 @@ struct DecodeTProblem {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Decoder with the codes stationary: one block dequantises the INT4 codes of
+// 64 tokens once into LDS (bf16, rows padded against bank conflicts) and
+// sweeps every output channel against them, 128 channels per step; wave w
+// owns channels 32w..32w+31 of each step and streams its decoder rows from
+// L2 into registers eight k-steps ahead (a GEMM tiled over channels would
+// dequantise every token once per channel tile).  C[tok][ch] = codes . D^T
+// plus the token's center (requested before the step's MFMAs) is rounded to
+// bf16 into an LDS tile -- [tok][ch] for K rows, [ch][tok] for the per-head
+// transposed V -- and leaves the block as 16-byte row chunks.
+// ---------------------------------------------------------------------------
+constexpr int DS_TOK = 64, DS_CH = 128;
+
+template <bool ROWS>
+__global__ __launch_bounds__(256) void k_decode_stationary(BranchArgs b, RangeTable rows, int W,
+                                                           int r, int group,
+                                                           uint16_t* __restrict__ out,
+                                                           int64_t ld) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  const int rs = r + 8;                                    // bf16 row stride of the codes
+  uint16_t* sA = reinterpret_cast<uint16_t*>(dsm);         // [64][r + 8]
+  // output tile: K [64][128 + 8], V [128][64 + 8] (bf16)
+  uint16_t* sO = reinterpret_cast<uint16_t*>(dsm + DS_TOK * rs * 2);
+  constexpr int OS = ROWS ? DS_CH + 8 : DS_TOK + 8;
+  __shared__ int64_t sTok[DS_TOK];
+  __shared__ int32_t sIdx[DS_TOK];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t m0 = (int64_t)blockIdx.x * DS_TOK;
+  const int nvalid = (int)min<int64_t>(DS_TOK, rows.total - m0);
+  const uint16_t* D = static_cast<const uint16_t*>(b.decoder);
+  const uint16_t* mu = static_cast<const uint16_t*>(b.centers);
+  if (tid < DS_TOK) {
+    const int64_t t = tid < nvalid ? map_index(rows, m0 + tid) : -1;
+    sTok[tid] = t;
+    sIdx[tid] = t >= 0 ? b.idx[t] : 0;
+  }
+  __syncthreads();
+  // dequantise: 8 coefficients per item
+  const int kc_per_tok = r / 8;
+  for (int c = tid; c < DS_TOK * kc_per_tok; c += 256) {
+    const int tl = c / kc_per_tok, k = (c - tl * kc_per_tok) * 8;
+    const int64_t t = sTok[tl];
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (t >= 0) {
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(b.codes + t * (r / 2) + k / 2);
+      const float sc = fp16_bits_to_f32(b.scales[t * (r / group) + k / group]);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int n0 = (cw >> (8 * h)) & 15, n1 = (cw >> (8 * h + 4)) & 15;
+        v[h] = pack_bf16x2((float)(n0 - ((n0 & 8) << 1)) * sc, (float)(n1 - ((n1 & 8) << 1)) * sc);
+      }
+    }
+    *reinterpret_cast<u32x4*>(sA + tl * rs + k) = v;
+  }
+  __syncthreads();
+  const int nks = r / 16;
+  auto afrag = [&](int i, int ks) __attribute__((always_inline)) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(sA + (32 * i + (lane & 31)) * rs + 16 * ks +
+                                                     8 * hl));
+  };
+  // this block's share of the sweep (grid y splits the channel steps when
+  // there are few token blocks)
+  const int nsteps = W / DS_CH, per = (nsteps + gridDim.y - 1) / gridDim.y;
+  const int n_beg = blockIdx.y * per * DS_CH, n_end = min(nsteps, (int)(blockIdx.y + 1) * per) * DS_CH;
+  // decoder fragments of k-steps ks0..ks0+7 for the rows of sweep step n0
+  constexpr int PF = 8;
+  auto ldd = [&](int n0, int ks0, u32x4 (&d)[PF]) __attribute__((always_inline)) {
+    const uint16_t* drow = D + (int64_t)(n0 + wave * 32 + (lane & 31)) * r + 8 * hl;
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      d[u] = (ks0 + u < nks && n0 < n_end) ? ld_u32x4(drow + 16 * (ks0 + u)) : u32x4{0u, 0u, 0u, 0u};
+  };
+  u32x4 d0[PF], d1[PF];
+  ldd(n_beg, 0, d0);
+  for (int n0 = n_beg; n0 < n_end; n0 += DS_CH) {
+    const int chl = wave * 32 + (lane & 31);               // lane's channel within the step
+    // the centers of the lane's 32 elements, requested before the MFMAs
+    uint32_t mk[32];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        mk[16 * i + e] = mu[(int64_t)sIdx[32 * i + acc_row(e, lane)] * W + n0 + chl];
+    f32x16 acc[2] = {zero16(), zero16()};
+    auto mm = [&](int ks0, const u32x4 (&d)[PF]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        if (ks0 + u >= nks) break;
+        const bf16x8 dv = as_bf16x8(d[u]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i] = mfma_bf16(afrag(i, ks0 + u), dv, acc[i]);
+      }
+    };
+    // d0 holds k-steps 0..PF-1 of this step on entry; the last group's
+    // buffer is refilled with the next step's first k-steps
+    for (int ks0 = 0; ks0 < nks; ks0 += 2 * PF) {
+      if (ks0 + PF < nks) ldd(n0, ks0 + PF, d1);
+      else ldd(n0 + DS_CH, 0, d1);
+      mm(ks0, d0);
+      if (ks0 + 2 * PF < nks) ldd(n0, ks0 + 2 * PF, d0);
+      else if (ks0 + PF < nks) ldd(n0 + DS_CH, 0, d0);
+      if (ks0 + PF < nks) mm(ks0 + PF, d1);
+    }
+    if (((nks + PF - 1) / PF) % 2 == 1) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) d0[u] = d1[u];
+    }
+    __syncthreads();  // the previous step's reads of sO are done
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tl = 32 * i + acc_row(e, lane);
+        const uint16_t v = f32_to_bf16_bits(acc[i][e] + bf16_bits_to_f32(uint16_t(mk[16 * i + e])));
+        if constexpr (ROWS) sO[tl * OS + chl] = v;
+        else sO[chl * OS + tl] = v;
+      }
+    __syncthreads();
+    if constexpr (ROWS) {
+      // 64 token rows x 16 chunks of 8 channels
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = tid + 256 * u, tl = c >> 4, cc = c & 15;
+        if (tl < nvalid)
+          *reinterpret_cast<u32x4*>(out + (m0 + tl) * W + n0 + cc * 8) =
+              *reinterpret_cast<const u32x4*>(sO + tl * OS + cc * 8);
+      }
+    } else {
+      // 128 channel rows x 8 chunks of 8 tokens (ld % 8 == 0: aligned chunks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = tid + 256 * u, cl = c >> 3, tc = (c & 7) * 8;
+        uint16_t* dst = out + (int64_t)(n0 + cl) * ld + m0 + tc;
+        const uint16_t* src = sO + cl * OS + tc;
+        if (tc + 8 <= nvalid) {
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          for (int k = 0; k < 8 && tc + k < nvalid; ++k) dst[k] = src[k];
+        }
+      }
+    }
+  }
+}
+
+size_t decode_stationary_lds(int r) {
+  const size_t o = std::max<size_t>((size_t)DS_TOK * (DS_CH + 8), (size_t)DS_CH * (DS_TOK + 8));
+  return (size_t)DS_TOK * (r + 8) * 2 + o * 2;
+}
+
 nkv_status launch_decode_tuned(const BranchArgs& b, int W, int r, int group,
                                const RangeTable& rows, uint16_t* out, int64_t ld, bool transposed,
                                hipStream_t st) {
   if (rows.total == 0) return NKV_OK;
+  if (r <= 512 && W % DS_CH == 0 && (transposed ? ld % 8 == 0 : true)) {
+    const size_t lds = decode_stationary_lds(r);
+    // about four blocks per CU: split the channel sweep when tokens are few
+    const int64_t tb = ceil_div(rows.total, DS_TOK);
+    const int ysplit = (int)std::min<int64_t>(W / DS_CH, std::max<int64_t>(1, 1024 / tb));
+    const dim3 grid((unsigned)tb, (unsigned)ysplit);
+    if (transposed) {
+      if (lds > 64 * 1024)
+        NKV_HIP_CHECK(hipFuncSetAttribute((const void*)k_decode_stationary<false>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+      hipLaunchKernelGGL(k_decode_stationary<false>, grid, dim3(256), lds, st, b, rows, W, r,
+                         group, out, ld);
+    } else {
+      if (lds > 64 * 1024)
+        NKV_HIP_CHECK(hipFuncSetAttribute((const void*)k_decode_stationary<true>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+      hipLaunchKernelGGL(k_decode_stationary<true>, grid, dim3(256), lds, st, b, rows, W, r,
+                         group, out, ld);
+    }
+    NKV_LAUNCH_CHECK();
+    return NKV_OK;
+  }
   if (transposed) {
     DecodeTProblem p{W, (int)rows.total, r, group, b, rows, out, ld};
     return launch_gemm(p, 1, st);
