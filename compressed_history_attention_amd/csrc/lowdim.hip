@@ -119,8 +119,10 @@ Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& l
   P.img = take((size_t)P.max_tiles * P.g.bytes);
   // partial sums of the main pass: (split, query, head of the group) rows
   const int64_t prows = Nq * part_units;
-  P.acc = take(sizeof(float) * prows * r_low);
-  P.wmass = take(sizeof(float) * prows * A_v);
+  // fp32 partials, or (one split) bf16 hi/lo planes of the same byte size:
+  // acc rows of 2 x ra, mass rows of 2 x GV * 64 bf16
+  P.acc = take(sizeof(float) * prows * P.ra);
+  P.wmass = take(sizeof(float) * prows * P.GV * CR);
   P.ell = take(sizeof(float) * prows);
   P.total = off;
   return P;
@@ -539,7 +541,7 @@ struct MainArgs {
   float* wmass;
   float* ell;
   int64_t Nq;
-  int H, A_k, A_v, GK, GV, NB, r_low;
+  int H, A_k, A_v, GK, GV, NB, r_low, ra;
   float c;
   HeadSet hs;  // grid row y serves head hs.h[y]; grid z = key-range split
 };
@@ -668,8 +670,32 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   };
 
   // masses of the a^V range gv from the accumulators
+  // With one split the restoration reads the partials as bf16 hi/lo planes
+  // (x = hi + lo to ~16 significant bits), written here once instead of being
+  // split again for every use; rows [hi | lo] of 2 x GV * 64 (masses) and
+  // 2 x ra (coefficient sums) bf16.
+  const bool planes = nsplit == 1;
+  const int WS = a.GV * CR;
+  auto put_hilo = [&](uint16_t* hi, uint16_t* lo, f32x4 v) __attribute__((always_inline)) {
+    float l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) l[u] = v[u] - (float)(__bf16)v[u];
+    *reinterpret_cast<uint2*>(hi) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<uint2*>(lo) = uint2{pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3])};
+  };
   auto put_mass = [&](int gv) __attribute__((always_inline)) {
-    if (rok) {
+    if (rok && planes) {
+      uint16_t* row = reinterpret_cast<uint16_t*>(a.wmass) + prow * 2 * WS + gv * CR;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int c = cb * 32 + e4 * 8 + hl * 4;
+          put_hilo(row + c, row + WS + c,
+                   f32x4{accW[cb][4 * e4], accW[cb][4 * e4 + 1], accW[cb][4 * e4 + 2],
+                         accW[cb][4 * e4 + 3]});
+        }
+    } else if (rok) {
       float* dst = a.wmass + prow * a.A_v + gv * CR;
       const int lim = a.A_v - gv * CR;
 #pragma unroll
@@ -693,6 +719,15 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   // restoration reads every range)
   auto zero_mass = [&](int g0, int g1) __attribute__((always_inline)) {
     if (!rok) return;
+    if (planes) {
+      uint16_t* row = reinterpret_cast<uint16_t*>(a.wmass) + prow * 2 * WS;
+      for (int gv = g0; gv < g1; ++gv)
+        for (int c = hl * 4; c < CR; c += 8) {
+          *reinterpret_cast<uint2*>(row + gv * CR + c) = uint2{0u, 0u};
+          *reinterpret_cast<uint2*>(row + WS + gv * CR + c) = uint2{0u, 0u};
+        }
+      return;
+    }
     for (int gv = g0; gv < g1; ++gv) {
       float* dst = a.wmass + prow * a.A_v + gv * CR;
       const int lim = min(CR, a.A_v - gv * CR);
@@ -898,10 +933,16 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int dim = db * 32 + e4 * 8 + hl * 4;  // r_low % 16 == 0: whole f32x4 or none
-        if (dim < a.r_low)
-          *reinterpret_cast<f32x4*>(a.acc + prow * a.r_low + dim) =
-              f32x4{accT[db][4 * e4], accT[db][4 * e4 + 1], accT[db][4 * e4 + 2],
-                    accT[db][4 * e4 + 3]};
+        const f32x4 v{accT[db][4 * e4], accT[db][4 * e4 + 1], accT[db][4 * e4 + 2],
+                      accT[db][4 * e4 + 3]};
+        if (dim < a.r_low) {
+          if (planes) {
+            uint16_t* row = reinterpret_cast<uint16_t*>(a.acc) + prow * 2 * a.ra;
+            put_hilo(row + dim, row + a.ra + dim, v);
+          } else {
+            *reinterpret_cast<f32x4*>(a.acc + prow * a.r_low + dim) = v;
+          }
+        }
       }
     if (hl == 0) a.ell[prow] = lsum;
   }
@@ -924,6 +965,7 @@ struct RestoreProblem {
   int M, N, K;  // Nq, 128, 2 ra + 2 av
   int H, ldv, r_low, ra, A_v, av;
   int nsplit;   // key-range splits of the main pass: their partial sums add
+  int WS;       // one split: bf16 hi/lo planes, mass rows [hi | lo] of 2 x WS
   const float* acc;    // partials [nsplit][Nq][hs.n][r_low]
   const float* wmass;  // partials [nsplit][Nq][hs.n][A_v]
   const uint16_t* dv;    // restoration map [W, ldv]
@@ -939,6 +981,17 @@ struct RestoreProblem {
   }
   __device__ u32x4 load_a(int zb, int m, int k) const {
     if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
+    if (nsplit == 1) {
+      const int64_t pr = prow(0, m, zb);
+      if (k < 2 * ra) {
+        const int j = k >= ra ? k - ra : k;
+        if (j >= r_low) return u32x4{0u, 0u, 0u, 0u};
+        return ld_u32x4(reinterpret_cast<const uint16_t*>(acc) + pr * 2 * ra + k);
+      }
+      const int kk = k - 2 * ra;
+      const int c = kk >= av ? kk - av + WS : kk;
+      return ld_u32x4(reinterpret_cast<const uint16_t*>(wmass) + pr * 2 * WS + c);
+    }
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.f;
@@ -1141,7 +1194,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   {
   ProfScope ps_main("low_main", st);
   MainArgs m{q, static_cast<const uint16_t*>(kb.centers), qt16, bound, img, tile_start,
-             tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.GV, P.NB, r_low, c, hs};
+             tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.GV, P.NB, r_low, ra, c, hs};
   switch (rlp) {
     case 16: e = launch_main<16>(m, Nq, nsplit, st); break;
     case 32: e = launch_main<32>(m, Nq, nsplit, st); break;
@@ -1158,7 +1211,8 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   // restoration
   {
   ProfScope ps_restore("low_restore", st);
-  RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, mp.ld, r_low, ra, vb.A, P.av, nsplit, acc, wmass,
+  RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, mp.ld, r_low, ra, vb.A, P.av, nsplit,
+                    P.GV * CR, acc, wmass,
                     static_cast<const uint16_t*>(mp.omap), mvt, ell, bound, o_low, lse_low, hs};
   if ((e = launch_gemm(rp, hs.n, st))) return e;
   }
