@@ -147,6 +147,144 @@ struct ProjProblem {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Projection with the residual computed once: z = E (x - mu_a) for 64 tokens
+// and every one of the r outputs per block, over one share of the channels
+// (grid y; partial sums per share, added in a fixed order by the quantiser).
+// Per 32-channel chunk the block forms the residual e = x - mu_a (exact in
+// fp32 for bf16 inputs), splits it into three bf16 terms hi + mid + lo = e
+// and stores them in LDS; each wave (32 tokens x r/QW outputs, 2 QW waves)
+// multiplies the three terms by the same encoder fragments, read from L2
+// one chunk ahead.  Exact products and fp32 sums reproduce an fp32
+// projection.
+// ---------------------------------------------------------------------------
+constexpr int PS_TOK = 64, PS_KC = 32, PS_SHARE = 768;
+constexpr int PS_AS = PS_KC + 8;  // bf16 row stride of a residual term tile
+
+template <int NT, int QW>  // r = 64 NT outputs in QW groups; 2 QW waves
+__global__ __launch_bounds__(128 * QW) void k_project_stationary(const uint16_t* __restrict__ x,
+                                                            int64_t N, int W,
+                                                            const uint16_t* __restrict__ mu,
+                                                            const int32_t* __restrict__ idx,
+                                                            const uint16_t* __restrict__ enc,
+                                                            float* __restrict__ z) {
+  constexpr int R = 64 * NT, TW = 2 * NT / QW;  // 32-output tiles per wave
+  static_assert(2 * NT % QW == 0, "output groups");
+  // [stage][term][64 tokens][32 + 8]
+  __shared__ __attribute__((aligned(16))) uint16_t sE[2][3][PS_TOK * PS_AS];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = (int64_t)blockIdx.x * PS_TOK;
+  const int w_beg = blockIdx.y * PS_SHARE, w_end = min(W, w_beg + PS_SHARE);
+  const int nchunk = (w_end - w_beg) / PS_KC;
+  // residual loads (threads 0..255): thread -> (token tid / 4, channels
+  // 8 (tid % 4) .. + 7)
+  const bool stager = tid < 256;
+  const int rt = (tid & 255) >> 2, rc = (tid & 3) * 8;
+  const int64_t rtok = t0 + rt;
+  const bool rok = stager && rtok < N;
+  const uint16_t* xrow = x + (rok ? rtok : 0) * W;
+  const uint16_t* mrow = mu + (int64_t)(rok ? idx[rtok] : 0) * W;
+  auto ld_res = [&](int c, u32x4& xv, u32x4& mv) __attribute__((always_inline)) {
+    const int w = w_beg + c * PS_KC + rc;
+    xv = rok ? ld_u32x4(xrow + w) : u32x4{0u, 0u, 0u, 0u};
+    mv = rok ? ld_u32x4(mrow + w) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto put_res = [&](int stage, const u32x4& xv, const u32x4& mv) __attribute__((always_inline)) {
+    if (!stager) return;
+    u32x4 th, tm, tl;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float hi2[2], mid2[2], lo2[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const float e = bf16_bits_to_f32(uint16_t(xv[h] >> (16 * s2))) -
+                        bf16_bits_to_f32(uint16_t(mv[h] >> (16 * s2)));
+        const float hi = bf16_bits_to_f32(f32_to_bf16_bits(e));
+        const float r1 = e - hi;
+        const float mid = bf16_bits_to_f32(f32_to_bf16_bits(r1));
+        hi2[s2] = hi;
+        mid2[s2] = mid;
+        lo2[s2] = r1 - mid;
+      }
+      th[h] = pack_bf16x2(hi2[0], hi2[1]);
+      tm[h] = pack_bf16x2(mid2[0], mid2[1]);
+      tl[h] = pack_bf16x2(lo2[0], lo2[1]);
+    }
+    *reinterpret_cast<u32x4*>(&sE[stage][0][rt * PS_AS + rc]) = th;
+    *reinterpret_cast<u32x4*>(&sE[stage][1][rt * PS_AS + rc]) = tm;
+    *reinterpret_cast<u32x4*>(&sE[stage][2][rt * PS_AS + rc]) = tl;
+  };
+  // wave tile: tokens 32 (wave & 1) .., outputs (wave >> 1) R/QW ..
+  const int tw = (wave & 1) * 32, ow = (wave >> 1) * (R / QW);
+  // encoder fragments of one chunk: TW tiles x 2 k-steps
+  auto ld_enc = [&](int c, u32x4 (&b)[TW][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < TW; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        b[j][ks] = c < nchunk ? ld_u32x4(enc + (int64_t)(ow + 32 * j + (lane & 31)) * W + w_beg +
+                                         c * PS_KC + 16 * ks + 8 * hl)
+                              : u32x4{0u, 0u, 0u, 0u};
+  };
+  f32x16 acc[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) acc[j] = zero16();
+  // Inputs are requested two chunks ahead: the residual rows (from HBM) in
+  // two register sets, the encoder fragments (from L2) in three buffers.
+  // Chunk k uses residual set k % 2, LDS stage k % 2 and buffer k % 3.
+  u32x4 xv[2], mv[2];
+  u32x4 bb[3][TW][2];
+  ld_res(0, xv[0], mv[0]);
+  if (nchunk > 1) ld_res(1, xv[1], mv[1]);
+  ld_enc(0, bb[0]);
+  ld_enc(1, bb[1]);
+  put_res(0, xv[0], mv[0]);
+  __syncthreads();
+  auto step = [&](int c, auto RS, auto BS) __attribute__((always_inline)) {
+    constexpr int rs = decltype(RS)::value, bs = decltype(BS)::value;
+    if (c + 2 < nchunk) ld_res(c + 2, xv[rs], mv[rs]);
+    ld_enc(c + 2, bb[(bs + 2) % 3]);
+#pragma unroll
+    for (int term = 0; term < 3; ++term)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            &sE[rs][term][(tw + (lane & 31)) * PS_AS + 16 * ks + 8 * hl]));
+#pragma unroll
+        for (int j = 0; j < TW; ++j) acc[j] = mfma_bf16(a, as_bf16x8(bb[bs][j][ks]), acc[j]);
+      }
+    if (c + 1 < nchunk) put_res(rs ^ 1, xv[rs ^ 1], mv[rs ^ 1]);
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  for (int c = 0; c < nchunk; c += 6) {
+    step(c, I0{}, I0{});
+    if (c + 1 < nchunk) step(c + 1, I1{}, I1{});
+    if (c + 2 < nchunk) step(c + 2, I0{}, I2{});
+    if (c + 3 < nchunk) step(c + 3, I1{}, I0{});
+    if (c + 4 < nchunk) step(c + 4, I0{}, I1{});
+    if (c + 5 < nchunk) step(c + 5, I1{}, I2{});
+  }
+  float* zp = z + (int64_t)blockIdx.y * N * R;
+#pragma unroll
+  for (int j = 0; j < TW; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t t = t0 + tw + acc_row(e, lane);
+      if (t < N) zp[t * R + ow + 32 * j + (lane & 31)] = acc[j][e];
+    }
+}
+
+// the stationary projection serves r = 64 NT (NT in 1..4, 6) and W % 32 == 0;
+// its channel shares are fixed per W, so results do not depend on N
+inline bool proj_stationary(int W, int r) {
+  return r % 64 == 0 && r <= 384 && r != 320 && W % PS_KC == 0;
+}
+inline int proj_shares(int W) { return (W + PS_SHARE - 1) / PS_SHARE; }
+
 // split-K factor of the projection (fixed per width, so results are
 // deterministic): the three residual terms, each possibly halved
 inline int proj_splits(int W) {
@@ -209,8 +347,10 @@ nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void
 }
 
 size_t tuned_encode_workspace(const nkv_shape* s, int64_t N, int32_t A) {
+  const int W = s->H * s->d;
+  const int parts = proj_stationary(W, s->r) ? proj_shares(W) : proj_splits(W);
   size_t off = tuned_assign_workspace(N, A);
-  off = align_up(off + sizeof(float) * N * s->r * proj_splits(s->H * s->d), 256);
+  off = align_up(off + sizeof(float) * N * s->r * parts, 256);
   return off;
 }
 
@@ -222,15 +362,29 @@ nkv_status tuned_encode(const nkv_shape* s, const void* x, int64_t N, const void
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* mub = static_cast<const uint16_t*>(centers);
   nkv_status e;
-  const int splits = proj_splits(W);
+  const bool stat = proj_stationary(W, r);
+  const int splits = stat ? proj_shares(W) : proj_splits(W);
   {
   ProfScope ps("encode_assign", st);
   if ((e = tuned_assign(s, x, N, centers, A, idx, ws, st))) return e;
   }
   {
   ProfScope ps("encode_project", st);
-  ProjProblem pp{(int)N, r, 3 * W / splits, W, xb, mub, idx, static_cast<const uint16_t*>(enc), z};
-  if ((e = launch_gemm(pp, splits, st))) return e;
+  const uint16_t* eb = static_cast<const uint16_t*>(enc);
+  if (stat) {
+    const dim3 grid((unsigned)ceil_div(N, PS_TOK), (unsigned)splits);
+    switch (r / 64) {
+      case 1: hipLaunchKernelGGL((k_project_stationary<1, 2>), grid, dim3(256), 0, st, xb, N, W, mub, idx, eb, z); break;
+      case 2: hipLaunchKernelGGL((k_project_stationary<2, 2>), grid, dim3(256), 0, st, xb, N, W, mub, idx, eb, z); break;
+      case 3: hipLaunchKernelGGL((k_project_stationary<3, 2>), grid, dim3(256), 0, st, xb, N, W, mub, idx, eb, z); break;
+      case 4: hipLaunchKernelGGL((k_project_stationary<4, 4>), grid, dim3(512), 0, st, xb, N, W, mub, idx, eb, z); break;
+      default: hipLaunchKernelGGL((k_project_stationary<6, 4>), grid, dim3(512), 0, st, xb, N, W, mub, idx, eb, z); break;
+    }
+    NKV_LAUNCH_CHECK();
+  } else {
+    ProjProblem pp{(int)N, r, 3 * W / splits, W, xb, mub, idx, eb, z};
+    if ((e = launch_gemm(pp, splits, st))) return e;
+  }
   }
   ProfScope ps("encode_quantize", st);
   hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)ceil_div(N * r, 256)), dim3(256), 0, st, z,
