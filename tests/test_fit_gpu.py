@@ -82,6 +82,16 @@ def test_fit_generic_f32():
     _check(cfg, x, mu0, 2)
 
 
+def test_fit_tuned_ragged_counts():
+    # center count not a multiple of the 64-row LDS blocks, rows not a
+    # multiple of anything
+    cfg = synth.small_config("C3", H=4, r=128, A=100, n_hist=777, chunk=777)
+    w = synth.workload(cfg)
+    x, labels, _ = w.history_chunk(0, 0)
+    mu0 = _init_from_labels(x, labels, cfg.A, np.random.default_rng(4))
+    _check(cfg, x, mu0, 2)
+
+
 def test_fit_no_rows():
     cfg = synth.small_config("C3", H=4, r=128, A=64)
     shape = lib.Shape(cfg.H, cfg.d, cfg.r, cfg.group, cfg.dtype)

@@ -50,6 +50,12 @@ SMALL = {
             n_full_tail=200, seed=36),
     "S10": S("C3", H=4, r=128, A=90, n_hist=2000, Nq=260, N_cur=100, chunk=100, r_low=64,
              n_full_tail=400, seed=37),
+    # widths outside the stationary decode / projection kernels (r > 512,
+    # r = 320): their GEMM fallbacks
+    "S11": S("C3", H=5, r=544, A=16, n_hist=300, Nq=70, N_cur=20, chunk=300, mode="full",
+             n_full_tail=0, r_low=0, seed=42),
+    "S12": S("C3", H=3, r=320, A=40, n_hist=500, Nq=90, N_cur=33, chunk=250, r_low=64,
+             n_full_tail=120, seed=43),
     "C0f": S("C0", mode="fast", r_low=4, n_full_tail=32),
     "C0d": S("C0", mode="fast", r_low=4, n_full_tail=32, center_scale=0.05),
 }
@@ -84,7 +90,7 @@ def _encode_and_check(cfg, x, b, w):
     return rep, (idx, codes, scales)
 
 
-@pytest.mark.parametrize("name", ["C0", "S1", "S2", "C1"])
+@pytest.mark.parametrize("name", ["C0", "S1", "S2", "C1", "S11", "S12"])
 def test_encode_history_chunk(name):
     cfg = _cfg(name)
     w = synth.workload(cfg)
@@ -183,14 +189,14 @@ def _check_attend(name, sample=None, route=None, r_low=None, drule=None):
     return rel, lerr
 
 
-@pytest.mark.parametrize("name", ["C0", "S1"])
+@pytest.mark.parametrize("name", ["C0", "S1", "S11"])
 def test_attend_full_small(name):
     _check_attend(name)
 
 
 @pytest.mark.parametrize("name,drule", [("C0f", 0.5), ("C0d", 0.1), ("S2", 0.5), ("S3", 0.5),
                                         ("S2d", 0.1), ("S4", 0.5), ("S5", 0.5), ("S6", 0.5),
-                                        ("S7", 0.5), ("S8", 0.5)])
+                                        ("S7", 0.5), ("S8", 0.5), ("S12", 0.5)])
 def test_attend_fast_small(name, drule):
     _check_attend(name, drule=drule)
 
