@@ -13,6 +13,8 @@
 // through double-buffered LDS.  Per wave and tile: S^T = K Q^T is 2 x 8
 // MFMA 32x32x16 (lane = query column, 32 keys per lane), O^T += V^T P^T is
 // 4 x 4 MFMAs whose B operand is the wave's own P in registers.
+#include <cmath>
+
 #include "tuned_internal.hpp"
 
 namespace nkv {
@@ -30,6 +32,7 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][128 * FA_VS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
   const int h = blockIdx.y;
+  const int split = blockIdx.z, nsplit = gridDim.z;  // key-range split (partials merged later)
   const int W = H * 128;
   const int64_t q0 = (int64_t)blockIdx.x * FA_QB + wave * 32;
   const int64_t qrow = q0 + (lane & 31);
@@ -46,7 +49,8 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
   for (int i = 0; i < 4; ++i) o[i] = zero16();
   float m_run = -INFINITY, l_part = 0.f;
 
-  const int64_t ntiles = (Nk + FA_KT - 1) / FA_KT;
+  const int64_t ntiles_all = (Nk + FA_KT - 1) / FA_KT;
+  const int64_t t_beg = ntiles_all * split / nsplit, t_end = ntiles_all * (split + 1) / nsplit;
   u32x4 rk[4], rv[4];
   auto fetch = [&](int64_t t0) {
 #pragma unroll
@@ -70,14 +74,14 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
     }
   };
 
-  if (ntiles > 0) {
-    fetch(0);
+  if (t_beg < t_end) {
+    fetch(t_beg * FA_KT);
     stash(0);
   }
   __syncthreads();
-  for (int64_t tile = 0; tile < ntiles; ++tile) {
-    const int buf = (int)(tile & 1);
-    if (tile + 1 < ntiles) fetch((tile + 1) * FA_KT);
+  for (int64_t tile = t_beg; tile < t_end; ++tile) {
+    const int buf = (int)((tile - t_beg) & 1);
+    if (tile + 1 < t_end) fetch((tile + 1) * FA_KT);
     // ---- S^T = K Q^T: K fragments read four k-steps ahead of their MFMAs ----
     // (sched_barrier keeps each batch of reads ahead of the MFMAs using it)
     f32x16 s[2] = {zero16(), zero16()};
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(vb[db], p, o[db]);
-    if (tile + 1 < ntiles) {
+    if (tile + 1 < t_end) {
       stash(buf ^ 1);
       __syncthreads();
     }
@@ -182,6 +186,9 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
   // ---- epilogue -------------------------------------------------------------
   const float l = l_part + __shfl_xor(l_part, 32, 64);
   const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  // split z writes its partial (normalised O, LSE) at slice z
+  out = static_cast<char*>(out) + (size_t)split * Nq * W * (OUT_F32 ? 4 : 2);
+  lse += (int64_t)split * Nq * H;
   if (qok) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -207,12 +214,32 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
   }
 }
 
+int flash_splits(int64_t Nq, int H, int64_t Nk) {
+  // two blocks per CU.  Splitting costs a merge of S fp32 partials, so split
+  // only when the last round of blocks would be under 85 % full, and then
+  // take the smallest count that fills it to 90 % (at least 4 key tiles per
+  // split)
+  const double slots = 512.0;
+  const int64_t blocks = ceil_div(Nq, FA_QB) * H, tiles = ceil_div(Nk, FA_KT);
+  auto eff = [&](int S) {
+    const double rounds = (double)(blocks * S) / slots;
+    return rounds / std::ceil(rounds);
+  };
+  if (eff(1) >= 0.85) return 1;
+  int best = 1;
+  for (int S = 2; S <= 8 && tiles >= 4 * S; ++S) {
+    if (eff(S) > eff(best)) best = S;
+    if (eff(S) >= 0.9) return S;
+  }
+  return best;
+}
+
 nkv_status launch_flash(const uint16_t* q, int64_t Nq, int H, float tau, const uint16_t* kall,
                         const uint16_t* vt, int64_t Nk, int64_t ld, bool out_f32, void* out,
-                        float* lse, hipStream_t st) {
+                        float* lse, int nsplit, hipStream_t st) {
   if (Nq == 0) return NKV_OK;
   const float c = tau * 1.4426950408889634f;
-  dim3 grid((unsigned)ceil_div(Nq, FA_QB), (unsigned)H);
+  dim3 grid((unsigned)ceil_div(Nq, FA_QB), (unsigned)H, (unsigned)nsplit);
   if (out_f32)
     hipLaunchKernelGGL(k_flash<true>, grid, dim3(256), 0, st, q, Nq, H, c, kall, vt, Nk, ld, out, lse);
   else

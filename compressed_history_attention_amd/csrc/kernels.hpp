@@ -58,6 +58,11 @@ nkv_status launch_fit_update(int dt, const void* x, int64_t N, int W, const int3
 nkv_status launch_fit_counts(const int32_t* idx, int64_t N, int A, int32_t* counts,
                              hipStream_t s);
 
+// LSE merge (merge.hip): n parts at slices of (o_parts, lse_parts) with
+// strides Nq W / Nq H, plus an optional extra part (o_x, lse_x)
+nkv_status launch_lse_merge_parts(int64_t Nq, int H, int d, int n, const float* o_parts,
+                                  const float* lse_parts, const float* o_x, const float* lse_x,
+                                  void* out, int out_dt, float* lse_out, hipStream_t s);
 // LSE merge (merge.hip)
 nkv_status launch_lse_merge(int64_t Nq, int H, int d, const float* o_a, const float* lse_a,
                             const float* o_b, const float* lse_b, void* out, int out_dt,

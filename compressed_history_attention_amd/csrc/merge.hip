@@ -4,59 +4,92 @@
 // HBM-bound elementwise pass: one block per query row, the per-head weights
 // computed once into LDS, then every channel of the row streamed once.
 #include "kernels.hpp"
+#include "mfma.hpp"
 
 namespace nkv {
 
+// Parts 0..n-1 are the slices p = 0..n-1 of (o_parts, lse_parts) with
+// strides Nq W and Nq H; an optional extra part (o_x, lse_x) follows.
+// L = logsumexp_p L_p; O = sum_p exp(L_p - L) O_p (a -inf part adds nothing).
 template <int DT>
-__global__ __launch_bounds__(256) void k_lse_merge(int H, int d, const float* __restrict__ o_a,
-                                                   const float* __restrict__ lse_a,
-                                                   const float* __restrict__ o_b,
-                                                   const float* __restrict__ lse_b,
+__global__ __launch_bounds__(256) void k_lse_merge(int64_t Nq, int H, int d, int n,
+                                                   const float* __restrict__ o_parts,
+                                                   const float* __restrict__ lse_parts,
+                                                   const float* __restrict__ o_x,
+                                                   const float* __restrict__ lse_x,
                                                    void* __restrict__ out,
                                                    float* __restrict__ lse_out) {
-  extern __shared__ float sw[];  // wa[H], wb[H], L[H]
-  float* wa = sw;
-  float* wb = sw + H;
-  float* Ls = sw + 2 * H;
+  extern __shared__ float sw[];  // weights [n + 1][H], L[H]
+  const int np = n + (o_x ? 1 : 0);
+  float* Ls = sw + (size_t)np * H;
   const int64_t qi = blockIdx.x;
   const int W = H * d;
+  auto part_lse = [&](int p, int h) {
+    return p < n ? lse_parts[((int64_t)p * Nq + qi) * H + h] : lse_x[qi * H + h];
+  };
   for (int h = threadIdx.x; h < H; h += blockDim.x) {
-    const float la = lse_a[qi * H + h], lb = lse_b[qi * H + h];
-    const float mx = fmaxf(la, lb);
+    float mx = -INFINITY;
+    for (int p = 0; p < np; ++p) mx = fmaxf(mx, part_lse(p, h));
     if (mx == -INFINITY) {
-      wa[h] = 0.f; wb[h] = 0.f; Ls[h] = -INFINITY;
+      for (int p = 0; p < np; ++p) sw[p * H + h] = 0.f;
+      Ls[h] = -INFINITY;
     } else {
-      const float ea = expf(la - mx), eb = expf(lb - mx);
-      const float tot = ea + eb;
-      wa[h] = ea / tot;
-      wb[h] = eb / tot;
+      float tot = 0.f;
+      for (int p = 0; p < np; ++p) {
+        const float e = expf(part_lse(p, h) - mx);
+        sw[p * H + h] = e;
+        tot += e;
+      }
+      for (int p = 0; p < np; ++p) sw[p * H + h] /= tot;
       Ls[h] = mx + logf(tot);
     }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < W; c += blockDim.x) {
+  // four channels (one head: d % 4 == 0) per thread and step
+  for (int c = 4 * threadIdx.x; c < W; c += 4 * blockDim.x) {
     const int h = c / d;
-    const float va = wa[h] > 0.f ? o_a[qi * W + c] : 0.f;
-    const float vb = wb[h] > 0.f ? o_b[qi * W + c] : 0.f;
-    st<DT>(out, qi * W + c, wa[h] * va + wb[h] * vb);
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < np; ++p) {
+      const float wgt = sw[p * H + h];
+      if (wgt > 0.f) {
+        const float* src = p < n ? o_parts + ((int64_t)p * Nq + qi) * W + c : o_x + qi * W + c;
+        const f32x4 o = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] += wgt * o[u];
+      }
+    }
+    if constexpr (DT == NKV_F32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + qi * W + c) = v;
+    } else {
+      uint16_t* ob = static_cast<uint16_t*>(out) + qi * W + c;
+      *reinterpret_cast<uint2*>(ob) =
+          uint2{uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16),
+                uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16)};
+    }
   }
   __syncthreads();
   for (int h = threadIdx.x; h < H; h += blockDim.x) lse_out[qi * H + h] = Ls[h];
 }
 
+nkv_status launch_lse_merge_parts(int64_t Nq, int H, int d, int n, const float* o_parts,
+                                  const float* lse_parts, const float* o_x, const float* lse_x,
+                                  void* out, int out_dt, float* lse_out, hipStream_t s) {
+  if (Nq == 0) return NKV_OK;
+  const size_t lds = ((size_t)(n + 1) + 1) * H * sizeof(float);
+  if (out_dt == NKV_F32)
+    hipLaunchKernelGGL(k_lse_merge<NKV_F32>, dim3((unsigned)Nq), dim3(256), lds, s, Nq, H, d, n,
+                       o_parts, lse_parts, o_x, lse_x, out, lse_out);
+  else
+    hipLaunchKernelGGL(k_lse_merge<NKV_BF16>, dim3((unsigned)Nq), dim3(256), lds, s, Nq, H, d, n,
+                       o_parts, lse_parts, o_x, lse_x, out, lse_out);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
 nkv_status launch_lse_merge(int64_t Nq, int H, int d, const float* o_a, const float* lse_a,
                             const float* o_b, const float* lse_b, void* out, int out_dt,
                             float* lse_out, hipStream_t s) {
-  if (Nq == 0) return NKV_OK;
-  const size_t lds = 3 * (size_t)H * sizeof(float);
-  if (out_dt == NKV_F32)
-    hipLaunchKernelGGL(k_lse_merge<NKV_F32>, dim3((unsigned)Nq), dim3(256), lds, s, H, d, o_a,
-                       lse_a, o_b, lse_b, out, lse_out);
-  else
-    hipLaunchKernelGGL(k_lse_merge<NKV_BF16>, dim3((unsigned)Nq), dim3(256), lds, s, H, d, o_a,
-                       lse_a, o_b, lse_b, out, lse_out);
-  NKV_LAUNCH_CHECK();
-  return NKV_OK;
+  return launch_lse_merge_parts(Nq, H, d, 1, o_a, lse_a, o_b, lse_b, out, out_dt, lse_out, s);
 }
 
 }  // namespace nkv

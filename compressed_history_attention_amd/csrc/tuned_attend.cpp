@@ -12,6 +12,7 @@ namespace {
 
 struct Layout {
   int64_t nk = 0, nk_pad = 0;
+  int fsplit = 1;  // key-range splits of the flash launch
   size_t kall = 0, vt = 0, o_full = 0, lse_full = 0, o_low = 0, lse_low = 0, low = 0;
   size_t total = 0;
 };
@@ -31,9 +32,14 @@ Layout make_layout(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTabl
   L.nk_pad = ceil_div(L.nk, FA_KT) * FA_KT;
   L.kall = take(sizeof(uint16_t) * L.nk_pad * W);
   L.vt = take(sizeof(uint16_t) * L.nk_pad * W);
+  L.fsplit = flash_splits(Nq, s->H, L.nk);
+  if (low.total == 0 && L.fsplit > 1) {
+    L.o_full = take(sizeof(float) * Nq * W * L.fsplit);
+    L.lse_full = take(sizeof(float) * Nq * s->H * L.fsplit);
+  }
   if (low.total > 0) {
-    L.o_full = take(sizeof(float) * Nq * W);
-    L.lse_full = take(sizeof(float) * Nq * s->H);
+    L.o_full = take(sizeof(float) * Nq * W * L.fsplit);
+    L.lse_full = take(sizeof(float) * Nq * s->H * L.fsplit);
     L.o_low = take(sizeof(float) * Nq * W);
     L.lse_low = take(sizeof(float) * Nq * s->H);
     L.low = take(low_workspace_bytes(s, A_k, A_v, low, r_low, r_low_h, Nq));
@@ -73,17 +79,28 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
       return e;
   }
   const uint16_t* qb = static_cast<const uint16_t*>(q);
-  if (low.total == 0) {
-    ProfScope ps("flash", st);
-    return launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, false, out, lse, st);
-  }
   float* of = reinterpret_cast<float*>(ws + L.o_full);
   float* lf = reinterpret_cast<float*>(ws + L.lse_full);
+  if (low.total == 0) {
+    if (L.fsplit == 1) {
+      ProfScope ps("flash", st);
+      return launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, false, out, lse, 1, st);
+    }
+    {
+      ProfScope ps("flash", st);
+      if ((e = launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, L.fsplit, st)))
+        return e;
+    }
+    ProfScope ps("merge", st);
+    return launch_lse_merge_parts(Nq, H, s->d, L.fsplit, of, lf, nullptr, nullptr, out, NKV_BF16,
+                                  lse, st);
+  }
   float* ol = reinterpret_cast<float*>(ws + L.o_low);
   float* ll = reinterpret_cast<float*>(ws + L.lse_low);
   {
     ProfScope ps("flash", st);
-    if ((e = launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, st))) return e;
+    if ((e = launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, L.fsplit, st)))
+      return e;
   }
   // heads grouped by width (one group when every head shares r_low), in the
   // order their widths first appear; r_low is the widest
@@ -107,7 +124,7 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
                         units, groups[g], g == 0, st)))
       return e;
   ProfScope ps("merge", st);
-  return launch_lse_merge(Nq, H, s->d, of, lf, ol, ll, out, NKV_BF16, lse, st);
+  return launch_lse_merge_parts(Nq, H, s->d, L.fsplit, of, lf, ol, ll, out, NKV_BF16, lse, st);
 }
 
 }  // namespace nkv

@@ -15,9 +15,13 @@ nkv_status launch_decode_tuned(const BranchArgs& b, int W, int r, int group,
 nkv_status launch_stage_current(const uint16_t* ck, const uint16_t* cv, int64_t n_cur,
                                 int64_t n_pad_tail, int W, uint16_t* kall, uint16_t* vt,
                                 int64_t ld, int64_t key0, hipStream_t st);
-// out_f32: write fp32 O [Nq, W] (for merging) instead of bf16
+// Key-range splits for a flash launch (fill the last round of blocks).
+int flash_splits(int64_t Nq, int H, int64_t Nk);
+// out_f32: write fp32 O [Nq, W] (for merging) instead of bf16.  With
+// nsplit > 1, split z writes its partial (normalised O, LSE) at slices
+// out + z Nq W and lse + z Nq H (fp32 output only).
 nkv_status launch_flash(const uint16_t* q, int64_t Nq, int H, float tau, const uint16_t* kall,
                         const uint16_t* vt, int64_t Nk, int64_t ld, bool out_f32, void* out,
-                        float* lse, hipStream_t st);
+                        float* lse, int nsplit, hipStream_t st);
 
 }  // namespace nkv
