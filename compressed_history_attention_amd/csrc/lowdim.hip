@@ -73,6 +73,7 @@ struct Plan {
   int GK = 0, GV = 0, NB = 0, rlp = 0, rp = 0, ra = 0, av = 0, avp = 0;
   TileGeom g;
   // byte offsets inside the low-path workspace
+  size_t racc, rell;  // split coefficient sums reduced to bf16 hi/lo planes, and their ell
   size_t dkt, mvt, qt32, qt16, bound, tmax, present, misc, flags, cnt, base, tile_start, bcount,
       tile_bucket, perm, img, acc, wmass, ell, total;
 };
@@ -124,6 +125,8 @@ Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& l
   P.acc = take(sizeof(float) * prows * P.ra);
   P.wmass = take(sizeof(float) * prows * P.GV * CR);
   P.ell = take(sizeof(float) * prows);
+  P.racc = take(sizeof(float) * P.rows * P.ra);   // rows of 2 x ra bf16
+  P.rell = take(sizeof(float) * P.rows);
   P.total = off;
   return P;
 }
@@ -542,6 +545,7 @@ struct MainArgs {
   float* ell;
   int64_t Nq;
   int H, A_k, A_v, GK, GV, NB, r_low, ra;
+  int gvsplit;  // key-range splits at a^V-range boundaries
   float c;
   HeadSet hs;  // grid row y serves head hs.h[y]; grid z = key-range split
 };
@@ -647,8 +651,14 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
 
   // this split's tiles [ts, te) of the bucket-sorted sequence
   const int ntiles = __builtin_amdgcn_readfirstlane(a.tile_start[a.NB]);
-  const int ts = __builtin_amdgcn_readfirstlane((int)((int64_t)ntiles * split / nsplit));
-  const int te = __builtin_amdgcn_readfirstlane((int)((int64_t)ntiles * (split + 1) / nsplit));
+  // Splits at a^V-range boundaries (gvsplit) own disjoint center-mass ranges
+  // [g0, g1); otherwise a split is an equal share of the tile sequence
+  const int g0 = a.gvsplit ? a.GV * split / nsplit : 0;
+  const int g1 = a.gvsplit ? a.GV * (split + 1) / nsplit : a.GV;
+  const int ts = __builtin_amdgcn_readfirstlane(
+      a.gvsplit ? a.tile_start[g0 * a.GK] : (int)((int64_t)ntiles * split / nsplit));
+  const int te = __builtin_amdgcn_readfirstlane(
+      a.gvsplit ? a.tile_start[g1 * a.GK] : (int)((int64_t)ntiles * (split + 1) / nsplit));
   const char* sTrow = reinterpret_cast<const char*>(sT + rloc * TS);
   const uint16_t* qsrc = a.q + (rok ? qrow : q0) * W + h * 128 + 8 * hl;
 
@@ -674,7 +684,11 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   // (x = hi + lo to ~16 significant bits), written here once instead of being
   // split again for every use; rows [hi | lo] of 2 x GV * 64 (masses) and
   // 2 x ra (coefficient sums) bf16.
-  const bool planes = nsplit == 1;
+  // masses as planes when no other split writes the same rows; coefficient
+  // sums as planes only without splits
+  const bool planes = nsplit == 1 || a.gvsplit;
+  const bool acc_planes = nsplit == 1;
+  const int64_t mrow = a.gvsplit ? ((rok ? qrow : q0) * a.hs.n + blockIdx.y) : prow;
   const int WS = a.GV * CR;
   auto put_hilo = [&](uint16_t* hi, uint16_t* lo, f32x4 v) __attribute__((always_inline)) {
     float l[4];
@@ -685,7 +699,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   };
   auto put_mass = [&](int gv) __attribute__((always_inline)) {
     if (rok && planes) {
-      uint16_t* row = reinterpret_cast<uint16_t*>(a.wmass) + prow * 2 * WS + gv * CR;
+      uint16_t* row = reinterpret_cast<uint16_t*>(a.wmass) + mrow * 2 * WS + gv * CR;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -720,7 +734,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   auto zero_mass = [&](int g0, int g1) __attribute__((always_inline)) {
     if (!rok) return;
     if (planes) {
-      uint16_t* row = reinterpret_cast<uint16_t*>(a.wmass) + prow * 2 * WS;
+      uint16_t* row = reinterpret_cast<uint16_t*>(a.wmass) + mrow * 2 * WS;
       for (int gv = g0; gv < g1; ++gv)
         for (int c = hl * 4; c < CR; c += 8) {
           *reinterpret_cast<uint2*>(row + gv * CR + c) = uint2{0u, 0u};
@@ -734,7 +748,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       for (int c = hl; c < lim; c += 2) dst[c] = 0.f;
     }
   };
-  int zgv = 0;  // first a^V range of this split's rows not yet written
+  int zgv = g0;  // first a^V range of this split's rows not yet written
   auto flush = [&](int gv) __attribute__((always_inline)) {
     if (zgv < gv) zero_mass(zgv, gv);
     put_mass(gv);
@@ -925,7 +939,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   // no row or tile load may still be in flight into LDS when the block ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (prev_gv >= 0) flush(prev_gv);
-  if (zgv < a.GV) zero_mass(zgv, a.GV);
+  if (zgv < g1) zero_mass(zgv, g1);
   lsum += __shfl_xor(lsum, 32, 64);
   if (rok) {
 #pragma unroll
@@ -936,7 +950,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
         const f32x4 v{accT[db][4 * e4], accT[db][4 * e4 + 1], accT[db][4 * e4 + 2],
                       accT[db][4 * e4 + 3]};
         if (dim < a.r_low) {
-          if (planes) {
+          if (acc_planes) {
             uint16_t* row = reinterpret_cast<uint16_t*>(a.acc) + prow * 2 * a.ra;
             put_hilo(row + dim, row + a.ra + dim, v);
           } else {
@@ -957,6 +971,37 @@ nkv_status launch_main(const MainArgs& m, int64_t Nq, int nsplit, hipStream_t st
 }
 
 // ---------------------------------------------------------------------------
+// Split coefficient sums -> one bf16 hi/lo plane row each (and ell summed),
+// in split order: rows = (query, head of the group), one block per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void k_reduce_acc(const float* __restrict__ acc,
+                                                    const float* __restrict__ ell, int64_t rows,
+                                                    int nsplit, int r_low, int ra,
+                                                    uint16_t* __restrict__ racc,
+                                                    float* __restrict__ rell) {
+  const int64_t row = blockIdx.x;
+  for (int c = 4 * threadIdx.x; c < r_low; c += 4 * blockDim.x) {  // r_low % 16 == 0
+    f32x4 v = *reinterpret_cast<const f32x4*>(acc + row * r_low + c);
+    for (int sp = 1; sp < nsplit; ++sp) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(acc + ((int64_t)sp * rows + row) * r_low + c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] += w[u];
+    }
+    float l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) l[u] = v[u] - (float)(__bf16)v[u];
+    uint16_t* dst = racc + row * 2 * ra + c;
+    *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<uint2*>(dst + ra) = uint2{pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3])};
+  }
+  if (threadIdx.x == 0) {
+    float t = ell[row];
+    for (int sp = 1; sp < nsplit; ++sp) t += ell[(int64_t)sp * rows + row];
+    rell[row] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // restoration: O_low = (D_{V,h} acc + M mu^V_h) / ell,  LSE = (B + log2 ell) ln 2
 // GEMM over K = [acc hi | acc lo | M hi | M lo] (fp32 split into bf16 pairs)
 // ---------------------------------------------------------------------------
@@ -964,8 +1009,11 @@ struct RestoreProblem {
   static constexpr int BK = 64;
   int M, N, K;  // Nq, 128, 2 ra + 2 av
   int H, ldv, r_low, ra, A_v, av;
-  int nsplit;   // key-range splits of the main pass: their partial sums add
-  int WS;       // one split: bf16 hi/lo planes, mass rows [hi | lo] of 2 x WS
+  int nsplit;   // mass partials when !mass_planes (key-range splits: they add)
+  int WS;       // bf16 hi/lo planes: mass rows [hi | lo] of 2 x WS
+  int mass_planes;  // masses as planes (no split, or splits at a^V-range boundaries)
+  // the coefficient sums are always planes [hi | lo] of 2 x ra and ell one
+  // value per row (split partials are reduced before this GEMM)
   const float* acc;    // partials [nsplit][Nq][hs.n][r_low]
   const float* wmass;  // partials [nsplit][Nq][hs.n][A_v]
   const uint16_t* dv;    // restoration map [W, ldv]
@@ -981,7 +1029,7 @@ struct RestoreProblem {
   }
   __device__ u32x4 load_a(int zb, int m, int k) const {
     if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
-    if (nsplit == 1) {
+    if (k < 2 * ra || mass_planes != 0) {
       const int64_t pr = prow(0, m, zb);
       if (k < 2 * ra) {
         const int j = k >= ra ? k - ra : k;
@@ -992,23 +1040,12 @@ struct RestoreProblem {
       const int c = kk >= av ? kk - av + WS : kk;
       return ld_u32x4(reinterpret_cast<const uint16_t*>(wmass) + pr * 2 * WS + c);
     }
+    // masses as fp32 partials of key-range splits: summed and split here
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.f;
     bool lo;
-    if (k < 2 * ra) {
-      lo = k >= ra;
-      const int j = lo ? k - ra : k;
-      if (j + 8 <= r_low) {  // r_low % 16 == 0: 32-byte aligned row chunk
-        for (int s = 0; s < nsplit; ++s) {
-          const float* src = acc + prow(s, m, zb) * r_low + j;
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { v[i] += x0[i]; v[4 + i] += x1[i]; }
-        }
-      }
-    } else {
+    {
       const int kk = k - 2 * ra;
       lo = kk >= av;
       const int c = lo ? kk - av : kk;
@@ -1058,8 +1095,7 @@ struct RestoreProblem {
         const int m = m0 + 32 * i + acc_row(e, lane);
         if (m >= M) continue;
         const int64_t row = (int64_t)m * H + z;
-        float l = 0.f;
-        for (int s = 0; s < nsplit; ++s) l += ell[prow(s, m, zb)];
+        const float l = ell[prow(0, m, zb)];
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -1075,14 +1111,38 @@ struct RestoreProblem {
 
 }  // namespace
 
-int low_splits(int64_t Nq, int n_heads, int64_t n_low) {
-  const int64_t blocks = ceil_div(Nq, RBW) * n_heads;
-  int64_t S = std::max<int64_t>(1, 512 / std::max<int64_t>(blocks, 1));  // ~2 blocks per CU
-  S = std::min<int64_t>(S, std::max<int64_t>(1, ceil_div(n_low, NT) / 8));  // >= 8 tiles each
-  return (int)std::min<int64_t>(S, 16);
+LowSplit low_split_plan(int64_t Nq, int n_heads, int64_t n_low, int A_v) {
+  // One block per CU: choose the split count by how full the last round of
+  // blocks is, less a small cost per split (partial sums, block set-up).
+  // With several a^V ranges, split at range boundaries (powers of two, at
+  // most one split per range) so that the center masses are not duplicated.
+  const int GV = (int)ceil_div(A_v, CR);
+  const int64_t blocks = std::max<int64_t>(1, ceil_div(Nq, RBW) * n_heads);
+  const int64_t tiles = ceil_div(n_low, NT);
+  auto score = [&](int S) {
+    const double r = (double)(blocks * S) / 256.0;
+    return r / std::ceil(r) - 0.004 * S;
+  };
+  LowSplit best{1, false};
+  double bs = score(1);
+  if (GV >= 2) {
+    for (int S = 2; S <= 16 && S <= GV && tiles >= 8 * S; S *= 2)
+      if (score(S) > bs + 1e-3) {
+        bs = score(S);
+        best = LowSplit{S, true};
+      }
+  } else {
+    for (int S = 2; S <= 16 && tiles >= 8 * S; ++S)
+      if (score(S) > bs + 1e-3) {
+        bs = score(S);
+        best = LowSplit{S, false};
+      }
+  }
+  return best;
 }
 
-int64_t low_part_units(int64_t Nq, int H, int32_t r_low, const int32_t* r_low_h, int64_t n_low) {
+int64_t low_part_units(int64_t Nq, int H, int32_t r_low, const int32_t* r_low_h, int64_t n_low,
+                       int A_v) {
   int64_t best = 0;
   std::vector<int> done(H, 0);
   for (int h0 = 0; h0 < H; ++h0) {
@@ -1095,14 +1155,14 @@ int64_t low_part_units(int64_t Nq, int H, int32_t r_low, const int32_t* r_low_h,
         ++n;
       }
     }
-    best = std::max<int64_t>(best, (int64_t)n * low_splits(Nq, n, n_low));
+    best = std::max<int64_t>(best, (int64_t)n * low_split_plan(Nq, n, n_low, A_v).S);
   }
   return best;
 }
 
 size_t low_workspace_bytes(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& low,
                            int32_t r_low, const int32_t* r_low_h, int64_t Nq) {
-  const int64_t units = low_part_units(Nq, s->H, r_low, r_low_h, low.total);
+  const int64_t units = low_part_units(Nq, s->H, r_low, r_low_h, low.total, A_v);
   return make_plan(s, A_k, A_v, low, r_low, Nq, units).total;
 }
 
@@ -1114,7 +1174,8 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   // offsets from the widest group's plan, so that every group finds the
   // shared sort results in the same place; geometry from this group's width
   const Plan P = make_plan(s, kb.A, vb.A, low, r_low_max, Nq, part_units);
-  const int nsplit = low_splits(Nq, hs.n, low.total);
+  const LowSplit split = low_split_plan(Nq, hs.n, low.total, vb.A);
+  const int nsplit = split.S;
   const int rlp = (int)ceil_div(r_low, 16) * 16, ra = (int)ceil_div(r_low, 32) * 32;
   const TileGeom geom = tile_geom(rlp);
   const int H = s->H, W = H * s->d, r = s->r;
@@ -1194,7 +1255,8 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   {
   ProfScope ps_main("low_main", st);
   MainArgs m{q, static_cast<const uint16_t*>(kb.centers), qt16, bound, img, tile_start,
-             tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.GV, P.NB, r_low, ra, c, hs};
+             tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.GV, P.NB, r_low, ra,
+             split.gv ? 1 : 0, c, hs};
   switch (rlp) {
     case 16: e = launch_main<16>(m, Nq, nsplit, st); break;
     case 32: e = launch_main<32>(m, Nq, nsplit, st); break;
@@ -1211,9 +1273,20 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   // restoration
   {
   ProfScope ps_restore("low_restore", st);
+  const float* acc_r = acc;
+  const float* ell_r = ell;
+  if (nsplit > 1) {
+    const int64_t rows_g = Nq * hs.n;
+    hipLaunchKernelGGL(k_reduce_acc, dim3((unsigned)rows_g), dim3(128), 0, st, acc, ell, rows_g,
+                       nsplit, r_low, ra, reinterpret_cast<uint16_t*>(at(P.racc)),
+                       reinterpret_cast<float*>(at(P.rell)));
+    NKV_LAUNCH_CHECK();
+    acc_r = reinterpret_cast<const float*>(at(P.racc));
+    ell_r = reinterpret_cast<const float*>(at(P.rell));
+  }
   RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, mp.ld, r_low, ra, vb.A, P.av, nsplit,
-                    P.GV * CR, acc, wmass,
-                    static_cast<const uint16_t*>(mp.omap), mvt, ell, bound, o_low, lse_low, hs};
+                    P.GV * CR, (nsplit == 1 || split.gv) ? 1 : 0, acc_r, wmass,
+                    static_cast<const uint16_t*>(mp.omap), mvt, ell_r, bound, o_low, lse_low, hs};
   if ((e = launch_gemm(rp, hs.n, st))) return e;
   }
   // rows whose bound may be loose: exact generic recomputation

@@ -9,8 +9,13 @@ namespace nkv {
 // alone would leave CUs idle), and the partial-sum rows per query that the
 // widest demand over the head groups of a call needs (groups as in
 // tuned_attend: heads of equal width).
-int low_splits(int64_t Nq, int n_heads, int64_t n_low);
-int64_t low_part_units(int64_t Nq, int H, int32_t r_low, const int32_t* r_low_h, int64_t n_low);
+struct LowSplit {
+  int S;    // splits of the tile sequence (grid z)
+  bool gv;  // at a^V-range boundaries: each split owns its center-mass ranges
+};
+LowSplit low_split_plan(int64_t Nq, int n_heads, int64_t n_low, int A_v);
+int64_t low_part_units(int64_t Nq, int H, int32_t r_low, const int32_t* r_low_h, int64_t n_low,
+                       int A_v);
 size_t low_workspace_bytes(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& low,
                            int32_t r_low, const int32_t* r_low_h, int64_t Nq);
 // Writes the columns of O_low fp32 [Nq, W] and LSE_low [Nq, H] of the heads

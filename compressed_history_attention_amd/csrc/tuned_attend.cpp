@@ -118,7 +118,7 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
     }
     groups[g].h[groups[g].n++] = h;
   }
-  const int64_t units = low_part_units(Nq, H, r_low, r_low_h, low.total);
+  const int64_t units = low_part_units(Nq, H, r_low, r_low_h, low.total, vb.A);
   for (int g = 0; g < ng; ++g)
     if ((e = launch_low(s, kb, vb, mp, low, widths[g], tau, qb, Nq, ol, ll, ws + L.low, r_low,
                         units, groups[g], g == 0, st)))
