@@ -972,29 +972,32 @@ nkv_status launch_main(const MainArgs& m, int64_t Nq, int nsplit, hipStream_t st
 
 // ---------------------------------------------------------------------------
 // Split coefficient sums -> one bf16 hi/lo plane row each (and ell summed),
-// in split order: rows = (query, head of the group), one block per row.
+// in split order: rows = (query, head of the group); one thread per four
+// coefficients of a row (r_low % 16 == 0).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void k_reduce_acc(const float* __restrict__ acc,
+__global__ __launch_bounds__(256) void k_reduce_acc(const float* __restrict__ acc,
                                                     const float* __restrict__ ell, int64_t rows,
                                                     int nsplit, int r_low, int ra,
                                                     uint16_t* __restrict__ racc,
                                                     float* __restrict__ rell) {
-  const int64_t row = blockIdx.x;
-  for (int c = 4 * threadIdx.x; c < r_low; c += 4 * blockDim.x) {  // r_low % 16 == 0
-    f32x4 v = *reinterpret_cast<const f32x4*>(acc + row * r_low + c);
-    for (int sp = 1; sp < nsplit; ++sp) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(acc + ((int64_t)sp * rows + row) * r_low + c);
+  const int per = r_low / 4;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * per) return;
+  const int64_t row = i / per;
+  const int c = (int)(i - row * per) * 4;
+  f32x4 v = *reinterpret_cast<const f32x4*>(acc + row * r_low + c);
+  for (int sp = 1; sp < nsplit; ++sp) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(acc + ((int64_t)sp * rows + row) * r_low + c);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] += w[u];
-    }
-    float l[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) l[u] = v[u] - (float)(__bf16)v[u];
-    uint16_t* dst = racc + row * 2 * ra + c;
-    *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    *reinterpret_cast<uint2*>(dst + ra) = uint2{pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3])};
+    for (int u = 0; u < 4; ++u) v[u] += w[u];
   }
-  if (threadIdx.x == 0) {
+  float l[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) l[u] = v[u] - (float)(__bf16)v[u];
+  uint16_t* dst = racc + row * 2 * ra + c;
+  *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  *reinterpret_cast<uint2*>(dst + ra) = uint2{pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3])};
+  if (c == 0) {
     float t = ell[row];
     for (int sp = 1; sp < nsplit; ++sp) t += ell[(int64_t)sp * rows + row];
     rell[row] = t;
@@ -1277,8 +1280,9 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   const float* ell_r = ell;
   if (nsplit > 1) {
     const int64_t rows_g = Nq * hs.n;
-    hipLaunchKernelGGL(k_reduce_acc, dim3((unsigned)rows_g), dim3(128), 0, st, acc, ell, rows_g,
-                       nsplit, r_low, ra, reinterpret_cast<uint16_t*>(at(P.racc)),
+    hipLaunchKernelGGL(k_reduce_acc, dim3((unsigned)ceil_div(rows_g * (r_low / 4), 256)), dim3(256),
+                       0, st, acc, ell, rows_g, nsplit, r_low, ra,
+                       reinterpret_cast<uint16_t*>(at(P.racc)),
                        reinterpret_cast<float*>(at(P.rell)));
     NKV_LAUNCH_CHECK();
     acc_r = reinterpret_cast<const float*>(at(P.racc));
