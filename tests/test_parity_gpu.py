@@ -327,6 +327,42 @@ def test_low_read_with_few_tokens_ignores_stale_workspace():
         assert rel <= OUT_TOL and lerr <= LSE_TOL
 
 
+def test_low_read_center_range_splits_with_empty_ranges():
+    """Splits of the main pass at V-center-range boundaries: 960 far-away V
+    centers that no token uses put every token in the first of 16 ranges,
+    so most splits own no tiles at all and must still leave zero masses,
+    zero coefficient sums and zero ell behind (workspace filled with NaN)."""
+    cfg = S("C3", H=2, r=128, A=64, n_hist=3000, Nq=100, N_cur=30, chunk=1000, r_low=64,
+            n_full_tail=200, seed=44)
+    w = synth.workload(cfg)
+    rng = np.random.default_rng(9)
+    far = synth.store(100.0 * rng.standard_normal((960, cfg.W)), cfg.dtype)
+    cen = [w.centers(0), np.concatenate([w.centers(1), far])]
+    hist = [w.history_tokens(b) for b in range(2)]
+    enc = [oracle.encode(hist[b], cen[b], w.encoder(b), cfg.group, cfg.dtype) for b in range(2)]
+    assert enc[1]["idx"].max() < 64
+    shape = shape_of(cfg)
+    dev_b = [lib.Branch(to_dev(enc[b]["idx"]), to_dev(enc[b]["codes"]), to_dev(enc[b]["scales_bits"]),
+                        to_dev(cen[b], cfg.dtype), to_dev(w.decoder(b), cfg.dtype)) for b in range(2)]
+    q = to_dev(w.queries(), cfg.dtype)
+    ck, cv = to_dev(w.current(0), cfg.dtype), to_dev(w.current(1), cfg.dtype)
+    route = cfg.segments()
+    n = lib.nkv_attend_workspace_size(shape, 64, 1024, cfg.n_hist, route, cfg.r_low, cfg.Nq,
+                                      cfg.N_cur)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    out, lse = lib.attend_fast(shape, dev_b[0], dev_b[1], cfg.n_hist, route, cfg.r_low, q, ck, cv,
+                               ws=ws)
+    torch.cuda.synchronize()
+    ob = [oracle.Branch(enc[b]["idx"], enc[b]["codes"], enc[b]["scales_bits"], cen[b],
+                        w.decoder(b), cfg.dtype, cfg.group) for b in range(2)]
+    qf = oracle.as_f64(w.queries(), cfg.dtype)
+    kf, vf = oracle.as_f64(w.current(0), cfg.dtype), oracle.as_f64(w.current(1), cfg.dtype)
+    ro, rl = oracle.attend_fast(qf, ob[0], ob[1], route, cfg.r_low, kf, vf, cfg.H, cfg.d, cfg.tau)
+    rel, lerr = attention_errors(from_dev(out), from_dev(lse), ro, rl)
+    log(f"  empty center ranges: rel={rel:.3e} dLSE={lerr:.3e}")
+    assert rel <= OUT_TOL and lerr <= LSE_TOL
+
+
 def test_attend_full_C1():
     _check_attend("C1", sample=48)
 
