@@ -124,9 +124,14 @@ def test_attend_heads_validation():
     bad = (ctypes.c_int32 * 2)(16, 99)
     assert L.nkv_attend_heads_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, bad, 4, 2) \
         == lib.SIZE_MAX
-    # the widest head sizes the workspace: never smaller than the uniform call at that width
+    # equal widths are the uniform call: the same workspace
     uni = L.nkv_attend_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, 48, 4, 2)
-    assert need >= uni
+    same = (ctypes.c_int32 * 2)(48, 48)
+    assert L.nkv_attend_heads_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, same, 4, 2) == uni
+    # with the same head grouping, a wider head never needs less
+    narrow = (ctypes.c_int32 * 2)(16, 32)
+    assert need >= L.nkv_attend_heads_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, narrow,
+                                                     4, 2)
     assert _attend_heads(sh, [16, 48], Nq=0, ws=FAKE, wsb=need) == 0
 
 
