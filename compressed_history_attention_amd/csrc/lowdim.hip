@@ -54,8 +54,11 @@ constexpr float BOUND_GAP_LIMIT = 60.f;  // log2 units
 //   [ko_off, +256)       per key: byte offset of its a^K slot in the T table row
 //   [hd_off, +16)        header: the facts of the FOLLOWING tile (its bucket,
 //                        whether it opens that bucket, the a^K range of the
-//                        bucket after it or -1), so a kernel learns them while
-//                        it works on this tile; zero after the last tile
+//                        bucket after it or -1; zero after the last tile), so
+//                        a kernel learns them while it works on this tile;
+//                        then this tile's step mask: bit 2s + u set when a
+//                        real key of 16-key step s (keys 16 s .. 16 s + 15)
+//                        has its V center in half u of the a^V range
 struct TileGeom {
   int rlp, rp, nks, nvb, ck_bytes, cv_off, cv_bytes, ko_off, hd_off, bytes;
 };
@@ -111,8 +114,9 @@ Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& l
   P.present = take(sizeof(uint32_t) * A_k);
   P.misc = take(sizeof(uint32_t) * 4);
   P.flags = take(sizeof(int32_t) * P.rows);
-  P.cnt = take(sizeof(int32_t) * P.nchunk * P.NB);
-  P.base = take(sizeof(int32_t) * P.nchunk * P.NB);
+  // counting sort over sub-buckets: (bucket, which half of its a^V range)
+  P.cnt = take(sizeof(int32_t) * P.nchunk * 2 * P.NB);
+  P.base = take(sizeof(int32_t) * P.nchunk * 2 * P.NB);
   P.tile_start = take(sizeof(int32_t) * (P.NB + 1));
   P.bcount = take(sizeof(int32_t) * P.NB);
   P.tile_bucket = take(sizeof(int32_t) * P.max_tiles);
@@ -157,31 +161,37 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
   }
 }
 
-__device__ __forceinline__ int bucket_of(const BranchArgs& kb, const BranchArgs& vb, int64_t t,
-                                         int GK) {
-  return (vb.idx[t] / CR) * GK + kb.idx[t] / CR;
+// Sub-bucket of a token: its bucket (a^V range, a^K range) times two, plus
+// which half of the a^V range its V center lies in.  Within a bucket the
+// tokens of the lower half come first, so most 16-key steps of a tile touch
+// one half of the range and need only one of the two one-hot MFMAs.
+__device__ __forceinline__ int sub_bucket_of(const BranchArgs& kb, const BranchArgs& vb, int64_t t,
+                                             int GK) {
+  const int av = vb.idx[t];
+  return ((av / CR) * GK + kb.idx[t] / CR) * 2 + ((av % CR) >= CR / 2 ? 1 : 0);
 }
 
 __global__ __launch_bounds__(256) void k_bucket_count(BranchArgs kb, BranchArgs vb, RangeTable low,
                                                       int GK, int NB, int32_t* __restrict__ cnt,
                                                       uint32_t* __restrict__ present) {
-  extern __shared__ int lc[];
-  for (int b = threadIdx.x; b < NB; b += 256) lc[b] = 0;
+  extern __shared__ int lc[];  // per sub-bucket
+  for (int b = threadIdx.x; b < 2 * NB; b += 256) lc[b] = 0;
   __syncthreads();
   const int64_t j0 = (int64_t)blockIdx.x * CHUNK;
   for (int i = threadIdx.x; i < CHUNK; i += 256) {
     const int64_t j = j0 + i;
     if (j < low.total) {
       const int64_t t = map_index(low, j);
-      atomicAdd(&lc[bucket_of(kb, vb, t, GK)], 1);
+      atomicAdd(&lc[sub_bucket_of(kb, vb, t, GK)], 1);
       present[kb.idx[t]] = 1u;
     }
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < NB; b += 256) cnt[(int64_t)blockIdx.x * NB + b] = lc[b];
+  for (int b = threadIdx.x; b < 2 * NB; b += 256) cnt[(int64_t)blockIdx.x * 2 * NB + b] = lc[b];
 }
 
-// one block: bucket totals, padded tile ranges, per-chunk bases, tile->bucket
+// one block: bucket totals, padded tile ranges, per-chunk bases of the
+// sub-buckets (a bucket's lower-half tokens first), tile->bucket
 __global__ __launch_bounds__(1024) void k_bucket_scan(const int32_t* __restrict__ cnt, int nchunk,
                                                       int NB, int32_t* __restrict__ base,
                                                       int32_t* __restrict__ tile_start,
@@ -193,7 +203,8 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(const int32_t* __restrict_
   const int tid = threadIdx.x;
   for (int b = tid; b < NB; b += 1024) {
     int tot = 0;
-    for (int c = 0; c < nchunk; ++c) tot += cnt[(int64_t)c * NB + b];
+    for (int c = 0; c < nchunk; ++c)
+      tot += cnt[(int64_t)c * 2 * NB + 2 * b] + cnt[(int64_t)c * 2 * NB + 2 * b + 1];
     bcount[b] = tot;
     ntile[b] = (tot + NT - 1) / NT;
   }
@@ -220,16 +231,17 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(const int32_t* __restrict_
     tile_start[b] = run;
     for (int k = 0; k < nt; ++k) tile_bucket[run + k] = b;
     int acc = run * NT;
-    for (int c = 0; c < nchunk; ++c) {
-      base[(int64_t)c * NB + b] = acc;
-      acc += cnt[(int64_t)c * NB + b];
-    }
+    for (int half = 0; half < 2; ++half)
+      for (int c = 0; c < nchunk; ++c) {
+        base[(int64_t)c * 2 * NB + 2 * b + half] = acc;
+        acc += cnt[(int64_t)c * 2 * NB + 2 * b + half];
+      }
     run += nt;
   }
 }
 
-// stable scatter: slot = base[chunk][bucket] + rank of the token among the
-// chunk's earlier tokens of the same bucket
+// stable scatter: slot = base[chunk][sub-bucket] + rank of the token among
+// the chunk's earlier tokens of the same sub-bucket
 __global__ __launch_bounds__(256) void k_bucket_scatter(BranchArgs kb, BranchArgs vb, RangeTable low,
                                                         int GK, int NB,
                                                         const int32_t* __restrict__ base,
@@ -237,13 +249,13 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(BranchArgs kb, BranchArg
   __shared__ int bid[CHUNK];
   const int64_t j0 = (int64_t)blockIdx.x * CHUNK;
   const int n = (int)min<int64_t>(CHUNK, low.total - j0);
-  for (int i = threadIdx.x; i < n; i += 256) bid[i] = bucket_of(kb, vb, map_index(low, j0 + i), GK);
+  for (int i = threadIdx.x; i < n; i += 256) bid[i] = sub_bucket_of(kb, vb, map_index(low, j0 + i), GK);
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += 256) {
     const int b = bid[i];
     int rank = 0;
     for (int k = 0; k < i; ++k) rank += (bid[k] == b);
-    perm[base[(int64_t)blockIdx.x * NB + b] + rank] = (int32_t)map_index(low, j0 + i);
+    perm[base[(int64_t)blockIdx.x * 2 * NB + b] + rank] = (int32_t)map_index(low, j0 + i);
   }
 }
 
@@ -346,6 +358,9 @@ __global__ __launch_bounds__(256) void k_build_images(
       hd = u32x4{(uint32_t)bn, tile + 1 == tile_start[bn] ? 1u : 0u,
                  (uint32_t)(tn < ntl ? tile_bucket[tn] % GK : -1), 0u};
     }
+    uint32_t mask = 0u;
+    for (int k = 0; k < nreal; ++k) mask |= 1u << (2 * (k / 16) + ((sav[k] % CR) >= CR / 2 ? 1 : 0));
+    hd[3] = mask;
     *reinterpret_cast<u32x4*>(base + g.hd_off) = hd;
   }
   static_assert(NT == 64, "one wave holds the keys of a tile");
@@ -673,7 +688,9 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     const int c = wave + 8 * k;
     if (c < Geo::CHUNKS && tt < te) {
       const char* chunk = a.img + ((int64_t)tt * G.bytes + c * 1024);  // wave-uniform
-      __builtin_amdgcn_global_load_lds(chunk + (uint32_t)(lane * 16),
+      uint32_t lo = lane * 16;
+      asm volatile("" : "+v"(lo));
+      __builtin_amdgcn_global_load_lds(chunk + lo,
                                        (__attribute__((address_space(3))) void*)(dst + c * 1024),
                                        16, 0, 0);
     }
@@ -767,7 +784,12 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     bf16x8 qv[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qv[ks] = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
-    // two center blocks: independent accumulation chains, interleaved
+    // two center blocks: independent accumulation chains, interleaved.  The
+    // lane's LDS offsets are derived here from an opaque copy of the lane
+    // index: hoisted out of the tile loop they would hold 64 registers for
+    // the whole kernel.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
     f32x16 tt[2] = {zero16(), zero16()};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -775,7 +797,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       for (int cb = 0; cb < 2; ++cb) {
         bf16x8 m;
         if constexpr (SM) {
-          m = as_bf16x8(lds_row_block(sM, cb * 32 + (lane & 31), 2 * ks + hl));
+          m = as_bf16x8(lds_row_block(sM, cb * 32 + (ln & 31), 2 * ks + (ln >> 5)));
         } else {
           const int cen = gk * CR + cb * 32 + (lane & 31);
           m = as_bf16x8(ld_u32x4(a.muk + (int64_t)(cen < a.A_k ? cen : 0) * W + h * 128 +
@@ -787,8 +809,9 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int cl = cb * 32 + acc_row(e, lane);
-        sT[rloc * TS + cl] = (gk * CR + cl < a.A_k) ? fmaf(tt[cb][e], a.c, -Bq) : -INFINITY;
+        const int cl = cb * 32 + acc_row(e, ln);
+        sT[(wave * 32 + (ln & 31)) * TS + cl] =
+            (gk * CR + cl < a.A_k) ? fmaf(tt[cb][e], a.c, -Bq) : -INFINITY;
       }
     if (hl == 0) sT[rloc * TS + CR] = -INFINITY;
   };
@@ -822,11 +845,13 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       }
     }
     // this tile's header: the bucket facts of tile t + 1
+    uint32_t smask;  // this tile's step mask (which one-hot halves each step needs)
     {
       const u32x4 hd = *reinterpret_cast<const u32x4*>(cur + G.hd_off);
       cur_b = __builtin_amdgcn_readfirstlane((int)hd[0]);
       cur_first = __builtin_amdgcn_readfirstlane((int)hd[1]);
       cur_ngk = __builtin_amdgcn_readfirstlane((int)hd[2]);
+      smask = __builtin_amdgcn_readfirstlane(hd[3]);
     }
     if (!active) {
 #pragma unroll
@@ -876,11 +901,15 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       }
       return as_bf16x8(pk);
     };
-    auto pv = [&](const bf16x8 (&vo)[NPB + 2], bf16x8 p) __attribute__((always_inline)) {
+    // step s of the tile: MFMAs only for what its real keys touch (a step
+    // of padding keys only has p = 0)
+    auto pv = [&](const bf16x8 (&vo)[NPB + 2], bf16x8 p, int step) __attribute__((always_inline)) {
+      const uint32_t m = (smask >> (2 * step)) & 3u;
+      if (m == 0u) return;
 #pragma unroll
       for (int db = 0; db < NPB; ++db) accT[db] = mfma_bf16(vo[db], p, accT[db]);
-      accW[0] = mfma_bf16(vo[NPB], p, accW[0]);
-      accW[1] = mfma_bf16(vo[NPB + 1], p, accW[1]);
+      if (m & 1u) accW[0] = mfma_bf16(vo[NPB], p, accW[0]);
+      if (m & 2u) accW[1] = mfma_bf16(vo[NPB + 1], p, accW[1]);
     };
     // wide coefficient rows: one K operand set, reloaded for the second half
     constexpr bool KDB = RLP <= 96;
@@ -917,20 +946,20 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     read_v(0, 1, vb);
     dma(t + 1, nxt, 2);
     __builtin_amdgcn_sched_barrier(0);
-    pv(va, p);
+    pv(va, p, 0);
     p = expo(s0, 1);
 #pragma unroll
     for (int k = 3; k < Geo::DMA_PER_WAVE; ++k) dma(t + 1, nxt, k);
     __builtin_amdgcn_sched_barrier(0);
     read_v(1, 0, va);
-    pv(vb, p);
+    pv(vb, p, 1);
     p = expo(s1, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_v(1, 1, vb);
-    pv(va, p);
+    pv(va, p, 2);
     p = expo(s1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    pv(vb, p);
+    pv(vb, p, 3);
   };
   for (int t = ts; t < te; t += 2) {
     body(t, sB0, sB1);
@@ -1226,7 +1255,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(kb.A, 256)), dim3(256), 0, st, present, (int64_t)kb.A);
   // bucket sort of the low-routed tokens
   const int nch = (int)P.nchunk;
-  hipLaunchKernelGGL(k_bucket_count, dim3(nch), dim3(256), P.NB * sizeof(int), st, kb, vb, low,
+  hipLaunchKernelGGL(k_bucket_count, dim3(nch), dim3(256), 2 * P.NB * sizeof(int), st, kb, vb, low,
                      P.GK, P.NB, cnt, present);
   hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), (P.NB + 1024) * sizeof(int), st, cnt, nch,
                      P.NB, base, tile_start, bcount, tile_bucket);
