@@ -1,5 +1,7 @@
 // Orchestration of the tuned (MFMA) attention path: workspace layout and the
 // sequence of kernels for the full-dimensional and the Fast reads.
+#include <mutex>
+
 #include "lowdim.hpp"
 #include "prof.hpp"
 #include "tuned_internal.hpp"
@@ -48,6 +50,37 @@ Layout make_layout(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTabl
   return L;
 }
 
+// A second stream per device for the full-dimensional half of a Fast read
+// with per-head widths: decode + flash attention run there while the
+// caller's stream runs the low-dimensional passes, and the LSE merge on the
+// caller's stream waits for both (fork and join through two events).
+// Created on first use (default priority, non-blocking), kept until the
+// process ends; a mutex covers each read's enqueue so that calls from
+// several host threads use the events one at a time.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+  bool ok = false;
+};
+
+SideStream* side_stream() {
+  constexpr int MAX_DEV = 64;
+  static std::mutex g;
+  static SideStream* tab[MAX_DEV] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return nullptr;
+  std::lock_guard<std::mutex> lock(g);
+  if (!tab[dev]) {
+    SideStream* ss = new SideStream;
+    ss->ok = hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) == hipSuccess &&
+             hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) == hipSuccess;
+    tab[dev] = ss;
+  }
+  return tab[dev]->ok ? tab[dev] : nullptr;
+}
+
 }  // namespace
 
 size_t tuned_attend_workspace(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& full,
@@ -65,43 +98,38 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
   const int H = s->H, W = H * s->d;
   uint16_t* kall = reinterpret_cast<uint16_t*>(ws + L.kall);
   uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
-  nkv_status e;
-  {
-    ProfScope ps("decode", st);
-    if ((e = launch_decode_tuned(kb, W, s->r, s->group, full, kall, 0, false, st))) return e;
-    if ((e = launch_decode_tuned(vb, W, s->r, s->group, full, vt, L.nk_pad, true, st))) return e;
-  }
-  {
-    ProfScope ps("stage_current", st);
-    if ((e = launch_stage_current(static_cast<const uint16_t*>(cur_k),
-                                  static_cast<const uint16_t*>(cur_v), N_cur,
-                                  L.nk_pad - full.total, W, kall, vt, L.nk_pad, full.total, st)))
-      return e;
-  }
   const uint16_t* qb = static_cast<const uint16_t*>(q);
   float* of = reinterpret_cast<float*>(ws + L.o_full);
   float* lf = reinterpret_cast<float*>(ws + L.lse_full);
-  if (low.total == 0) {
-    if (L.fsplit == 1) {
-      ProfScope ps("flash", st);
-      return launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, false, out, lse, 1, st);
+  // decoded history + current chunk, then flash attention over them
+  auto full_part = [&](bool to_out, hipStream_t fs) -> nkv_status {
+    nkv_status e;
+    {
+      ProfScope ps("decode", fs);
+      if ((e = launch_decode_tuned(kb, W, s->r, s->group, full, kall, 0, false, fs))) return e;
+      if ((e = launch_decode_tuned(vb, W, s->r, s->group, full, vt, L.nk_pad, true, fs))) return e;
     }
     {
-      ProfScope ps("flash", st);
-      if ((e = launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, L.fsplit, st)))
+      ProfScope ps("stage_current", fs);
+      if ((e = launch_stage_current(static_cast<const uint16_t*>(cur_k),
+                                    static_cast<const uint16_t*>(cur_v), N_cur,
+                                    L.nk_pad - full.total, W, kall, vt, L.nk_pad, full.total, fs)))
         return e;
     }
+    ProfScope ps("flash", fs);
+    if (to_out) return launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, false, out, lse, 1, fs);
+    return launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, L.fsplit, fs);
+  };
+  nkv_status e;
+  if (low.total == 0) {
+    if (L.fsplit == 1) return full_part(true, st);
+    if ((e = full_part(false, st))) return e;
     ProfScope ps("merge", st);
     return launch_lse_merge_parts(Nq, H, s->d, L.fsplit, of, lf, nullptr, nullptr, out, NKV_BF16,
                                   lse, st);
   }
   float* ol = reinterpret_cast<float*>(ws + L.o_low);
   float* ll = reinterpret_cast<float*>(ws + L.lse_low);
-  {
-    ProfScope ps("flash", st);
-    if ((e = launch_flash(qb, Nq, H, tau, kall, vt, L.nk, L.nk_pad, true, of, lf, L.fsplit, st)))
-      return e;
-  }
   // heads grouped by width (one group when every head shares r_low), in the
   // order their widths first appear; r_low is the widest
   int widths[NKV_MAX_HEADS];
@@ -119,10 +147,40 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
     groups[g].h[groups[g].n++] = h;
   }
   const int64_t units = low_part_units(Nq, H, r_low, r_low_h, low.total, vb.A);
-  for (int g = 0; g < ng; ++g)
-    if ((e = launch_low(s, kb, vb, mp, low, widths[g], tau, qb, Nq, ol, ll, ws + L.low, r_low,
-                        units, groups[g], g == 0, st)))
-      return e;
+  auto low_part = [&]() -> nkv_status {
+    nkv_status e2;
+    for (int g = 0; g < ng; ++g)
+      if ((e2 = launch_low(s, kb, vb, mp, low, widths[g], tau, qb, Nq, ol, ll, ws + L.low, r_low,
+                           units, groups[g], g == 0, st)))
+        return e2;
+    return NKV_OK;
+  };
+  // With one width group the main pass fills the chip by itself, and running
+  // the full half beside it only moves time between the two; with several
+  // groups the low half is a chain of short passes whose preparation and
+  // last rounds leave the chip idle, which the full half then uses.
+  SideStream* ss = ng > 1 ? side_stream() : nullptr;
+  if (!ss) {
+    if ((e = full_part(false, st)) || (e = low_part())) return e;
+  } else {
+    std::lock_guard<std::mutex> lock(ss->mu);
+    if (hipEventRecord(ss->fork, st) != hipSuccess ||
+        hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
+      set_error("fork onto the side stream failed");
+      return NKV_EHIP;
+    }
+    const nkv_status ef = full_part(false, ss->s);
+    // join even after an error: the caller's stream must not run ahead of
+    // work already queued on the side stream
+    const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess;
+    const nkv_status el = ef ? NKV_OK : low_part();
+    if (!joined || hipStreamWaitEvent(st, ss->join, 0) != hipSuccess) {
+      set_error("join of the side stream failed");
+      return NKV_EHIP;
+    }
+    if (ef) return ef;
+    if (el) return el;
+  }
   ProfScope ps("merge", st);
   return launch_lse_merge_parts(Nq, H, s->d, L.fsplit, of, lf, ol, ll, out, NKV_BF16, lse, st);
 }
