@@ -26,15 +26,24 @@ template <bool OUT_F32>
 __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q, int64_t Nq, int H,
                                                   float c, const uint16_t* __restrict__ K,
                                                   const uint16_t* __restrict__ VT, int64_t Nk,
-                                                  int64_t ld, void* __restrict__ out,
+                                                  int64_t ld, int nsplit, void* __restrict__ out,
                                                   float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][FA_KT * FA_KS];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][128 * FA_VS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
-  const int h = blockIdx.y;
-  const int split = blockIdx.z, nsplit = gridDim.z;  // key-range split (partials merged later)
+  // XCD-aware order: block L runs on XCD L % 8; work unit u (query block
+  // fastest, then head, then key-range split) is given to block
+  // (u % per) * 8 + u / per, so that each XCD's L2 serves the K/V rows of a
+  // few heads instead of slices of all of them
+  const int nqb = (int)((Nq + FA_QB - 1) / FA_QB);
+  const int nunits = nqb * H * nsplit;
+  const int per = (nunits + 7) / 8;
+  const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (u >= nunits) return;  // the whole block, before any barrier
+  const int h = (u / nqb) % H;
+  const int split = u / (nqb * H);  // key-range split (partials merged later)
   const int W = H * 128;
-  const int64_t q0 = (int64_t)blockIdx.x * FA_QB + wave * 32;
+  const int64_t q0 = (int64_t)(u % nqb) * FA_QB + wave * 32;
   const int64_t qrow = q0 + (lane & 31);
   const bool qok = qrow < Nq;
 
@@ -239,11 +248,14 @@ nkv_status launch_flash(const uint16_t* q, int64_t Nq, int H, float tau, const u
                         float* lse, int nsplit, hipStream_t st) {
   if (Nq == 0) return NKV_OK;
   const float c = tau * 1.4426950408889634f;
-  dim3 grid((unsigned)ceil_div(Nq, FA_QB), (unsigned)H, (unsigned)nsplit);
+  const int64_t units = ceil_div(Nq, FA_QB) * H * nsplit;
+  const dim3 grid((unsigned)(ceil_div(units, 8) * 8));
   if (out_f32)
-    hipLaunchKernelGGL(k_flash<true>, grid, dim3(256), 0, st, q, Nq, H, c, kall, vt, Nk, ld, out, lse);
+    hipLaunchKernelGGL(k_flash<true>, grid, dim3(256), 0, st, q, Nq, H, c, kall, vt, Nk, ld, nsplit,
+                       out, lse);
   else
-    hipLaunchKernelGGL(k_flash<false>, grid, dim3(256), 0, st, q, Nq, H, c, kall, vt, Nk, ld, out, lse);
+    hipLaunchKernelGGL(k_flash<false>, grid, dim3(256), 0, st, q, Nq, H, c, kall, vt, Nk, ld, nsplit,
+                       out, lse);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }

@@ -561,8 +561,9 @@ struct MainArgs {
   int64_t Nq;
   int H, A_k, A_v, GK, GV, NB, r_low, ra;
   int gvsplit;  // key-range splits at a^V-range boundaries
+  int nqb, nsplit;  // query blocks and key-range splits (work unit = (query block, head, split))
   float c;
-  HeadSet hs;  // grid row y serves head hs.h[y]; grid z = key-range split
+  HeadSet hs;  // heads of the group
 };
 
 constexpr int RBW = 256;                // query rows per block: 8 waves x 32 rows
@@ -639,17 +640,28 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   // LDS destinations of the tile loads are then computed on the scalar unit
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = a.hs.h[blockIdx.y];
-  const int split = blockIdx.z, nsplit = gridDim.z;
+  // XCD-aware order: the hardware deals consecutive block ids to the 8 XCDs
+  // in turn (block L runs on XCD L % 8), so work unit u -- query block
+  // fastest, then head, then key-range split -- is given to block
+  // (u % per) * 8 + u / per: each XCD runs a contiguous run of units, which
+  // read the same tiles (one split's tile range) at about the same time and
+  // share them in that XCD's L2.
+  const int nunits = a.nqb * a.hs.n * a.nsplit;
+  const int per = (nunits + 7) / 8;
+  const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (u >= nunits) return;  // the whole block, before any barrier
+  const int bx = u % a.nqb, by = (u / a.nqb) % a.hs.n;
+  const int split = u / (a.nqb * a.hs.n), nsplit = a.nsplit;
+  const int h = a.hs.h[by];
   const int W = a.H * 128;
-  const int64_t q0 = (int64_t)blockIdx.x * RBW;
+  const int64_t q0 = (int64_t)bx * RBW;
   const int rloc = wave * 32 + (lane & 31);
   const int64_t qrow = q0 + rloc;
   const bool rok = qrow < a.Nq;
   const bool active = q0 + wave * 32 < a.Nq;  // the wave owns at least one row
   const int64_t grow = (rok ? qrow : q0) * a.H + h;
   // partial-sum row of this (key-range split, query, head of the group)
-  const int64_t prow = ((int64_t)split * a.Nq + (rok ? qrow : q0)) * a.hs.n + blockIdx.y;
+  const int64_t prow = ((int64_t)split * a.Nq + (rok ? qrow : q0)) * a.hs.n + by;
 
   f16x8 qtf[RLP / 16];
 #pragma unroll
@@ -705,7 +717,7 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   // sums as planes only without splits
   const bool planes = nsplit == 1 || a.gvsplit;
   const bool acc_planes = nsplit == 1;
-  const int64_t mrow = a.gvsplit ? ((rok ? qrow : q0) * a.hs.n + blockIdx.y) : prow;
+  const int64_t mrow = a.gvsplit ? ((rok ? qrow : q0) * a.hs.n + by) : prow;
   const int WS = a.GV * CR;
   auto put_hilo = [&](uint16_t* hi, uint16_t* lo, f32x4 v) __attribute__((always_inline)) {
     float l[4];
@@ -992,9 +1004,9 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
 }
 
 template <int RLP>
-nkv_status launch_main(const MainArgs& m, int64_t Nq, int nsplit, hipStream_t st) {
-  dim3 grid((unsigned)ceil_div(Nq, RBW), (unsigned)m.hs.n, (unsigned)nsplit);
-  hipLaunchKernelGGL(k_low_rows<RLP>, grid, dim3(512), 0, st, m);
+nkv_status launch_main(const MainArgs& m, hipStream_t st) {
+  const int64_t units = (int64_t)m.nqb * m.hs.n * m.nsplit;
+  hipLaunchKernelGGL(k_low_rows<RLP>, dim3((unsigned)(ceil_div(units, 8) * 8)), dim3(512), 0, st, m);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }
@@ -1288,16 +1300,16 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   ProfScope ps_main("low_main", st);
   MainArgs m{q, static_cast<const uint16_t*>(kb.centers), qt16, bound, img, tile_start,
              tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.GV, P.NB, r_low, ra,
-             split.gv ? 1 : 0, c, hs};
+             split.gv ? 1 : 0, (int)ceil_div(Nq, RBW), nsplit, c, hs};
   switch (rlp) {
-    case 16: e = launch_main<16>(m, Nq, nsplit, st); break;
-    case 32: e = launch_main<32>(m, Nq, nsplit, st); break;
-    case 48: e = launch_main<48>(m, Nq, nsplit, st); break;
-    case 64: e = launch_main<64>(m, Nq, nsplit, st); break;
-    case 80: e = launch_main<80>(m, Nq, nsplit, st); break;
-    case 96: e = launch_main<96>(m, Nq, nsplit, st); break;
-    case 112: e = launch_main<112>(m, Nq, nsplit, st); break;
-    case 128: e = launch_main<128>(m, Nq, nsplit, st); break;
+    case 16: e = launch_main<16>(m, st); break;
+    case 32: e = launch_main<32>(m, st); break;
+    case 48: e = launch_main<48>(m, st); break;
+    case 64: e = launch_main<64>(m, st); break;
+    case 80: e = launch_main<80>(m, st); break;
+    case 96: e = launch_main<96>(m, st); break;
+    case 112: e = launch_main<112>(m, st); break;
+    case 128: e = launch_main<128>(m, st); break;
     default: set_error("tuned low-dimensional read supports r_low <= 128"); return NKV_EUNSUPPORTED;
   }
   if (e) return e;
