@@ -688,6 +688,15 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       a.gvsplit ? a.tile_start[g1 * a.GK] : (int)((int64_t)ntiles * (split + 1) / nsplit));
   const char* sTrow = reinterpret_cast<const char*>(sT + rloc * TS);
   const uint16_t* qsrc = a.q + (rok ? qrow : q0) * W + h * 128 + 8 * hl;
+  // the wave's q row fragments for the T slices: loaded once and kept in
+  // registers up to r_low 96 (a bucket start then needs no q reload);
+  // wider coefficient rows leave no room and reload them per bucket
+  constexpr bool QRES = RLP <= 96;
+  bf16x8 qres[QRES ? 8 : 1];
+  if constexpr (QRES) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qres[ks] = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
+  }
 
   // mu^K rows of the 64-center slice gk for this head
   auto load_mu = [&](int gk) __attribute__((always_inline)) {
@@ -795,7 +804,9 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   auto t_slice = [&](int gk) __attribute__((always_inline)) {
     bf16x8 qv[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qv[ks] = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
+    for (int ks = 0; ks < 8; ++ks)
+      if constexpr (QRES) qv[ks] = qres[ks];
+      else qv[ks] = as_bf16x8(ld_u32x4(qsrc + 16 * ks));
     // two center blocks: independent accumulation chains, interleaved.  The
     // lane's LDS offsets are derived here from an opaque copy of the lane
     // index: hoisted out of the tile loop they would hold 64 registers for
@@ -882,16 +893,6 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
         for (int u = 0; u < 4; ++u) acc[4 * g + u] = *reinterpret_cast<const float*>(sTrow + kov[u]);
       }
     };
-    auto read_k = [&](int kb, f16x8 (&ck)[RLP / 16]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int ks = 0; ks < RLP / 16; ++ks)
-        ck[ks] = as_f16x8(*reinterpret_cast<const u32x4*>(
-            cur + (kb * G.nks + ks) * 1024 + lane * 16));
-    };
-    auto score = [&](f32x16& acc, const f16x8 (&ck)[RLP / 16]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int ks = 0; ks < RLP / 16; ++ks) acc = mfma_f16(ck[ks], qtf[ks], acc);
-    };
     auto read_v = [&](int kb, int j, bf16x8 (&vo)[NPB + 2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < NPB + 2; ++db)
@@ -923,31 +924,42 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       if (m & 1u) accW[0] = mfma_bf16(vo[NPB], p, accW[0]);
       if (m & 2u) accW[1] = mfma_bf16(vo[NPB + 1], p, accW[1]);
     };
-    // wide coefficient rows: one K operand set, reloaded for the second half
-    constexpr bool KDB = RLP <= 96;
+    // K operands in two batches of k-steps (both key halves each), the
+    // second read while the first batch's MFMAs run
+    constexpr int NKS = RLP / 16, HB = (NKS + 1) / 2;
     f32x16 s0, s1;
-    f16x8 ck0[RLP / 16], ck1[KDB ? RLP / 16 : 1];
+    f16x8 c0[HB], c1[HB];
     bf16x8 va[NPB + 2], vb[NPB + 2];
+    auto read_kb = [&](int ks0, int n) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < HB; ++i)
+        if (i < n) {
+          c0[i] = as_f16x8(*reinterpret_cast<const u32x4*>(cur + (ks0 + i) * 1024 + lane * 16));
+          c1[i] = as_f16x8(
+              *reinterpret_cast<const u32x4*>(cur + (G.nks + ks0 + i) * 1024 + lane * 16));
+        }
+    };
+    auto score_kb = [&](int ks0, int n) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < HB; ++i)
+        if (i < n) {
+          s0 = mfma_f16(c0[i], qtf[ks0 + i], s0);
+          s1 = mfma_f16(c1[i], qtf[ks0 + i], s1);
+        }
+    };
     gather(0, s0);
     gather(1, s1);
-    read_k(0, ck0);
-    if constexpr (KDB) read_k(1, ck1);
+    read_kb(0, HB);
     dma(t + 1, nxt, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // S^T = T + (c q~) . c^K for both key halves (fp16 MFMA)
-    if constexpr (KDB) {
-      // two independent accumulation chains, interleaved
-#pragma unroll
-      for (int ks = 0; ks < RLP / 16; ++ks) {
-        s0 = mfma_f16(ck0[ks], qtf[ks], s0);
-        s1 = mfma_f16(ck1[ks], qtf[ks], s1);
-      }
-    } else {
-      score(s0, ck0);
+    // S^T = T + (c q~) . c^K for both key halves (fp16 MFMA): two independent
+    // accumulation chains, interleaved
+    score_kb(0, HB);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NKS > HB) {
+      read_kb(HB, NKS - HB);
       __builtin_amdgcn_sched_barrier(0);
-      read_k(1, ck0);
-      __builtin_amdgcn_sched_barrier(0);
-      score(s1, ck0);
+      score_kb(HB, NKS - HB);
     }
     read_v(0, 0, va);
     dma(t + 1, nxt, 1);
