@@ -9,18 +9,33 @@
 // bf16 (per-head transposed so PV operands are contiguous along keys).
 // Keys beyond Nk up to the 64-key padding are zero and masked.
 //
-// Block = 4 waves x 32 queries of one head; each tile of 64 keys is staged
-// through double-buffered LDS.  Per wave and tile: S^T = K Q^T is 2 x 8
-// MFMA 32x32x16 (lane = query column, 32 keys per lane), O^T += V^T P^T is
-// 4 x 4 MFMAs whose B operand is the wave's own P in registers.
+// Block = 4 waves x 32 queries of one head; each tile of 64 keys moves from
+// HBM/L2 into double-buffered LDS with direct-to-LDS loads (1 KiB per wave
+// instruction, no registers, no LDS stores).  Per wave and tile: S^T = K Q^T
+// is 2 x 8 MFMA 32x32x16 (lane = query column, 32 keys per lane), O^T +=
+// V^T P^T is 4 x 4 MFMAs whose B operand is the wave's own P in registers.
+//
+// LDS layouts (both conflict-free for the MFMA operand reads):
+//  * K tile: 64 rows of 256 bytes; 16-byte block j of key row r is stored at
+//    block j ^ (r & 15).
+//  * V^T tile: 128 rows (dims) of 128 bytes (64 keys); block j of dim row r
+//    is stored at block j ^ ((r >> 1) & 7).
+// The S MFMA takes its 32 key rows in the order r -> r with bits 2 and 3
+// swapped, so that each lane's P values for a 16-key step are 8 consecutive
+// keys: the PV A operand is then one 16-byte read per lane.
 #include <cmath>
 
 #include "tuned_internal.hpp"
 
 namespace nkv {
 
-constexpr int FA_KS = 136;  // LDS row stride of the K tile (128 + 8 bf16)
-constexpr int FA_VS = 68;   // LDS row stride of the V^T tile (64 + 4 bf16)
+constexpr int FA_KB = FA_KT * 256;  // bytes of a K tile (64 keys x 128 bf16)
+constexpr int FA_VB = 128 * FA_KT * 2;  // bytes of a V^T tile (128 dims x 64 keys)
+
+// key row of MFMA output row i within a 32-key block: bits 2 and 3 swapped
+__device__ __forceinline__ int fa_key_of_row(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q, int64_t Nq, int H,
@@ -28,9 +43,13 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
                                                   const uint16_t* __restrict__ VT, int64_t Nk,
                                                   int64_t ld, int nsplit, void* __restrict__ out,
                                                   float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][FA_KT * FA_KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][128 * FA_VS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+  // one array per stage and operand: the stage of every LDS access is static
+  __shared__ __attribute__((aligned(1024))) char sK0[FA_KB];
+  __shared__ __attribute__((aligned(1024))) char sK1[FA_KB];
+  __shared__ __attribute__((aligned(1024))) char sV0[FA_VB];
+  __shared__ __attribute__((aligned(1024))) char sV1[FA_VB];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware order: block L runs on XCD L % 8; work unit u (query block
   // fastest, then head, then key-range split) is given to block
   // (u % per) * 8 + u / per, so that each XCD's L2 serves the K/V rows of a
@@ -60,37 +79,38 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
 
   const int64_t ntiles_all = (Nk + FA_KT - 1) / FA_KT;
   const int64_t t_beg = ntiles_all * split / nsplit, t_end = ntiles_all * (split + 1) / nsplit;
-  u32x4 rk[4], rv[4];
-  auto fetch = [&](int64_t t0) {
+  // this wave's 8 of the 32 1-KiB chunks of tile t: K chunks 0..15 (16 key
+  // rows each), V^T chunks 16..31 (8 dim rows each), each lane one 16-byte
+  // block of the swizzled layout
+  const char* kbase = reinterpret_cast<const char*>(K + h * 128);
+  const char* vbase = reinterpret_cast<const char*>(VT + (int64_t)h * 128 * ld);
+  auto dma = [&](int64_t t, char* dk, char* dv) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int cidx = tid + 256 * j;
-      const int kr = cidx >> 4, kc = (cidx & 15) * 8;
-      rk[j] = ld_u32x4(K + (t0 + kr) * W + h * 128 + kc);
-      const int vd = cidx >> 3, vc = (cidx & 7) * 8;
-      rv[j] = ld_u32x4(VT + ((int64_t)h * 128 + vd) * ld + t0 + vc);
+      const int ch = wave + 4 * j;  // K chunk
+      const int s = ch * 64 + lane, r = s >> 4, blk = (s & 15) ^ (r & 15);
+      uint32_t off = (uint32_t)(r * W * 2 + blk * 16);
+      asm volatile("" : "+v"(off));
+      __builtin_amdgcn_global_load_lds(kbase + t * FA_KT * W * 2 + off,
+                                       (__attribute__((address_space(3))) void*)(dk + ch * 1024),
+                                       16, 0, 0);
     }
-  };
-  auto stash = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int cidx = tid + 256 * j;
-      const int kr = cidx >> 4, kc = (cidx & 15) * 8;
-      *reinterpret_cast<u32x4*>(&sK[buf][kr * FA_KS + kc]) = rk[j];
-      const int vd = cidx >> 3, vc = (cidx & 7) * 8;
-      *reinterpret_cast<u32x2*>(&sV[buf][vd * FA_VS + vc]) = u32x2{rv[j][0], rv[j][1]};
-      *reinterpret_cast<u32x2*>(&sV[buf][vd * FA_VS + vc + 4]) = u32x2{rv[j][2], rv[j][3]};
+      const int ch = wave + 4 * j;  // V^T chunk
+      const int s = ch * 64 + lane, r = s >> 3, blk = (s & 7) ^ ((r >> 1) & 7);
+      uint32_t off = (uint32_t)(r * ld * 2 + blk * 16);
+      asm volatile("" : "+v"(off));
+      __builtin_amdgcn_global_load_lds(vbase + t * FA_KT * 2 + off,
+                                       (__attribute__((address_space(3))) void*)(dv + ch * 1024),
+                                       16, 0, 0);
     }
   };
 
-  if (t_beg < t_end) {
-    fetch(t_beg * FA_KT);
-    stash(0);
-  }
-  __syncthreads();
-  for (int64_t tile = t_beg; tile < t_end; ++tile) {
-    const int buf = (int)((tile - t_beg) & 1);
-    if (tile + 1 < t_end) fetch((tile + 1) * FA_KT);
+  const int krow = fa_key_of_row(lane & 31);  // this lane's key row in a 32-key block
+  auto body = [&](int64_t tile, const char* cK, const char* cV, char* nK, char* nV)
+      __attribute__((always_inline)) {
+    if (tile + 1 < t_end) dma(tile + 1, nK, nV);
     // ---- S^T = K Q^T: K fragments read four k-steps ahead of their MFMAs ----
     // (sched_barrier keeps each batch of reads ahead of the MFMAs using it)
     f32x16 s[2] = {zero16(), zero16()};
@@ -98,17 +118,16 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          kf[kb][u] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              &sK[buf][(kb * 32 + (lane & 31)) * FA_KS + 16 * (ks0 + u) + 8 * hl]));
+        for (int uu = 0; uu < 4; ++uu) {
+          const int r = kb * 32 + krow, j = 2 * (ks0 + uu) + hl;
+          kf[kb][uu] = as_bf16x8(*reinterpret_cast<const u32x4*>(cK + r * 256 + ((j ^ (r & 15)) << 4)));
+        }
     };
     auto read_v4 = [&](int j, bf16x8 (&vf)[4]) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint16_t* vrow = &sV[buf][(db * 32 + (lane & 31)) * FA_VS + 16 * j + 4 * hl];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        vf[db] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        const int r = db * 32 + (lane & 31), b = 2 * j + hl;
+        vf[db] = as_bf16x8(*reinterpret_cast<const u32x4*>(cV + r * 128 + ((b ^ ((r >> 1) & 7)) << 4)));
       }
     };
     {
@@ -117,14 +136,14 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
       __builtin_amdgcn_sched_barrier(0);
       read_k4(4, k1);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int uu = 0; uu < 4; ++uu)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(k0[kb][u], qf[u], s[kb]);
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(k0[kb][uu], qf[uu], s[kb]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int uu = 0; uu < 4; ++uu)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(k1[kb][u], qf[4 + u], s[kb]);
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(k1[kb][uu], qf[4 + uu], s[kb]);
     }
     bf16x8 va[4], vb[4];
     read_v4(0, va);
@@ -134,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (tile * FA_KT + kb * 32 + acc_row(e, lane) >= Nk) s[kb][e] = -INFINITY;
+          if (tile * FA_KT + kb * 32 + fa_key_of_row(acc_row(e, lane)) >= Nk) s[kb][e] = -INFINITY;
     }
     // ---- online softmax (base 2, lazy rescale) ----------------------------
     float mt = -INFINITY;
@@ -152,17 +171,17 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       m_run = mt;
     }
-    // P for 16 keys (step j: key block j/2, half j%2), packed to bf16 in the
-    // key order of the B operand
+    // P for 16 keys (step j: key block j/2, half j%2), packed to bf16: the
+    // elements 8 (j%2) .. +7 of the lane are the keys 16 j + 8 (lane/32) + 0..7
     auto probs = [&](int j) __attribute__((always_inline)) {
       const int kb = j >> 1, half = j & 1;
       u32x4 pk;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * u], c, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * u + 1], c, -m_run));
+      for (int uu = 0; uu < 4; ++uu) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * uu], c, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * uu + 1], c, -m_run));
         l_part += p0 + p1;
-        pk[u] = pack_bf16x2(p0, p1);
+        pk[uu] = pack_bf16x2(p0, p1);
       }
       return as_bf16x8(pk);
     };
@@ -187,10 +206,20 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(vb[db], p, o[db]);
-    if (tile + 1 < t_end) {
-      stash(buf ^ 1);
-      __syncthreads();
-    }
+    // tile + 1 has landed (this wave's share) and every wave is done with
+    // this stage before it is loaded again
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if (t_beg < t_end) {
+    dma(t_beg, sK0, sV0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  for (int64_t tile = t_beg; tile < t_end; tile += 2) {
+    body(tile, sK0, sV0, sK1, sV1);
+    if (tile + 1 < t_end) body(tile + 1, sK1, sV1, sK0, sV0);
   }
   // ---- epilogue -------------------------------------------------------------
   const float l = l_part + __shfl_xor(l_part, 32, 64);
