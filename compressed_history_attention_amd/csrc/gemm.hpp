@@ -88,11 +88,163 @@ __global__ __launch_bounds__(256) void k_gemm(const P p) {
   p.epilogue(z, m_blk + wm, n_blk + wn, lane, acc);
 }
 
+// The same tile (128 x 128, 4 waves of 64 x 64) for problems whose operands
+// are plain bf16 rows: K % 32 == 0 and P supplies
+//   __device__ const uint16_t* a_ptr(int z, int m, int k) const;  // &A[z](m, k), 8-aligned k
+//   __device__ const uint16_t* b_ptr(int z, int n, int k) const;  // &B[z](n, k)
+// (rows m < M, n < N; a k step of 32 never crosses a change of source).
+// K steps of 32 move by direct-to-LDS loads (1 KiB per wave instruction,
+// no staging registers) through a ring of 4 stages, three steps ahead of the
+// MFMAs.  Within a stage each operand is 128 rows of 64 bytes; 16-byte block
+// j of row r sits at block j ^ ((r >> 2) & 3), so the 32 rows an MFMA
+// operand read touches spread over all banks.  Rows past M or N load row
+// M - 1 or N - 1 (finite values whose products only reach discarded
+// outputs).
+constexpr int GD_BK = 32, GD_STAGES = 4;
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; all-ones = no wait on that counter)
+constexpr int GD_WAIT_VM8 = 8 | (7 << 4) | (15 << 8);           // vmcnt(8)
+constexpr int GD_WAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0)
+constexpr int GD_OP = 128 * GD_BK * 2;  // bytes of one operand tile per stage
+
+// Lane state of the direct-to-LDS loads: chunk c = wave + 4 j (j < 2) of
+// each operand holds slots 64 c .. 64 c + 63 of a stage, slot s = row 4 r +
+// physical block; the lane loads row r of that chunk, logical k block kblk.
+struct GdLanes {
+  int wave, arow[2], brow[2], kblk[2];
+};
+
+// stage kt into dS (A tile at offset 0, B tile at GD_OP); stages past the
+// end reload the last one (the ring then issues the same loads on every
+// path, which lets the compiler's own waits match the counts in k_gemm_dma;
+// their data is never read)
+template <class P>
+__device__ __forceinline__ void gd_load(const P& p, int z, const GdLanes& L, int kt, int nk,
+                                        char* dS) {
+  const int k0 = min(kt, nk - 1) * GD_BK;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = L.wave + 4 * j;
+    // (sources as plain pointers: a builtin call whose arguments depend on
+    // P would be rejected by the host pass of this template)
+    const void* sa = p.a_ptr(z, L.arow[j], k0 + 8 * L.kblk[j]);
+    const void* sb = p.b_ptr(z, L.brow[j], k0 + 8 * L.kblk[j]);
+    __builtin_amdgcn_global_load_lds(sa, (__attribute__((address_space(3))) void*)(dS + c * 1024),
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        sb, (__attribute__((address_space(3))) void*)(dS + GD_OP + c * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 gd_frag(const char* base, int r, int b) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(base + r * 64 + ((b ^ ((r >> 2) & 3)) << 4)));
+}
+
+// step kt: wait for stage kt (cS), load stage kt + 3 into nS, then the MFMAs
+// of stage kt into the wave's 64 x 64 quadrant (wm, wn)
+template <class P>
+__device__ __forceinline__ void gd_step(const P& p, int z, const GdLanes& L, int lane, int wm,
+                                        int wn, int kt, int nk, const char* cS, char* nS,
+                                        f32x16 (&acc)[2][2]) {
+  const char* cA = cS;
+  const char* cB = cS + GD_OP;
+  const int hl = lane >> 5;
+  // stage kt has landed once at most the two newer stages' loads (4 per
+  // stage per wave) are outstanding (the builtin, unlike inline asm, is seen
+  // by the compiler's own wait placement, which then adds none before the
+  // reads below) ...
+  __builtin_amdgcn_s_waitcnt(GD_WAIT_VM8);
+  // ... in every wave, and every wave's reads of stage kt - 1 (the one
+  // loaded next) have returned.  A bare barrier: the fence of __syncthreads
+  // would wait for every load in flight
+  __builtin_amdgcn_s_waitcnt(GD_WAIT_LGKM0);
+  __builtin_amdgcn_s_barrier();
+  // this stage's operand fragments first, then the loads into the ring (kept
+  // in this order, so that the compiler's count before the reads is exact)
+  bf16x8 fa[GD_BK / 16][2], fb[GD_BK / 16][2];
+#pragma unroll
+  for (int ks = 0; ks < GD_BK / 16; ++ks)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      fa[ks][i] = gd_frag(cA, wm + 32 * i + (lane & 31), 2 * ks + hl);
+      fb[ks][i] = gd_frag(cB, wn + 32 * i + (lane & 31), 2 * ks + hl);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  gd_load(p, z, L, kt + GD_STAGES - 1, nk, nS);
+  __builtin_amdgcn_sched_barrier(0);
+  // steps past the end multiply zeros (no branch around the MFMAs: the same
+  // straight line on every path)
+  const bool live = kt < nk;
+#pragma unroll
+  for (int ks = 0; ks < GD_BK / 16; ++ks) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (!live) fa[ks][i] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fa[ks][i], fb[ks][j], acc[i][j]);
+  }
+}
+
+template <class P>
+__global__ __launch_bounds__(256) void k_gemm_dma(const P p) {
+  // one array per stage: the stage of every LDS access is static (the loop
+  // below is unrolled by the ring size), so the compiler can see that
+  // reading one stage does not alias the loads in flight into another
+  __shared__ __attribute__((aligned(1024))) char s0[2 * GD_OP];
+  __shared__ __attribute__((aligned(1024))) char s1[2 * GD_OP];
+  __shared__ __attribute__((aligned(1024))) char s2[2 * GD_OP];
+  __shared__ __attribute__((aligned(1024))) char s3[2 * GD_OP];
+  static_assert(GD_STAGES == 4, "ring of four stages");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int z = blockIdx.z;
+  const int m_blk = blockIdx.y * GEMM_BM, n_blk = blockIdx.x * GEMM_BN;
+  const int nk = p.K / GD_BK;  // >= 1
+  GdLanes L;
+  L.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sl = (L.wave + 4 * j) * 64 + lane, r = sl >> 2;
+    L.kblk[j] = (sl & 3) ^ ((r >> 2) & 3);
+    L.arow[j] = min(m_blk + r, p.M - 1);
+    L.brow[j] = min(n_blk + r, p.N - 1);
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+  const int wm = (L.wave >> 1) * 64, wn = (L.wave & 1) * 64;
+  gd_load(p, z, L, 0, nk, s0);
+  gd_load(p, z, L, 1, nk, s1);
+  gd_load(p, z, L, 2, nk, s2);
+  for (int kt = 0; kt < nk; kt += 4) {
+    gd_step(p, z, L, lane, wm, wn, kt, nk, s0, s3, acc);
+    gd_step(p, z, L, lane, wm, wn, kt + 1, nk, s1, s0, acc);
+    gd_step(p, z, L, lane, wm, wn, kt + 2, nk, s2, s1, acc);
+    gd_step(p, z, L, lane, wm, wn, kt + 3, nk, s3, s2, acc);
+  }
+  // no load may still be in flight into LDS when the block ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  p.epilogue(z, m_blk + wm, n_blk + wn, lane, acc);
+}
+
 template <class P>
 inline nkv_status launch_gemm(const P& p, int batch, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || batch <= 0) return NKV_OK;
   dim3 grid((unsigned)ceil_div(p.N, GEMM_BN), (unsigned)ceil_div(p.M, GEMM_BM), (unsigned)batch);
   hipLaunchKernelGGL(k_gemm<P>, grid, dim3(256), 0, s, p);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
+template <class P>
+inline nkv_status launch_gemm_dma(const P& p, int batch, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0 || batch <= 0) return NKV_OK;
+  if (p.K < GD_BK || p.K % GD_BK != 0) return launch_gemm(p, batch, s);
+  dim3 grid((unsigned)ceil_div(p.N, GEMM_BN), (unsigned)ceil_div(p.M, GEMM_BM), (unsigned)batch);
+  hipLaunchKernelGGL(k_gemm_dma<P>, grid, dim3(256), 0, s, p);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }

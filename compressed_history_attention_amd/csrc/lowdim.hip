@@ -392,6 +392,15 @@ struct QtProblem {
     if (n >= N) return u32x4{0u, 0u, 0u, 0u};
     return ld_u32x4(dkt + (int64_t)n * H * 128 + hs.h[z] * 128 + k);
   }
+  __device__ const uint16_t* a_ptr(int z, int m, int k) const {
+    return q + (int64_t)m * H * 128 + hs.h[z] * 128 + k;
+  }
+  __device__ const uint16_t* b_ptr(int z, int n, int k) const {
+    return dkt + (int64_t)n * H * 128 + hs.h[z] * 128 + k;
+  }
+  bool dma_ok() const {
+    return ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(dkt)) & 15) == 0;
+  }
   __device__ void epilogue(int zb, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
     const int z = hs.h[zb];
 #pragma unroll
@@ -1002,13 +1011,13 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
         const int dim = db * 32 + e4 * 8 + hl * 4;  // r_low % 16 == 0: whole f32x4 or none
         const f32x4 v{accT[db][4 * e4], accT[db][4 * e4 + 1], accT[db][4 * e4 + 2],
                       accT[db][4 * e4 + 3]};
-        if (dim < a.r_low) {
-          if (acc_planes) {
-            uint16_t* row = reinterpret_cast<uint16_t*>(a.acc) + prow * 2 * a.ra;
-            put_hilo(row + dim, row + a.ra + dim, v);
-          } else {
-            *reinterpret_cast<f32x4*>(a.acc + prow * a.r_low + dim) = v;
-          }
+        if (acc_planes) {
+          // every dim < ra: past r_low the V rows are zero, and so are these
+          // sums (the restoration reads whole planes)
+          uint16_t* row = reinterpret_cast<uint16_t*>(a.acc) + prow * 2 * a.ra;
+          put_hilo(row + dim, row + a.ra + dim, v);
+        } else if (dim < a.r_low) {
+          *reinterpret_cast<f32x4*>(a.acc + prow * a.r_low + dim) = v;
         }
       }
     if (hl == 0) a.ell[prow] = lsum;
@@ -1026,20 +1035,21 @@ nkv_status launch_main(const MainArgs& m, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Split coefficient sums -> one bf16 hi/lo plane row each (and ell summed),
 // in split order: rows = (query, head of the group); one thread per four
-// coefficients of a row (r_low % 16 == 0).
+// plane columns of a row (r_low % 16 == 0; zeros in [r_low, ra)).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_reduce_acc(const float* __restrict__ acc,
                                                     const float* __restrict__ ell, int64_t rows,
                                                     int nsplit, int r_low, int ra,
                                                     uint16_t* __restrict__ racc,
                                                     float* __restrict__ rell) {
-  const int per = r_low / 4;
+  const int per = ra / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * per) return;
   const int64_t row = i / per;
   const int c = (int)(i - row * per) * 4;
-  f32x4 v = *reinterpret_cast<const f32x4*>(acc + row * r_low + c);
-  for (int sp = 1; sp < nsplit; ++sp) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (c < r_low) v = *reinterpret_cast<const f32x4*>(acc + row * r_low + c);
+  for (int sp = 1; sp < nsplit && c < r_low; ++sp) {
     const f32x4 w = *reinterpret_cast<const f32x4*>(acc + ((int64_t)sp * rows + row) * r_low + c);
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] += w[u];
@@ -1141,6 +1151,30 @@ struct RestoreProblem {
     const int kk = k - 2 * ra;
     const int c = kk >= av ? kk - av : kk;
     return ld_u32x4(mvt + ch * av + c);
+  }
+  // direct-to-LDS operand rows (mass planes only): the same values as
+  // load_a / load_b, except that past r_low the A planes hold zeros and B
+  // any finite decoder value of the same row
+  __device__ const uint16_t* a_ptr(int zb, int m, int k) const {
+    const int64_t pr = prow(0, m, zb);
+    if (k < 2 * ra) return reinterpret_cast<const uint16_t*>(acc) + pr * 2 * ra + k;
+    const int kk = k - 2 * ra;
+    return reinterpret_cast<const uint16_t*>(wmass) + pr * 2 * WS + (kk >= av ? kk - av + WS : kk);
+  }
+  __device__ const uint16_t* b_ptr(int zb, int n, int k) const {
+    const int64_t ch = (int64_t)hs.h[zb] * 128 + n;
+    if (k < 2 * ra) {
+      const int j = k >= ra ? k - ra : k;
+      return dv + ch * ldv + min(j, ldv - 8);
+    }
+    const int kk = k - 2 * ra;
+    return mvt + ch * av + (kk >= av ? kk - av : kk);
+  }
+  bool dma_ok() const {
+    const uintptr_t al = reinterpret_cast<uintptr_t>(acc) | reinterpret_cast<uintptr_t>(wmass) |
+                         reinterpret_cast<uintptr_t>(dv) | reinterpret_cast<uintptr_t>(mvt);
+    return mass_planes != 0 && (al & 15) == 0 && ldv % 8 == 0 && ldv >= 8 && ra % 8 == 0 &&
+           WS % 8 == 0 && av % 8 == 0;
   }
   __device__ void epilogue(int zb, int m0, int n0, int lane, const f32x16 (&accv)[2][2]) const {
     const int z = hs.h[zb];
@@ -1297,7 +1331,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   ProfScope ps_q("low_prep_query", st);
   // query reduction and per-row score bounds
   QtProblem qp{(int)Nq, r_low, 128, H, q, dkt, qt32, hs};
-  if ((e = launch_gemm(qp, hs.n, st))) return e;
+  if ((e = qp.dma_ok() ? launch_gemm_dma(qp, hs.n, st) : launch_gemm(qp, hs.n, st))) return e;
   hipLaunchKernelGGL(k_center_max, dim3((unsigned)ceil_div(Nq, CM_Q), (unsigned)hs.n), dim3(256),
                      0, st, q, static_cast<const uint16_t*>(kb.centers), present, Nq, H, kb.A, hs,
                      tmax);
@@ -1333,7 +1367,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   const float* ell_r = ell;
   if (nsplit > 1) {
     const int64_t rows_g = Nq * hs.n;
-    hipLaunchKernelGGL(k_reduce_acc, dim3((unsigned)ceil_div(rows_g * (r_low / 4), 256)), dim3(256),
+    hipLaunchKernelGGL(k_reduce_acc, dim3((unsigned)ceil_div(rows_g * (ra / 4), 256)), dim3(256),
                        0, st, acc, ell, rows_g, nsplit, r_low, ra,
                        reinterpret_cast<uint16_t*>(at(P.racc)),
                        reinterpret_cast<float*>(at(P.rell)));
@@ -1344,7 +1378,7 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, mp.ld, r_low, ra, vb.A, P.av, nsplit,
                     P.GV * CR, (nsplit == 1 || split.gv) ? 1 : 0, acc_r, wmass,
                     static_cast<const uint16_t*>(mp.omap), mvt, ell_r, bound, o_low, lse_low, hs};
-  if ((e = launch_gemm(rp, hs.n, st))) return e;
+  if ((e = rp.dma_ok() ? launch_gemm_dma(rp, hs.n, st) : launch_gemm(rp, hs.n, st))) return e;
   }
   // rows whose bound may be loose: exact generic recomputation
   ProfScope ps_fallback("low_fallback", st);
