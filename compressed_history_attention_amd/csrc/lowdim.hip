@@ -37,7 +37,7 @@ namespace {
 constexpr int NT = 64;        // keys per tile (bucket padding unit)
 constexpr int CR = 64;        // centers per range
 constexpr int TS = 65;        // LDS row stride of the center tables (64 + sentinel)
-constexpr int CHUNK = 1024;   // tokens per counting chunk
+constexpr int CHUNK = 256;    // tokens per counting chunk
 constexpr float BOUND_GAP_LIMIT = 60.f;  // log2 units
 
 // Tile image: the exact LDS layout the main kernel consumes, so a tile moves
@@ -190,53 +190,89 @@ __global__ __launch_bounds__(256) void k_bucket_count(BranchArgs kb, BranchArgs 
   for (int b = threadIdx.x; b < 2 * NB; b += 256) cnt[(int64_t)blockIdx.x * 2 * NB + b] = lc[b];
 }
 
-// one block: bucket totals, padded tile ranges, per-chunk bases of the
-// sub-buckets (a bucket's lower-half tokens first), tile->bucket
-__global__ __launch_bounds__(1024) void k_bucket_scan(const int32_t* __restrict__ cnt, int nchunk,
-                                                      int NB, int32_t* __restrict__ base,
-                                                      int32_t* __restrict__ tile_start,
-                                                      int32_t* __restrict__ bcount,
-                                                      int32_t* __restrict__ tile_bucket) {
-  extern __shared__ int sh[];   // NB tiles per bucket, then 1024 partial sums
-  int* ntile = sh;
-  int* part = sh + NB;
-  const int tid = threadIdx.x;
-  for (int b = tid; b < NB; b += 1024) {
-    int tot = 0;
-    for (int c = 0; c < nchunk; ++c)
-      tot += cnt[(int64_t)c * 2 * NB + 2 * b] + cnt[(int64_t)c * 2 * NB + 2 * b + 1];
-    bcount[b] = tot;
-    ntile[b] = (tot + NT - 1) / NT;
-  }
+// Bucket totals and tile counts: one block per bucket sums its two
+// sub-buckets' per-chunk counts.
+__global__ __launch_bounds__(256) void k_bucket_tot(const int32_t* __restrict__ cnt, int nchunk,
+                                                    int NB, int32_t* __restrict__ bcount,
+                                                    int32_t* __restrict__ ntile) {
+  __shared__ int red[256];
+  const int b = blockIdx.x;
+  int t = 0;
+  for (int c = threadIdx.x; c < nchunk; c += 256)
+    t += cnt[(int64_t)c * 2 * NB + 2 * b] + cnt[(int64_t)c * 2 * NB + 2 * b + 1];
+  red[threadIdx.x] = t;
   __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    bcount[b] = red[0];
+    ntile[b] = (red[0] + NT - 1) / NT;
+  }
+}
+
+// one block of 1024 threads: exclusive prefix sums of the tile counts
+// (padded tile ranges of the buckets, total at tile_start[NB]) and the
+// tile -> bucket table
+__global__ __launch_bounds__(1024) void k_bucket_tiles(const int32_t* __restrict__ ntile, int NB,
+                                                       int32_t* __restrict__ tile_start,
+                                                       int32_t* __restrict__ tile_bucket) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
   const int per = (NB + 1023) / 1024;
   const int lo = tid * per, hi = min(NB, lo + per);
   int sum = 0;
   for (int b = lo; b < hi; ++b) sum += ntile[b];
   part[tid] = sum;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < 1024; ++i) {
-      const int v = part[i];
-      part[i] = run;
-      run += v;
-    }
-    tile_start[NB] = run;
+  for (int st = 1; st < 1024; st <<= 1) {  // Hillis-Steele inclusive scan
+    const int v = tid >= st ? part[tid - st] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
   }
-  __syncthreads();
-  int run = part[tid];
+  int run = part[tid] - sum;
   for (int b = lo; b < hi; ++b) {
     const int nt = ntile[b];
     tile_start[b] = run;
     for (int k = 0; k < nt; ++k) tile_bucket[run + k] = b;
-    int acc = run * NT;
-    for (int half = 0; half < 2; ++half)
-      for (int c = 0; c < nchunk; ++c) {
-        base[(int64_t)c * 2 * NB + 2 * b + half] = acc;
-        acc += cnt[(int64_t)c * 2 * NB + 2 * b + half];
-      }
     run += nt;
+  }
+  if (tid == 1023) tile_start[NB] = part[1023];
+}
+
+// per-chunk bases of a bucket's sub-buckets (its lower-half tokens first,
+// each in chunk order): one block per bucket, an exclusive scan over the
+// 2 x nchunk counts in that order, offset by the bucket's first slot
+__global__ __launch_bounds__(256) void k_bucket_base(const int32_t* __restrict__ cnt, int nchunk,
+                                                     int NB, const int32_t* __restrict__ tile_start,
+                                                     int32_t* __restrict__ base) {
+  __shared__ int part[256];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n = 2 * nchunk;  // entry e: half e / nchunk, chunk e % nchunk
+  const int per = (n + 255) / 256;
+  const int lo = tid * per, hi = min(n, lo + per);
+  auto at = [&](int e) -> int64_t {
+    const int half = e >= nchunk ? 1 : 0, c = e - half * nchunk;
+    return (int64_t)c * 2 * NB + 2 * b + half;
+  };
+  int sum = 0;
+  for (int e = lo; e < hi; ++e) sum += cnt[at(e)];
+  part[tid] = sum;
+  __syncthreads();
+  for (int st = 1; st < 256; st <<= 1) {
+    const int v = tid >= st ? part[tid - st] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tile_start[b] * NT + part[tid] - sum;
+  for (int e = lo; e < hi; ++e) {
+    const int64_t k = at(e);
+    const int v = cnt[k];
+    base[k] = run;
+    run += v;
   }
 }
 
@@ -1315,8 +1351,12 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   const int nch = (int)P.nchunk;
   hipLaunchKernelGGL(k_bucket_count, dim3(nch), dim3(256), 2 * P.NB * sizeof(int), st, kb, vb, low,
                      P.GK, P.NB, cnt, present);
-  hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), (P.NB + 1024) * sizeof(int), st, cnt, nch,
-                     P.NB, base, tile_start, bcount, tile_bucket);
+  // the tile counts go through `base` (rewritten right after)
+  hipLaunchKernelGGL(k_bucket_tot, dim3(P.NB), dim3(256), 0, st, cnt, nch, P.NB, bcount, base);
+  hipLaunchKernelGGL(k_bucket_tiles, dim3(1), dim3(1024), 0, st, base, P.NB, tile_start,
+                     tile_bucket);
+  hipLaunchKernelGGL(k_bucket_base, dim3(P.NB), dim3(256), 0, st, cnt, nch, P.NB, tile_start,
+                     base);
   hipLaunchKernelGGL(k_bucket_scatter, dim3(nch), dim3(256), 0, st, kb, vb, low, P.GK, P.NB, base,
                      perm);
   }
