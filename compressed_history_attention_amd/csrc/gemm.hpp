@@ -104,6 +104,7 @@ constexpr int GD_BK = 32, GD_STAGES = 4;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; all-ones = no wait on that counter)
 constexpr int GD_WAIT_VM8 = 8 | (7 << 4) | (15 << 8);           // vmcnt(8)
+constexpr int GD_WAIT_VM4 = 4 | (7 << 4) | (15 << 8);           // vmcnt(4)
 constexpr int GD_WAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0)
 constexpr int GD_OP = 128 * GD_BK * 2;  // bytes of one operand tile per stage
 
@@ -140,50 +141,54 @@ __device__ __forceinline__ bf16x8 gd_frag(const char* base, int r, int b) {
   return as_bf16x8(*reinterpret_cast<const u32x4*>(base + r * 64 + ((b ^ ((r >> 2) & 3)) << 4)));
 }
 
-// step kt: wait for stage kt (cS), load stage kt + 3 into nS, then the MFMAs
-// of stage kt into the wave's 64 x 64 quadrant (wm, wn)
-template <class P>
-__device__ __forceinline__ void gd_step(const P& p, int z, const GdLanes& L, int lane, int wm,
-                                        int wn, int kt, int nk, const char* cS, char* nS,
-                                        f32x16 (&acc)[2][2]) {
-  const char* cA = cS;
-  const char* cB = cS + GD_OP;
+// operand fragments of a stage for the wave's 64 x 64 quadrant (wm, wn)
+struct GdFrags {
+  bf16x8 a[GD_BK / 16][2], b[GD_BK / 16][2];
+};
+__device__ __forceinline__ void gd_read(const char* cS, int lane, int wm, int wn, GdFrags& f) {
   const int hl = lane >> 5;
-  // stage kt has landed once at most the two newer stages' loads (4 per
-  // stage per wave) are outstanding (the builtin, unlike inline asm, is seen
-  // by the compiler's own wait placement, which then adds none before the
-  // reads below) ...
-  __builtin_amdgcn_s_waitcnt(GD_WAIT_VM8);
-  // ... in every wave, and every wave's reads of stage kt - 1 (the one
-  // loaded next) have returned.  A bare barrier: the fence of __syncthreads
-  // would wait for every load in flight
-  __builtin_amdgcn_s_waitcnt(GD_WAIT_LGKM0);
-  __builtin_amdgcn_s_barrier();
-  // this stage's operand fragments first, then the loads into the ring (kept
-  // in this order, so that the compiler's count before the reads is exact)
-  bf16x8 fa[GD_BK / 16][2], fb[GD_BK / 16][2];
 #pragma unroll
   for (int ks = 0; ks < GD_BK / 16; ++ks)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      fa[ks][i] = gd_frag(cA, wm + 32 * i + (lane & 31), 2 * ks + hl);
-      fb[ks][i] = gd_frag(cB, wn + 32 * i + (lane & 31), 2 * ks + hl);
+      f.a[ks][i] = gd_frag(cS, wm + 32 * i + (lane & 31), 2 * ks + hl);
+      f.b[ks][i] = gd_frag(cS + GD_OP, wn + 32 * i + (lane & 31), 2 * ks + hl);
     }
+}
+
+// step kt, with stage kt's fragments already in `cur`: wait for stage kt + 1
+// (nS1), load stage kt + 3 into nS3, read stage kt + 1's fragments into
+// `nxt` while the MFMAs of stage kt run
+template <class P>
+__device__ __forceinline__ void gd_step(const P& p, int z, const GdLanes& L, int lane, int wm,
+                                        int wn, int kt, int nk, const char* nS1, char* nS3,
+                                        const GdFrags& cur, GdFrags& nxt, f32x16 (&acc)[2][2]) {
+  // stage kt + 1 has landed once at most the next stage's loads (4 per wave)
+  // are outstanding (the builtin, unlike inline asm, is seen by the
+  // compiler's own wait placement, which then adds none before the reads
+  // below) ...
+  __builtin_amdgcn_s_waitcnt(GD_WAIT_VM4);
+  // ... in every wave, and every wave's reads of stage kt (read during the
+  // step before) have returned, so the stage loaded next (kt + 3, the ring
+  // slot of kt - 1) is free.  A bare barrier: the fence of __syncthreads
+  // would wait for every load in flight
+  __builtin_amdgcn_s_waitcnt(GD_WAIT_LGKM0);
+  __builtin_amdgcn_s_barrier();
+  gd_load(p, z, L, kt + GD_STAGES - 1, nk, nS3);
   __builtin_amdgcn_sched_barrier(0);
-  gd_load(p, z, L, kt + GD_STAGES - 1, nk, nS);
-  __builtin_amdgcn_sched_barrier(0);
+  gd_read(nS1, lane, wm, wn, nxt);
   // steps past the end multiply zeros (no branch around the MFMAs: the same
   // straight line on every path)
   const bool live = kt < nk;
 #pragma unroll
   for (int ks = 0; ks < GD_BK / 16; ++ks) {
+    bf16x8 fa[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fa[i] = live ? cur.a[ks][i] : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      if (!live) fa[ks][i] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fa[ks][i], fb[ks][j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fa[i], cur.b[ks][j], acc[i][j]);
   }
 }
 
@@ -219,11 +224,15 @@ __global__ __launch_bounds__(256) void k_gemm_dma(const P p) {
   gd_load(p, z, L, 0, nk, s0);
   gd_load(p, z, L, 1, nk, s1);
   gd_load(p, z, L, 2, nk, s2);
+  GdFrags f0, f1;
+  __builtin_amdgcn_s_waitcnt(GD_WAIT_VM8);  // stage 0 (two newer stages in flight)
+  __builtin_amdgcn_s_barrier();
+  gd_read(s0, lane, wm, wn, f0);
   for (int kt = 0; kt < nk; kt += 4) {
-    gd_step(p, z, L, lane, wm, wn, kt, nk, s0, s3, acc);
-    gd_step(p, z, L, lane, wm, wn, kt + 1, nk, s1, s0, acc);
-    gd_step(p, z, L, lane, wm, wn, kt + 2, nk, s2, s1, acc);
-    gd_step(p, z, L, lane, wm, wn, kt + 3, nk, s3, s2, acc);
+    gd_step(p, z, L, lane, wm, wn, kt, nk, s1, s3, f0, f1, acc);
+    gd_step(p, z, L, lane, wm, wn, kt + 1, nk, s2, s0, f1, f0, acc);
+    gd_step(p, z, L, lane, wm, wn, kt + 2, nk, s3, s1, f0, f1, acc);
+    gd_step(p, z, L, lane, wm, wn, kt + 3, nk, s0, s2, f1, f0, acc);
   }
   // no load may still be in flight into LDS when the block ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
