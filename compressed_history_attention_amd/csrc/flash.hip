@@ -9,9 +9,10 @@
 // bf16 (per-head transposed so PV operands are contiguous along keys).
 // Keys beyond Nk up to the 64-key padding are zero and masked.
 //
-// Block = 4 waves x 32 queries of one head; each tile of 64 keys moves from
-// HBM/L2 into double-buffered LDS with direct-to-LDS loads (1 KiB per wave
-// instruction, no registers, no LDS stores).  Per wave and tile: S^T = K Q^T
+// Block = NW waves (8, or 4 when 8-wave blocks would leave the chip's last
+// round of blocks under-filled) x 32 queries of one head; each tile of 64 keys
+// moves from HBM/L2 into double-buffered LDS with direct-to-LDS loads (1 KiB
+// per wave instruction, no registers, no LDS stores).  Per wave and tile: S^T = K Q^T
 // is 2 x 8 MFMA 32x32x16 (lane = query column, 32 keys per lane), O^T +=
 // V^T P^T is 4 x 4 MFMAs whose B operand is the wave's own P in registers.
 //
@@ -37,8 +38,8 @@ __device__ __forceinline__ int fa_key_of_row(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q, int64_t Nq, int H,
+template <bool OUT_F32, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_flash(const uint16_t* __restrict__ Q, int64_t Nq, int H,
                                                   float c, const uint16_t* __restrict__ K,
                                                   const uint16_t* __restrict__ VT, int64_t Nk,
                                                   int64_t ld, int nsplit, void* __restrict__ out,
@@ -54,7 +55,8 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
   // fastest, then head, then key-range split) is given to block
   // (u % per) * 8 + u / per, so that each XCD's L2 serves the K/V rows of a
   // few heads instead of slices of all of them
-  const int nqb = (int)((Nq + FA_QB - 1) / FA_QB);
+  constexpr int QB = 32 * NW;  // queries per block
+  const int nqb = (int)((Nq + QB - 1) / QB);
   const int nunits = nqb * H * nsplit;
   const int per = (nunits + 7) / 8;
   const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
   const int h = (u / nqb) % H;
   const int split = u / (nqb * H);  // key-range split (partials merged later)
   const int W = H * 128;
-  const int64_t q0 = (int64_t)(u % nqb) * FA_QB + wave * 32;
+  const int64_t q0 = (int64_t)(u % nqb) * QB + wave * 32;
   const int64_t qrow = q0 + (lane & 31);
   const bool qok = qrow < Nq;
 
@@ -79,15 +81,15 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
 
   const int64_t ntiles_all = (Nk + FA_KT - 1) / FA_KT;
   const int64_t t_beg = ntiles_all * split / nsplit, t_end = ntiles_all * (split + 1) / nsplit;
-  // this wave's 8 of the 32 1-KiB chunks of tile t: K chunks 0..15 (16 key
-  // rows each), V^T chunks 16..31 (8 dim rows each), each lane one 16-byte
-  // block of the swizzled layout
+  // this wave's 32 / NW of the 32 1-KiB chunks of tile t: K chunks 0..15 (16
+  // key rows each), V^T chunks 16..31 (8 dim rows each), each lane one
+  // 16-byte block of the swizzled layout
   const char* kbase = reinterpret_cast<const char*>(K + h * 128);
   const char* vbase = reinterpret_cast<const char*>(VT + (int64_t)h * 128 * ld);
   auto dma = [&](int64_t t, char* dk, char* dv) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ch = wave + 4 * j;  // K chunk
+    for (int j = 0; j < 16 / NW; ++j) {
+      const int ch = wave + NW * j;  // K chunk
       const int s = ch * 64 + lane, r = s >> 4, blk = (s & 15) ^ (r & 15);
       uint32_t off = (uint32_t)(r * W * 2 + blk * 16);
       asm volatile("" : "+v"(off));
@@ -96,8 +98,8 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
                                        16, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ch = wave + 4 * j;  // V^T chunk
+    for (int j = 0; j < 16 / NW; ++j) {
+      const int ch = wave + NW * j;  // V^T chunk
       const int s = ch * 64 + lane, r = s >> 3, blk = (s & 7) ^ ((r >> 1) & 7);
       uint32_t off = (uint32_t)(r * ld * 2 + blk * 16);
       asm volatile("" : "+v"(off));
@@ -252,17 +254,26 @@ __global__ __launch_bounds__(256, 2) void k_flash(const uint16_t* __restrict__ Q
   }
 }
 
+namespace {
+// fill of the last round of blocks: rounds / ceil(rounds)
+double flash_fill(int64_t blocks, double slots) {
+  const double rounds = (double)blocks / slots;
+  return rounds / std::ceil(rounds);
+}
+// 8-wave blocks (one per CU; each K/V tile serves 256 queries) unless their
+// last round would be under 85 % full
+bool flash_wide(int64_t Nq, int H) { return flash_fill(ceil_div(Nq, 256) * H, 256.0) >= 0.85; }
+}  // namespace
+
 int flash_splits(int64_t Nq, int H, int64_t Nk) {
-  // two blocks per CU.  Splitting costs a merge of S fp32 partials, so split
-  // only when the last round of blocks would be under 85 % full, and then
-  // take the smallest count that fills it to 90 % (at least 4 key tiles per
-  // split)
+  if (flash_wide(Nq, H)) return 1;
+  // 4-wave blocks, two per CU.  Splitting costs a merge of S fp32 partials,
+  // so split only when the last round of blocks would be under 85 % full,
+  // and then take the smallest count that fills it to 90 % (at least 4 key
+  // tiles per split)
   const double slots = 512.0;
-  const int64_t blocks = ceil_div(Nq, FA_QB) * H, tiles = ceil_div(Nk, FA_KT);
-  auto eff = [&](int S) {
-    const double rounds = (double)(blocks * S) / slots;
-    return rounds / std::ceil(rounds);
-  };
+  const int64_t blocks = ceil_div(Nq, 128) * H, tiles = ceil_div(Nk, FA_KT);
+  auto eff = [&](int S) { return flash_fill(blocks * S, slots); };
   if (eff(1) >= 0.85) return 1;
   int best = 1;
   for (int S = 2; S <= 8 && tiles >= 4 * S; ++S) {
@@ -277,14 +288,22 @@ nkv_status launch_flash(const uint16_t* q, int64_t Nq, int H, float tau, const u
                         float* lse, int nsplit, hipStream_t st) {
   if (Nq == 0) return NKV_OK;
   const float c = tau * 1.4426950408889634f;
-  const int64_t units = ceil_div(Nq, FA_QB) * H * nsplit;
-  const dim3 grid((unsigned)(ceil_div(units, 8) * 8));
-  if (out_f32)
-    hipLaunchKernelGGL(k_flash<true>, grid, dim3(256), 0, st, q, Nq, H, c, kall, vt, Nk, ld, nsplit,
+  const bool wide = nsplit == 1 && flash_wide(Nq, H);
+  const int nw = wide ? 8 : 4;
+  const int64_t units = ceil_div(Nq, 32 * nw) * H * nsplit;
+  const dim3 grid((unsigned)(ceil_div(units, 8) * 8)), block((unsigned)(64 * nw));
+  if (out_f32 && wide)
+    hipLaunchKernelGGL((k_flash<true, 8>), grid, block, 0, st, q, Nq, H, c, kall, vt, Nk, ld, nsplit,
                        out, lse);
+  else if (out_f32)
+    hipLaunchKernelGGL((k_flash<true, 4>), grid, block, 0, st, q, Nq, H, c, kall, vt, Nk, ld, nsplit,
+                       out, lse);
+  else if (wide)
+    hipLaunchKernelGGL((k_flash<false, 8>), grid, block, 0, st, q, Nq, H, c, kall, vt, Nk, ld,
+                       nsplit, out, lse);
   else
-    hipLaunchKernelGGL(k_flash<false>, grid, dim3(256), 0, st, q, Nq, H, c, kall, vt, Nk, ld, nsplit,
-                       out, lse);
+    hipLaunchKernelGGL((k_flash<false, 4>), grid, block, 0, st, q, Nq, H, c, kall, vt, Nk, ld,
+                       nsplit, out, lse);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }

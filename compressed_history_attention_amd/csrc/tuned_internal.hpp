@@ -7,7 +7,6 @@
 namespace nkv {
 
 constexpr int FA_KT = 64;     // keys per flash-attention tile (key padding unit)
-constexpr int FA_QB = 128;    // queries per flash-attention block
 
 nkv_status launch_decode_tuned(const BranchArgs& b, int W, int r, int group,
                                const RangeTable& rows, uint16_t* out, int64_t ld, bool transposed,
