@@ -326,11 +326,23 @@ __global__ __launch_bounds__(256) void k_build_images(
     sav[tid] = real ? vb.idx[t] : -1;
   }
   __syncthreads();
-  for (int i = tid; i < NT * nb; i += 256) {
+  // code bytes 4 at a time when the code arrays are word-aligned (rows and
+  // runs are then whole words: r % 32 == 0, r_low % 16 == 0)
+  const bool words = ((reinterpret_cast<uintptr_t>(kb.codes) | reinterpret_cast<uintptr_t>(vb.codes)) & 3) == 0;
+  const int nw4 = words ? nb / 4 : 0;
+  for (int i = tid; i < NT * nb && !words; i += 256) {
     const int k = i / nb, j = i - k * nb;
     const int64_t t = stok[k];
     skc[k][j] = t >= 0 ? kb.codes[t * (r / 2) + j] : uint8_t(0);
     svc[k][j] = t >= 0 ? vb.codes[t * (r / 2) + j] : uint8_t(0);
+  }
+  for (int i = tid; i < NT * nw4; i += 256) {
+    const int k = i / nw4, j = i - k * nw4;
+    const int64_t t = stok[k];
+    const uint32_t* kc = reinterpret_cast<const uint32_t*>(kb.codes + (t >= 0 ? t : 0) * (r / 2));
+    const uint32_t* vc = reinterpret_cast<const uint32_t*>(vb.codes + (t >= 0 ? t : 0) * (r / 2));
+    reinterpret_cast<uint32_t*>(skc[k])[j] = t >= 0 ? kc[j] : 0u;
+    reinterpret_cast<uint32_t*>(svc[k])[j] = t >= 0 ? vc[j] : 0u;
   }
   for (int i = tid; i < NT * ns; i += 256) {
     const int k = i / ns, j = i - k * ns;
