@@ -885,14 +885,25 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
         }
         tt[cb] = mfma_bf16(m, qv[ks], tt[cb]);
       }
+    // element e of block cb is center cb*32 + acc_row(e, lane): one base
+    // address per lane plus constant offsets
+    float* trow = sT + (wave * 32 + (ln & 31)) * TS + (ln >> 5) * 4;
+    if ((gk + 1) * CR <= a.A_k) {  // block-uniform: every center of the range exists
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int cl = cb * 32 + acc_row(e, ln);
-        sT[(wave * 32 + (ln & 31)) * TS + cl] =
-            (gk * CR + cl < a.A_k) ? fmaf(tt[cb][e], a.c, -Bq) : -INFINITY;
-      }
+        for (int e = 0; e < 16; ++e)
+          trow[cb * 32 + (e >> 2) * 8 + (e & 3)] = fmaf(tt[cb][e], a.c, -Bq);
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int cl = cb * 32 + acc_row(e, ln);
+          trow[cb * 32 + (e >> 2) * 8 + (e & 3)] =
+              (gk * CR + cl < a.A_k) ? fmaf(tt[cb][e], a.c, -Bq) : -INFINITY;
+        }
+    }
     if (hl == 0) sT[rloc * TS + CR] = -INFINITY;
   };
 
