@@ -744,6 +744,41 @@ __global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict_
   }
 }
 
+// The same with 16-byte accesses (ld, key0 and n_pad multiples of 8): a
+// 64-token x 64-channel tile is read as 8-channel chunks and written as
+// 8-token chunks.
+__global__ __launch_bounds__(256) void k_transpose_v16(const uint16_t* __restrict__ src, int64_t n,
+                                                       int64_t n_pad, int W,
+                                                       uint16_t* __restrict__ dst, int64_t ld,
+                                                       int64_t key0) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = threadIdx.x + 256 * k, tt = i >> 3, cc = (i & 7) * 8;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (t0 + tt < n) v = ld_u32x4(src + (t0 + tt) * W + c0 + cc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[tt][cc + 2 * q] = uint16_t(v[q] & 0xffffu);
+      tile[tt][cc + 2 * q + 1] = uint16_t(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = threadIdx.x + 256 * k, cc = i >> 3, tt = (i & 7) * 8;
+    if (t0 + tt >= n_pad) continue;  // n_pad % 8 == 0: a chunk is wholly in or out
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = uint32_t(tile[tt + 2 * q][cc]) | (uint32_t(tile[tt + 2 * q + 1][cc]) << 16);
+    const int c = c0 + cc;
+    *reinterpret_cast<u32x4*>(dst + ((int64_t)(c >> 7) * 128 + (c & 127)) * ld + key0 + t0 + tt) = v;
+  }
+}
+
 nkv_status launch_stage_current(const uint16_t* ck, const uint16_t* cv, int64_t n_cur,
                                 int64_t n_pad_tail, int W, uint16_t* kall, uint16_t* vt,
                                 int64_t ld, int64_t key0, hipStream_t st) {
@@ -753,8 +788,14 @@ nkv_status launch_stage_current(const uint16_t* ck, const uint16_t* cv, int64_t 
   hipLaunchKernelGGL(k_copy_rows, dim3((unsigned)ceil_div(nthreads, 256)), dim3(256), 0, st, ck,
                      n_cur, W, kall + key0 * W, n_pad_tail);
   NKV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_transpose_v, dim3((unsigned)ceil_div(n_pad_tail, 64), W / 64), dim3(256), 0,
-                     st, cv, n_cur, n_pad_tail, W, vt, ld, key0);
+  const bool wide = ld % 8 == 0 && key0 % 8 == 0 && n_pad_tail % 8 == 0 &&
+                    ((reinterpret_cast<uintptr_t>(cv) | reinterpret_cast<uintptr_t>(vt)) & 15) == 0;
+  if (wide)
+    hipLaunchKernelGGL(k_transpose_v16, dim3((unsigned)ceil_div(n_pad_tail, 64), W / 64), dim3(256),
+                       0, st, cv, n_cur, n_pad_tail, W, vt, ld, key0);
+  else
+    hipLaunchKernelGGL(k_transpose_v, dim3((unsigned)ceil_div(n_pad_tail, 64), W / 64), dim3(256), 0,
+                       st, cv, n_cur, n_pad_tail, W, vt, ld, key0);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }
