@@ -9,16 +9,18 @@
 //
 // Design for CDNA4:
 //  * The coefficients of a token are shared by every head (joint
-//    head-channel coding), so one staged coefficient tile feeds 128 query
+//    head-channel coding), so one staged coefficient tile feeds 256 query
 //    rows of a head through MFMA: scores as fp16 MFMA (q~ . c), the
 //    coefficient accumulation as bf16 MFMA (P c^V).
 //  * The per-row center tables T (read) and M (accumulate) have A entries per
-//    row -- too large for LDS at 128 rows.  Low-routed tokens are therefore
+//    row -- too large for LDS.  Low-routed tokens are therefore
 //    counting-sorted into buckets by (a^V range, a^K range) of 64 centers
-//    each; a block walks the buckets in order, keeps only the 64-entry slice
-//    of T (recomputed per bucket by MFMA, q_h . mu^K exact-product bf16) and
-//    of M (flushed to HBM when its a^V range is finished) in LDS, and gathers
-//    / scatter-adds them per score with conflict-free LDS accesses.
+//    each (and within a bucket by the half of the a^V range); a block walks
+//    the buckets in order, keeps the 64-entry slice of T in LDS (recomputed
+//    per bucket by MFMA, q_h . mu^K exact-product bf16) and gathers it per
+//    score with conflict-free LDS reads, and accumulates the 64 masses of the
+//    current a^V range in registers through a one-hot MFMA (flushed to HBM
+//    when the range is finished).
 //  * Softmax uses a per-row upper bound B on every score instead of a
 //    running maximum (B = tau (max over present centers of T + |q~| max|c^K|)),
 //    so p = 2^(x - B) <= 1 needs no rescaling of the LDS tables and partial
@@ -670,7 +672,8 @@ __device__ __forceinline__ void load_rows_swizzled(const uint16_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Main kernel.  One block = 256 query rows of one head; wave w owns rows
 // 32w..32w+31 and scores them against all 64 keys of every tile, so each
-// tile brought into LDS feeds 8 x 32 MFMAs and rows never meet across waves.
+// tile brought into LDS feeds 8 waves' MFMAs and rows never meet across
+// waves.
 //   S^T[key][row] = T[row][a^K] + (c q~) . c^K       (T gathered into the
 //                                                     accumulator, fp16 MFMA)
 //   p = 2^S                                          (bound B already in T)
