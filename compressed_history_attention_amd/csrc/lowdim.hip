@@ -163,6 +163,38 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
   }
 }
 
+// The same with 16-byte accesses, for lds % 8 == 0, ldd % 8 == 0 and 16-byte
+// aligned arrays: a 64 x 64 tile is read as 8-column chunks (columns past C
+// read as zero, C % 8 == 0) and written as 8-row chunks (rows past R zero).
+__global__ __launch_bounds__(256) void k_transpose_bf16_16(const uint16_t* __restrict__ src, int R,
+                                                           int C, int lds,
+                                                           uint16_t* __restrict__ dst, int ldd) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = threadIdx.x + 256 * k, rr = i >> 3, cc = (i & 7) * 8;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (r0 + rr < R && c0 + cc < C) v = ld_u32x4(src + (int64_t)(r0 + rr) * lds + c0 + cc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[rr][cc + 2 * q] = uint16_t(v[q] & 0xffffu);
+      tile[rr][cc + 2 * q + 1] = uint16_t(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = threadIdx.x + 256 * k, cc = i >> 3, rr = (i & 7) * 8;
+    if (c0 + cc >= C || r0 + rr >= ldd) continue;  // ldd % 8 == 0: a chunk is wholly in or out
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = uint32_t(tile[rr + 2 * q][cc]) | (uint32_t(tile[rr + 2 * q + 1][cc]) << 16);
+    *reinterpret_cast<u32x4*>(dst + (int64_t)(c0 + cc) * ldd + r0 + rr) = v;
+  }
+}
+
 // Sub-bucket of a token: its bucket (a^V range, a^K range) times two, plus
 // which half of the a^V range its V center lies in.  Within a bucket the
 // tokens of the lower half come first, so most 16-key steps of a tile touch
@@ -1361,13 +1393,19 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, st, misc, (int64_t)4);
   NKV_LAUNCH_CHECK();
   // transposed query-reduction map (this width), transposed V centers
-  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(W, 64), (unsigned)ceil_div(r_low, 64)),
-                     dim3(256), 0, st, static_cast<const uint16_t*>(mp.qmap), W, r_low, mp.ld, dkt,
-                     W);
-  if (first)
-    hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)ceil_div(P.avp, 64), (unsigned)ceil_div(W, 64)),
-                       dim3(256), 0, st, static_cast<const uint16_t*>(vb.centers), vb.A, W, W, mvt,
-                       P.avp);
+  auto transpose = [&](const void* src, int R, int C, int lds, uint16_t* dst, int ldd) {
+    const dim3 grid((unsigned)ceil_div(ldd, 64), (unsigned)ceil_div(C, 64));
+    const bool wide = lds % 8 == 0 && ldd % 8 == 0 && C % 8 == 0 &&
+                      ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+    if (wide)
+      hipLaunchKernelGGL(k_transpose_bf16_16, grid, dim3(256), 0, st,
+                         static_cast<const uint16_t*>(src), R, C, lds, dst, ldd);
+    else
+      hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, st, static_cast<const uint16_t*>(src),
+                         R, C, lds, dst, ldd);
+  };
+  transpose(mp.qmap, W, r_low, mp.ld, dkt, W);
+  if (first) transpose(vb.centers, vb.A, W, W, mvt, P.avp);
   NKV_LAUNCH_CHECK();
   }
   if (first) {
