@@ -38,7 +38,7 @@ namespace {
 
 constexpr int NT = 64;        // keys per tile (bucket padding unit)
 constexpr int CR = 64;        // centers per range
-constexpr int TS = 65;        // LDS row stride of the center tables (64 + sentinel)
+constexpr int TS = 65;        // LDS row stride of the center tables (odd: rows spread over banks)
 constexpr int CHUNK = 256;    // tokens per counting chunk
 constexpr float BOUND_GAP_LIMIT = 60.f;  // log2 units
 
@@ -53,7 +53,11 @@ constexpr float BOUND_GAP_LIMIT = 60.f;  // log2 units
 //                        row db*32 + l%32 (a coefficient, or a center for
 //                        db >= rp/32) for keys kb*32 + 16 j + 4 (l/32) + {0..3}
 //                        and the same + 8 (the key order of P in registers)
-//   [ko_off, +256)       per key: byte offset of its a^K slot in the T table row
+//   [ko_off, +64)        per key: byte offset of its a^K slot in the T table row
+//                        (one byte, 4 x the center's place in its range),
+//                        ordered so that lane l's 16 keys of 32-key block kb
+//                        (the keys of its score accumulator elements) are
+//                        the 16 bytes at kb*32 + 16 (l/32): one 16-byte read
 //   [hd_off, +16)        header: the facts of the FOLLOWING tile (its bucket,
 //                        whether it opens that bucket, the a^K range of the
 //                        bucket after it or -1; zero after the last tile), so
@@ -68,7 +72,7 @@ __host__ __device__ constexpr TileGeom tile_geom(int rlp) {
   const int rp = (rlp + 31) / 32 * 32;
   const int nks = rlp / 16, nvb = rp / 32 + CR / 32;  // K steps; V + one-hot row blocks
   const int ck_bytes = (NT / 32) * nks * 1024, cv_bytes = (NT / 32) * 2 * nvb * 1024;
-  const int ko_off = ck_bytes + cv_bytes, hd_off = ko_off + NT * 4;
+  const int ko_off = ck_bytes + cv_bytes, hd_off = ko_off + NT;
   return TileGeom{rlp, rp, nks, nvb, ck_bytes, ck_bytes, cv_bytes, ko_off, hd_off,
                   (hd_off + 16 + 1023) / 1024 * 1024};
 }
@@ -332,8 +336,7 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(BranchArgs kb, BranchArg
 // One block per tile writes the tile image with coalesced stores: the keys'
 // tokens, center indices and first r_low INT4 codes / fp16 scales are staged
 // in LDS, then the fp16 K rows (16-byte chunks), the bf16 V and a^V one-hot
-// rows (8-byte chunks), the T-table offsets (-inf sentinel for dummies) and
-// the header.  Also max |c^K[:r_low]|^2 over real keys.
+// rows (8-byte chunks), the T-table offsets and the header.  Also max |c^K[:r_low]|^2 over real keys.
 constexpr int IMG_MAXB = 64;   // code bytes staged per key (r_low <= 128)
 constexpr int IMG_MAXS = 16;   // scales staged per key (r_low / group, group >= 8)
 __global__ __launch_bounds__(256) void k_build_images(
@@ -430,8 +433,16 @@ __global__ __launch_bounds__(256) void k_build_images(
         u32x4{uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16),
               uint32_t(hv[4]) | (uint32_t(hv[5]) << 16), uint32_t(hv[6]) | (uint32_t(hv[7]) << 16)};
   }
-  if (tid < NT)
-    reinterpret_cast<int32_t*>(base + g.ko_off)[tid] = tid < nreal ? (sak[tid] % CR) * 4 : CR * 4;
+  if (tid < NT) {
+    // A dummy key takes the slot of key 0 (every tile has a real key 0):
+    // its score is then that of a center present in the low set, which the
+    // row bound covers, so p <= 1, and its zero V row and one-hot row make
+    // the p irrelevant.  Byte place of key k: block kb = k / 32, then the
+    // accumulator order (k % 32 = 8 g + 4 half + u -> 16 half + 4 g + u).
+    const int k = tid, w = k & 31;
+    const int place = (k >> 5) * 32 + ((w >> 2) & 1) * 16 + (w >> 3) * 4 + (w & 3);
+    base[g.ko_off + place] = (uint8_t)((sak[k < nreal ? k : 0] % CR) * 4);
+  }
   if (tid == 0) {
     u32x4 hd = {0u, 0u, 0u, 0u};
     if (tile + 1 < ntl) {
@@ -939,7 +950,6 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
               (gk * CR + cl < a.A_k) ? fmaf(tt[cb][e], a.c, -Bq) : -INFINITY;
         }
     }
-    if (hl == 0) sT[rloc * TS + CR] = -INFINITY;
   };
 
   // bucket facts of the tile about to be processed: tile 0's from the tables,
@@ -984,17 +994,16 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
       for (int k = 0; k < Geo::DMA_PER_WAVE; ++k) dma(t + 1, nxt, k);
       return;
     }
-    const int32_t* sKO = reinterpret_cast<const int32_t*>(cur + G.ko_off);
     // Operand batches are read into registers well ahead of their MFMAs;
     // sched_barrier keeps the scheduler from sinking each read next to its
     // use, which would expose a full LDS round trip per MFMA.
     auto gather = [&](int kb, f32x16& acc) __attribute__((always_inline)) {
+      const u32x4 kov = *reinterpret_cast<const u32x4*>(cur + G.ko_off + kb * 32 + hl * 16);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x4 kov = *reinterpret_cast<const u32x4*>(&sKO[kb * 32 + g * 8 + hl * 4]);
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[4 * g + u] = *reinterpret_cast<const float*>(sTrow + kov[u]);
-      }
+        for (int u = 0; u < 4; ++u)
+          acc[4 * g + u] = *reinterpret_cast<const float*>(sTrow + ((kov[g] >> (8 * u)) & 0xffu));
     };
     auto read_v = [&](int kb, int j, bf16x8 (&vo)[NPB + 2]) __attribute__((always_inline)) {
 #pragma unroll
