@@ -535,10 +535,17 @@ struct DecodeTProblem {
 // plus the token's center (requested before the step's MFMAs) is rounded to
 // bf16 into an LDS tile -- [tok][ch] for K rows, [ch][tok] for the per-head
 // transposed V -- and leaves the block as 16-byte row chunks.
+// NKS > 0 fixes the number of 16-wide k-steps (r / 16) at compile time: the
+// sweep of a step is then straight-line code, every decoder load
+// unconditional, and the waits before the MFMAs count exactly the loads they
+// need (with k-steps and loads under run-time conditions the compiler waits
+// for every load in flight, the centers' included, before each group).
+// NKS = 0 takes r / 16 at run time.
 // ---------------------------------------------------------------------------
 constexpr int DS_TOK = 64, DS_CH = 128;
+constexpr int DS_WAIT_VM0 = (7 << 4) | (15 << 8);  // s_waitcnt vmcnt(0) alone
 
-template <bool ROWS>
+template <bool ROWS, int NKS>
 __global__ __launch_bounds__(256) void k_decode_stationary(BranchArgs b, RangeTable rows, int W,
                                                            int r, int group,
                                                            uint16_t* __restrict__ out,
@@ -581,7 +588,7 @@ __global__ __launch_bounds__(256) void k_decode_stationary(BranchArgs b, RangeTa
     *reinterpret_cast<u32x4*>(sA + tl * rs + k) = v;
   }
   __syncthreads();
-  const int nks = r / 16;
+  const int nks = NKS > 0 ? NKS : r / 16;
   auto afrag = [&](int i, int ks) __attribute__((always_inline)) {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(sA + (32 * i + (lane & 31)) * rs + 16 * ks +
                                                      8 * hl));
@@ -593,22 +600,41 @@ __global__ __launch_bounds__(256) void k_decode_stationary(BranchArgs b, RangeTa
   // decoder fragments of k-steps ks0..ks0+7 for the rows of sweep step n0
   constexpr int PF = 8;
   auto ldd = [&](int n0, int ks0, u32x4 (&d)[PF]) __attribute__((always_inline)) {
-    const uint16_t* drow = D + (int64_t)(n0 + wave * 32 + (lane & 31)) * r + 8 * hl;
+    if constexpr (NKS > 0) {
+      // a prefetch past the block's last step rereads that step's rows
+      // (n_end >= DS_CH: the grid gives every block at least one step's range)
+      const int nn = min(n0, n_end - DS_CH);
+      const uint16_t* drow = D + (int64_t)(nn + wave * 32 + (lane & 31)) * r + 8 * hl;
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
-      d[u] = (ks0 + u < nks && n0 < n_end) ? ld_u32x4(drow + 16 * (ks0 + u)) : u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < PF; ++u)
+        if (ks0 + u < NKS) d[u] = ld_u32x4(drow + 16 * (ks0 + u));
+    } else {
+      const uint16_t* drow = D + (int64_t)(n0 + wave * 32 + (lane & 31)) * r + 8 * hl;
+#pragma unroll
+      for (int u = 0; u < PF; ++u)
+        d[u] = (ks0 + u < nks && n0 < n_end) ? ld_u32x4(drow + 16 * (ks0 + u))
+                                             : u32x4{0u, 0u, 0u, 0u};
+    }
   };
-  u32x4 d0[PF], d1[PF];
-  ldd(n_beg, 0, d0);
-  for (int n0 = n_beg; n0 < n_end; n0 += DS_CH) {
-    const int chl = wave * 32 + (lane & 31);               // lane's channel within the step
-    // the centers of the lane's 32 elements, requested before the MFMAs
-    uint32_t mk[32];
+  const int chl = wave * 32 + (lane & 31);  // lane's channel within a step
+  // the centers of the lane's 32 elements for sweep step n0 (a step past the
+  // block's last rereads that step's channels)
+  uint32_t mk[32];
+  auto ldmu = [&](int n0) __attribute__((always_inline)) {
+    const int nn = min(n0, n_end - DS_CH);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        mk[16 * i + e] = mu[(int64_t)sIdx[32 * i + acc_row(e, lane)] * W + n0 + chl];
+        mk[16 * i + e] = mu[(int64_t)sIdx[32 * i + acc_row(e, lane)] * W + nn + chl];
+  };
+  u32x4 d0[PF], d1[PF];
+  ldd(n_beg, 0, d0);
+  // as at the end of every step: the first decoder group is in registers
+  // before the loop, so its first MFMAs need no wait on any path
+  __builtin_amdgcn_s_waitcnt(DS_WAIT_VM0);
+  ldmu(n_beg);
+  for (int n0 = n_beg; n0 < n_end; n0 += DS_CH) {
     f32x16 acc[2] = {zero16(), zero16()};
     auto mm = [&](int ks0, const u32x4 (&d)[PF]) __attribute__((always_inline)) {
 #pragma unroll
@@ -621,17 +647,39 @@ __global__ __launch_bounds__(256) void k_decode_stationary(BranchArgs b, RangeTa
     };
     // d0 holds k-steps 0..PF-1 of this step on entry; the last group's
     // buffer is refilled with the next step's first k-steps
-    for (int ks0 = 0; ks0 < nks; ks0 += 2 * PF) {
-      if (ks0 + PF < nks) ldd(n0, ks0 + PF, d1);
-      else ldd(n0 + DS_CH, 0, d1);
-      mm(ks0, d0);
-      if (ks0 + 2 * PF < nks) ldd(n0, ks0 + 2 * PF, d0);
-      else if (ks0 + PF < nks) ldd(n0 + DS_CH, 0, d0);
-      if (ks0 + PF < nks) mm(ks0 + PF, d1);
-    }
-    if (((nks + PF - 1) / PF) % 2 == 1) {
+    if constexpr (NKS > 0) {
+      constexpr int NG = (NKS + PF - 1) / PF;
 #pragma unroll
-      for (int u = 0; u < PF; ++u) d0[u] = d1[u];
+      for (int g = 0; g < NG; ++g) {
+        u32x4(&cur)[PF] = (g & 1) ? d1 : d0;
+        u32x4(&nxt)[PF] = (g & 1) ? d0 : d1;
+        if (g + 1 < NG) ldd(n0, PF * (g + 1), nxt);
+        else ldd(n0 + DS_CH, 0, nxt);
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          if (PF * g + u >= NKS) break;
+          const bf16x8 dv = as_bf16x8(cur[u]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) acc[i] = mfma_bf16(afrag(i, PF * g + u), dv, acc[i]);
+        }
+      }
+      if constexpr (NG % 2 == 1) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) d0[u] = d1[u];
+      }
+    } else {
+      for (int ks0 = 0; ks0 < nks; ks0 += 2 * PF) {
+        if (ks0 + PF < nks) ldd(n0, ks0 + PF, d1);
+        else ldd(n0 + DS_CH, 0, d1);
+        mm(ks0, d0);
+        if (ks0 + 2 * PF < nks) ldd(n0, ks0 + 2 * PF, d0);
+        else if (ks0 + PF < nks) ldd(n0 + DS_CH, 0, d0);
+        if (ks0 + PF < nks) mm(ks0 + PF, d1);
+      }
+      if (((nks + PF - 1) / PF) % 2 == 1) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) d0[u] = d1[u];
+      }
     }
     __syncthreads();  // the previous step's reads of sO are done
 #pragma unroll
@@ -644,6 +692,12 @@ __global__ __launch_bounds__(256) void k_decode_stationary(BranchArgs b, RangeTa
         else sO[chl * OS + tl] = v;
       }
     __syncthreads();
+    // Every load done before the first store: while stores and loads are both
+    // in flight the compiler can only wait for a load with vmcnt(0), stores
+    // included, and the next step's first MFMAs would wait for this step's
+    // stores.  The loads still pending here are the next step's first
+    // decoder group, requested a whole group of MFMAs ago.
+    __builtin_amdgcn_s_waitcnt(DS_WAIT_VM0);
     if constexpr (ROWS) {
       // 64 token rows x 16 chunks of 8 channels
 #pragma unroll
@@ -667,6 +721,9 @@ __global__ __launch_bounds__(256) void k_decode_stationary(BranchArgs b, RangeTa
         }
       }
     }
+    // the next step's centers: their latency runs under the barrier and the
+    // first MFMA group
+    ldmu(n0 + DS_CH);
   }
 }
 
@@ -685,19 +742,31 @@ nkv_status launch_decode_tuned(const BranchArgs& b, int W, int r, int group,
     const int64_t tb = ceil_div(rows.total, DS_TOK);
     const int ysplit = (int)std::min<int64_t>(W / DS_CH, std::max<int64_t>(1, 1024 / tb));
     const dim3 grid((unsigned)tb, (unsigned)ysplit);
-    if (transposed) {
+    const int nks = r % 16 == 0 ? r / 16 : 0;
+    auto go = [&](auto kern) -> nkv_status {
       if (lds > 64 * 1024)
-        NKV_HIP_CHECK(hipFuncSetAttribute((const void*)k_decode_stationary<false>,
+        NKV_HIP_CHECK(hipFuncSetAttribute((const void*)kern,
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-      hipLaunchKernelGGL(k_decode_stationary<false>, grid, dim3(256), lds, st, b, rows, W, r,
-                         group, out, ld);
-    } else {
-      if (lds > 64 * 1024)
-        NKV_HIP_CHECK(hipFuncSetAttribute((const void*)k_decode_stationary<true>,
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-      hipLaunchKernelGGL(k_decode_stationary<true>, grid, dim3(256), lds, st, b, rows, W, r,
-                         group, out, ld);
+      hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, b, rows, W, r, group, out, ld);
+      return NKV_OK;
+    };
+    nkv_status e;
+    switch (nks) {
+#define NKV_DECODE_NKS(n)                                                                    \
+  case n:                                                                                   \
+    e = transposed ? go(k_decode_stationary<false, n>) : go(k_decode_stationary<true, n>);  \
+    break;
+      NKV_DECODE_NKS(6)
+      NKV_DECODE_NKS(8)
+      NKV_DECODE_NKS(12)
+      NKV_DECODE_NKS(16)
+      NKV_DECODE_NKS(24)
+      NKV_DECODE_NKS(32)
+#undef NKV_DECODE_NKS
+      default:
+        e = transposed ? go(k_decode_stationary<false, 0>) : go(k_decode_stationary<true, 0>);
     }
+    if (e) return e;
     NKV_LAUNCH_CHECK();
     return NKV_OK;
   }
