@@ -199,10 +199,14 @@ __global__ __launch_bounds__(128 * QW) void k_project_stationary(const uint16_t*
   const bool rok = stager && rtok < N;
   const uint16_t* xrow = x + (rok ? rtok : 0) * W;
   const uint16_t* mrow = mu + (int64_t)(rok ? idx[rtok] : 0) * W;
+  // Every load is unconditional (a chunk past the share rereads its last
+  // chunk; rows past N read row 0 and stage zeros): with loads under
+  // run-time conditions the compiler can only wait for all of them, and the
+  // residual rows requested two chunks ahead would be waited for at once.
   auto ld_res = [&](int c, u32x4& xv, u32x4& mv) __attribute__((always_inline)) {
-    const int w = w_beg + c * PS_KC + rc;
-    xv = rok ? ld_u32x4(xrow + w) : u32x4{0u, 0u, 0u, 0u};
-    mv = rok ? ld_u32x4(mrow + w) : u32x4{0u, 0u, 0u, 0u};
+    const int w = w_beg + min(c, nchunk - 1) * PS_KC + rc;
+    xv = ld_u32x4(xrow + w);
+    mv = ld_u32x4(mrow + w);
   };
   auto put_res = [&](int stage, const u32x4& xv, const u32x4& mv) __attribute__((always_inline)) {
     if (!stager) return;
@@ -225,9 +229,10 @@ __global__ __launch_bounds__(128 * QW) void k_project_stationary(const uint16_t*
       tm[h] = pack_bf16x2(mid2[0], mid2[1]);
       tl[h] = pack_bf16x2(lo2[0], lo2[1]);
     }
-    *reinterpret_cast<u32x4*>(&sE[stage][0][rt * PS_AS + rc]) = th;
-    *reinterpret_cast<u32x4*>(&sE[stage][1][rt * PS_AS + rc]) = tm;
-    *reinterpret_cast<u32x4*>(&sE[stage][2][rt * PS_AS + rc]) = tl;
+    const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(&sE[stage][0][rt * PS_AS + rc]) = rok ? th : z4;
+    *reinterpret_cast<u32x4*>(&sE[stage][1][rt * PS_AS + rc]) = rok ? tm : z4;
+    *reinterpret_cast<u32x4*>(&sE[stage][2][rt * PS_AS + rc]) = rok ? tl : z4;
   };
   // wave tile: tokens 32 (wave & 1) .., outputs (wave >> 1) R/QW ..
   const int tw = (wave & 1) * 32, ow = (wave >> 1) * (R / QW);
@@ -237,9 +242,8 @@ __global__ __launch_bounds__(128 * QW) void k_project_stationary(const uint16_t*
     for (int j = 0; j < TW; ++j)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        b[j][ks] = c < nchunk ? ld_u32x4(enc + (int64_t)(ow + 32 * j + (lane & 31)) * W + w_beg +
-                                         c * PS_KC + 16 * ks + 8 * hl)
-                              : u32x4{0u, 0u, 0u, 0u};
+        b[j][ks] = ld_u32x4(enc + (int64_t)(ow + 32 * j + (lane & 31)) * W + w_beg +
+                            min(c, nchunk - 1) * PS_KC + 16 * ks + 8 * hl);
   };
   f32x16 acc[TW];
 #pragma unroll
@@ -250,14 +254,14 @@ __global__ __launch_bounds__(128 * QW) void k_project_stationary(const uint16_t*
   u32x4 xv[2], mv[2];
   u32x4 bb[3][TW][2];
   ld_res(0, xv[0], mv[0]);
-  if (nchunk > 1) ld_res(1, xv[1], mv[1]);
+  ld_res(1, xv[1], mv[1]);
   ld_enc(0, bb[0]);
   ld_enc(1, bb[1]);
   put_res(0, xv[0], mv[0]);
   __syncthreads();
   auto step = [&](int c, auto RS, auto BS) __attribute__((always_inline)) {
     constexpr int rs = decltype(RS)::value, bs = decltype(BS)::value;
-    if (c + 2 < nchunk) ld_res(c + 2, xv[rs], mv[rs]);
+    ld_res(c + 2, xv[rs], mv[rs]);
     ld_enc(c + 2, bb[(bs + 2) % 3]);
 #pragma unroll
     for (int term = 0; term < 3; ++term)
