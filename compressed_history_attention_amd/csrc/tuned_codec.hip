@@ -172,7 +172,7 @@ struct ProjProblem {
 // one chunk ahead.  Exact products and fp32 sums reproduce an fp32
 // projection.
 // ---------------------------------------------------------------------------
-constexpr int PS_TOK = 64, PS_KC = 32, PS_SHARE = 768;
+constexpr int PS_TOK = 64, PS_KC = 32, PS_SHARE = 1024;
 constexpr int PS_AS = PS_KC + 8;  // bf16 row stride of a residual term tile
 
 template <int NT, int QW>  // r = 64 NT outputs in QW groups; 2 QW waves
