@@ -77,6 +77,17 @@ __host__ __device__ constexpr TileGeom tile_geom(int rlp) {
                   (hd_off + 16 + 1023) / 1024 * 1024};
 }
 
+// Center-mass planes (bf16 hi | lo: 2 WS columns per (query m, head zb of
+// the group) row) are stored in blocks of 128 rows x 32 columns (8 KiB):
+// block (zb * nmt + m / 128) * (2 WS / 32) + col / 32, then row m % 128,
+// then column col % 32 (nmt = ceil(Nq / 128)).  The restoration's K steps
+// of 32 columns then read one contiguous block per 128 query rows, and a
+// wave's flush of 32 rows writes contiguous 2 KiB pieces.
+__host__ __device__ inline int64_t mass_pos(int64_t m, int zb, int col, int64_t nmt, int WS) {
+  return ((((int64_t)zb * nmt + (m >> 7)) * (WS >> 4) + (col >> 5)) * 128 + (m & 127)) * 32 +
+         (col & 31);
+}
+
 struct Plan {
   int64_t n_low = 0, nchunk = 0, max_tiles = 0, max_slots = 0, rows = 0;
   int GK = 0, GV = 0, NB = 0, rlp = 0, rp = 0, ra = 0, av = 0, avp = 0;
@@ -131,9 +142,11 @@ Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& l
   // partial sums of the main pass: (split, query, head of the group) rows
   const int64_t prows = Nq * part_units;
   // fp32 partials, or (one split) bf16 hi/lo planes of the same byte size:
-  // acc rows of 2 x ra, mass rows of 2 x GV * 64 bf16
+  // acc rows of 2 x ra; mass rows of 2 x GV * 64 bf16, in 128-row blocks
+  // (the rows of every head of the read, Nq rounded up to 128)
   P.acc = take(sizeof(float) * prows * P.ra);
-  P.wmass = take(sizeof(float) * prows * P.GV * CR);
+  P.wmass = take(std::max(sizeof(float) * prows * P.GV * CR,
+                          sizeof(uint16_t) * 2 * P.GV * CR * s->H * ceil_div(Nq, 128) * 128));
   P.ell = take(sizeof(float) * prows);
   P.racc = take(sizeof(float) * P.rows * P.ra);   // rows of 2 x ra bf16
   P.rell = take(sizeof(float) * P.rows);
@@ -829,7 +842,6 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   // sums as planes only without splits
   const bool planes = nsplit == 1 || a.gvsplit;
   const bool acc_planes = nsplit == 1;
-  const int64_t mrow = a.gvsplit ? ((rok ? qrow : q0) * a.hs.n + by) : prow;
   const int WS = a.GV * CR;
   auto put_hilo = [&](uint16_t* hi, uint16_t* lo, f32x4 v) __attribute__((always_inline)) {
     float l[4];
@@ -838,15 +850,17 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
     *reinterpret_cast<uint2*>(hi) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     *reinterpret_cast<uint2*>(lo) = uint2{pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3])};
   };
+  uint16_t* const mplane = reinterpret_cast<uint16_t*>(a.wmass);
+  const int64_t nmt = (a.Nq + 127) / 128;
   auto put_mass = [&](int gv) __attribute__((always_inline)) {
     if (rok && planes) {
-      uint16_t* row = reinterpret_cast<uint16_t*>(a.wmass) + mrow * 2 * WS + gv * CR;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          const int c = cb * 32 + e4 * 8 + hl * 4;
-          put_hilo(row + c, row + WS + c,
+          const int c = gv * CR + cb * 32 + e4 * 8 + hl * 4;
+          put_hilo(mplane + mass_pos(qrow, by, c, nmt, WS),
+                   mplane + mass_pos(qrow, by, WS + c, nmt, WS),
                    f32x4{accW[cb][4 * e4], accW[cb][4 * e4 + 1], accW[cb][4 * e4 + 2],
                          accW[cb][4 * e4 + 3]});
         }
@@ -875,11 +889,10 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   auto zero_mass = [&](int g0, int g1) __attribute__((always_inline)) {
     if (!rok) return;
     if (planes) {
-      uint16_t* row = reinterpret_cast<uint16_t*>(a.wmass) + mrow * 2 * WS;
       for (int gv = g0; gv < g1; ++gv)
-        for (int c = hl * 4; c < CR; c += 8) {
-          *reinterpret_cast<uint2*>(row + gv * CR + c) = uint2{0u, 0u};
-          *reinterpret_cast<uint2*>(row + WS + gv * CR + c) = uint2{0u, 0u};
+        for (int c = gv * CR + hl * 4; c < (gv + 1) * CR; c += 8) {
+          *reinterpret_cast<uint2*>(mplane + mass_pos(qrow, by, c, nmt, WS)) = uint2{0u, 0u};
+          *reinterpret_cast<uint2*>(mplane + mass_pos(qrow, by, WS + c, nmt, WS)) = uint2{0u, 0u};
         }
       return;
     }
@@ -1184,7 +1197,7 @@ struct RestoreProblem {
   // the coefficient sums are always planes [hi | lo] of 2 x ra and ell one
   // value per row (split partials are reduced before this GEMM)
   const float* acc;    // partials [nsplit][Nq][hs.n][r_low]
-  const float* wmass;  // partials [nsplit][Nq][hs.n][A_v]
+  const float* wmass;  // partials [nsplit][Nq][hs.n][A_v], or bf16 planes in 128-row blocks
   const uint16_t* dv;    // restoration map [W, ldv]
   const uint16_t* mvt;   // [W, av]
   const float* ell;     // partials [nsplit][Nq][hs.n]
@@ -1196,6 +1209,7 @@ struct RestoreProblem {
   __device__ int64_t prow(int s, int m, int zb) const {
     return ((int64_t)s * M + m) * hs.n + zb;
   }
+  __device__ int64_t nmt() const { return (M + 127) / 128; }  // 128-row blocks of the mass planes
   __device__ u32x4 load_a(int zb, int m, int k) const {
     if (m >= M || k >= K) return u32x4{0u, 0u, 0u, 0u};
     if (k < 2 * ra || mass_planes != 0) {
@@ -1207,7 +1221,7 @@ struct RestoreProblem {
       }
       const int kk = k - 2 * ra;
       const int c = kk >= av ? kk - av + WS : kk;
-      return ld_u32x4(reinterpret_cast<const uint16_t*>(wmass) + pr * 2 * WS + c);
+      return ld_u32x4(reinterpret_cast<const uint16_t*>(wmass) + mass_pos(m, zb, c, nmt(), WS));
     }
     // masses as fp32 partials of key-range splits: summed and split here
     float v[8];
@@ -1262,7 +1276,8 @@ struct RestoreProblem {
     const int64_t pr = prow(0, m, zb);
     if (k < 2 * ra) return reinterpret_cast<const uint16_t*>(acc) + pr * 2 * ra + k;
     const int kk = k - 2 * ra;
-    return reinterpret_cast<const uint16_t*>(wmass) + pr * 2 * WS + (kk >= av ? kk - av + WS : kk);
+    return reinterpret_cast<const uint16_t*>(wmass) +
+           mass_pos(m, zb, kk >= av ? kk - av + WS : kk, nmt(), WS);
   }
   __device__ const uint16_t* b_ptr(int zb, int n, int k) const {
     const int64_t ch = (int64_t)hs.h[zb] * 128 + n;
