@@ -128,7 +128,7 @@ Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& l
   P.qt16 = take(sizeof(uint16_t) * P.rows * P.rlp);
   P.bound = take(sizeof(float) * P.rows);
   P.tmax = take(sizeof(uint32_t) * P.rows);
-  P.present = take(sizeof(uint32_t) * A_k);
+  P.present = take(sizeof(uint32_t) * ceil_div(A_k, 64) * 64);  // cleared to a whole 64-center block
   P.misc = take(sizeof(uint32_t) * 4);
   P.flags = take(sizeof(int32_t) * P.rows);
   // counting sort over sub-buckets: (bucket, which half of its a^V range)
@@ -534,7 +534,10 @@ __device__ __forceinline__ u32x4 lds_row_block(const char* lds, int r, int j) {
 // MFMA operand reads are conflict-free); each lane folds its centers into a
 // running max and one store per row replaces the atomics of a GEMM epilogue.
 // Products are exact (bf16), sums fp32 in k order: the same values as a
-// GEMM over k.
+// GEMM over k.  The presence flags (cleared to a whole 64-center block, so
+// every load is unconditional) are requested one block ahead with the
+// block's center rows, in two register sets: their latency runs under the
+// MFMAs of the block before instead of after each block's own MFMAs.
 constexpr int CM_Q = 128, CM_C = 64;
 __global__ __launch_bounds__(256) void k_center_max(const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ muk,
@@ -570,7 +573,16 @@ __global__ __launch_bounds__(256) void k_center_max(const uint16_t* __restrict__
   };
   float best = -INFINITY;
   const int nblk = (A_k + CM_C - 1) / CM_C;
-  auto block = [&](int blk, const char* cur) __attribute__((always_inline)) {
+  // presence flags of the lane's 32 centers of block blk: (cb, g) -> the 4
+  // consecutive centers blk*64 + 32 cb + 8 g + 4 hl .. + 3 (elements 4g..4g+3)
+  auto ldpr = [&](int blk, u32x4 (&pr)[8]) __attribute__((always_inline)) {
+    const int b = min(blk, nblk - 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      pr[i] = *reinterpret_cast<const u32x4*>(present + b * CM_C + (i >> 2) * 32 + (i & 3) * 8 +
+                                               hl * 4);
+  };
+  auto block = [&](const char* cur, const u32x4 (&pr)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       f32x16 acc = zero16();
@@ -578,34 +590,28 @@ __global__ __launch_bounds__(256) void k_center_max(const uint16_t* __restrict__
       for (int ks = 0; ks < 8; ++ks)
         acc = mfma_bf16(as_bf16x8(lds_row_block(cur, cb * 32 + (lane & 31), 2 * ks + hl)),
                         qv[ks], acc);
-      const int c0 = blk * CM_C + cb * 32;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int cg = c0 + g * 8 + hl * 4;  // the 4 consecutive centers of elements 4g..4g+3
-        u32x4 pr;
-        if (cg + 4 <= A_k) {
-          pr = *reinterpret_cast<const u32x4*>(present + cg);
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) pr[u] = cg + u < A_k ? present[cg + u] : 0u;
-        }
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (pr[u]) best = fmaxf(best, acc[4 * g + u]);
-      }
+          if (pr[cb * 4 + g][u]) best = fmaxf(best, acc[4 * g + u]);
     }
   };
+  u32x4 pr0[8], pr1[8];
   load(0, sMu0);
+  ldpr(0, pr0);
   for (int blk = 0; blk < nblk; blk += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (blk + 1 < nblk) load(blk + 1, sMu1);
-    block(blk, sMu0);
+    ldpr(blk + 1, pr1);
+    block(sMu0, pr0);
     if (blk + 1 < nblk) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (blk + 2 < nblk) load(blk + 2, sMu0);
-      block(blk + 1, sMu1);
+      ldpr(blk + 2, pr0);
+      block(sMu1, pr1);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1434,7 +1440,8 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   }
   if (first) {
   ProfScope ps_sort("low_prep_sort", st);
-  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(kb.A, 256)), dim3(256), 0, st, present, (int64_t)kb.A);
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)ceil_div(kb.A, 256)), dim3(256), 0, st, present,
+                     (int64_t)ceil_div(kb.A, 64) * 64);
   // bucket sort of the low-routed tokens
   const int nch = (int)P.nchunk;
   hipLaunchKernelGGL(k_bucket_count, dim3(nch), dim3(256), 2 * P.NB * sizeof(int), st, kb, vb, low,
