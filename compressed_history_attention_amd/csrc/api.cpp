@@ -57,7 +57,7 @@ static float tau_of(const nkv_shape* s) {
 }
 
 static bool tuned_applies(const nkv_shape* s, int32_t r_low) {
-  if (g_force_generic || !tuned_available()) return false;
+  if (g_force_generic) return false;
   return s->dtype == NKV_BF16 && s->d == 128 && s->r % 32 == 0 &&
          (r_low == 0 || (r_low % 16 == 0 && r_low <= 128));
 }
@@ -213,6 +213,10 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
     if ((st = build_routes(route, n_seg, N_hist, &full, &low))) return st;
   } else {
     if ((st = build_routes(nullptr, 0, N_hist, &full, &low))) return st;
+  }
+  // Nothing routed low: the widths play no part, exactly as in the size query
+  // (workspace_common), so dispatch and workspace layout are the same
+  if (low.total == 0) {
     r_low = 0;
     r_low_h = nullptr;
   }
@@ -226,8 +230,7 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
   }
   const bool tuned_maps = mp.ld % 8 == 0 && (reinterpret_cast<uintptr_t>(mp.qmap) & 15) == 0 &&
                           (reinterpret_cast<uintptr_t>(mp.omap) & 15) == 0;
-  const bool tuned = tuned_applies_all(shape, r_low, low.total > 0 ? r_low_h : nullptr) &&
-                     (low.total == 0 || tuned_maps);
+  const bool tuned = tuned_applies_all(shape, r_low, r_low_h) && (low.total == 0 || tuned_maps);
   if (low.total > 0 && r_low > 512 && !tuned)
     NKV_FAIL(NKV_EUNSUPPORTED, "generic low-dimensional read supports r_low <= 512");
   const size_t need = workspace_common(shape, k->A, v->A, N_hist, fast ? route : nullptr,
@@ -242,12 +245,15 @@ static nkv_status attend_common(const nkv_shape* shape, const nkv_branch* k, con
   const BranchArgs kb = to_args(k), vb = to_args(v);
 
   if (tuned) {
-    return tuned_attend(shape, kb, vb, mp, full, low, r_low, low.total > 0 ? r_low_h : nullptr, tau, q,
-                        Nq, cur_k, cur_v, N_cur, out, lse, static_cast<char*>(ws), ws_bytes, s);
+    return tuned_attend(shape, kb, vb, mp, full, low, r_low, r_low_h, tau, q, Nq, cur_k, cur_v,
+                        N_cur, out, lse, static_cast<char*>(ws), ws_bytes, s);
   }
 
   const int64_t W = (int64_t)H * d;
   const GenericLayout L = generic_layout(shape, full.total, low.total, Nq, N_cur, r_low_h != nullptr);
+  if (L.total > ws_bytes)  // the size query and this layout must agree
+    NKV_FAIL(NKV_EWORKSPACE, "internal: generic layout of %zu bytes exceeds the %zu given", L.total,
+             ws_bytes);
   char* base = static_cast<char*>(ws);
   float* kw = reinterpret_cast<float*>(base + L.k);
   float* vw = reinterpret_cast<float*>(base + L.v);
@@ -504,6 +510,24 @@ nkv_status nkv_lse_merge(int64_t Nq, int32_t H, int32_t d, const float* o_a, con
   if (Nq > 0 && (!o_a || !lse_a || !o_b || !lse_b || !out || !lse_out))
     NKV_FAIL(NKV_EINVAL, "NULL pointer with Nq>0");
   if ((int64_t)H * d > 16384) NKV_FAIL(NKV_EUNSUPPORTED, "H*d above 16384");
+  if (Nq > (int64_t)1 << 31) NKV_FAIL(NKV_EUNSUPPORTED, "Nq above 2^31");
+  // Only exact aliasing is safe: an fp32 output equal to a part (each element
+  // is read, then written, by one thread) and lse_out equal to a part's LSE.
+  // Any other overlap, and a bf16 output over a part's bytes, races.
+  const size_t ob = (size_t)Nq * H * d * (out_dtype == NKV_F32 ? 4 : 2);
+  const size_t pb = (size_t)Nq * H * d * 4, lb = (size_t)Nq * H * 4;
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+  };
+  for (const float* part : {o_a, o_b})
+    if (overlap(out, ob, part, pb) && !(out_dtype == NKV_F32 && out == (const void*)part))
+      NKV_FAIL(NKV_EINVAL, "out overlaps a part other than as the same fp32 array");
+  for (const float* pl : {lse_a, lse_b})
+    if (overlap(lse_out, lb, pl, lb) && lse_out != pl)
+      NKV_FAIL(NKV_EINVAL, "lse_out partly overlaps a part's LSE");
+  if (overlap(out, ob, lse_out, lb) || overlap(out, ob, lse_a, lb) || overlap(out, ob, lse_b, lb))
+    NKV_FAIL(NKV_EINVAL, "out overlaps an LSE array");
   return launch_lse_merge(Nq, H, d, o_a, lse_a, o_b, lse_b, out, out_dtype, lse_out,
                           static_cast<hipStream_t>(stream));
 }

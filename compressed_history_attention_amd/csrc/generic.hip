@@ -18,34 +18,43 @@ namespace nkv {
 // encode: nearest center (NanoKV abstract: shared cluster centers)
 // ---------------------------------------------------------------------------
 // One block of 256 threads per token; each wave scans a quarter of the
-// centers with lanes striding the channels; ties resolve to the lowest index.
+// centers with lanes striding the channels.  Distances are
+// ||mu_a||^2 - 2 mu_a . x in fp64 (products of fp32 or bf16 values are
+// exact in fp64), so near-ties resolve as exact arithmetic does; ties go to
+// the lowest index.
 template <int DT>
 __global__ __launch_bounds__(256) void k_assign_generic(
     const void* __restrict__ x, int64_t N, int W, const void* __restrict__ centers,
     int A, int32_t* __restrict__ idx) {
   extern __shared__ float smem[];
   float* xs = smem;                 // W
-  __shared__ float best_d[4];
+  __shared__ double best_d[4];
   __shared__ int best_a[4];
   const int64_t t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int w = threadIdx.x; w < W; w += 256) xs[w] = ld<DT>(x, t * W + w);
   __syncthreads();
-  float bd = FLT_MAX;
+  double bd = INFINITY;
   int ba = 0x7fffffff;
   for (int a = wave; a < A; a += 4) {
-    float acc = 0.f;
+    double m2 = 0.0, dot = 0.0;
     for (int w = lane; w < W; w += 64) {
-      const float df = xs[w] - ld<DT>(centers, (int64_t)a * W + w);
-      acc = fmaf(df, df, acc);
+      const double m = ld<DT>(centers, (int64_t)a * W + w);
+      m2 = fma(m, m, m2);
+      dot = fma((double)xs[w], m, dot);
     }
-    acc = wave_sum(acc);
-    if (acc < bd) { bd = acc; ba = a; }   // a increases: strict < keeps lowest
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      m2 += __shfl_xor(m2, o, 64);
+      dot += __shfl_xor(dot, o, 64);
+    }
+    const double dist = m2 - 2.0 * dot;
+    if (dist < bd) { bd = dist; ba = a; }   // a increases: strict < keeps lowest
   }
   if (lane == 0) { best_d[wave] = bd; best_a[wave] = ba; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float d0 = best_d[0];
+    double d0 = best_d[0];
     int a0 = best_a[0];
     for (int k = 1; k < 4; ++k) {
       if (best_d[k] < d0 || (best_d[k] == d0 && best_a[k] < a0)) { d0 = best_d[k]; a0 = best_a[k]; }

@@ -1,7 +1,9 @@
 // Per-stage HIP-event timing of the tuned path (profiling aid).
 #include <string.h>
 
+#include <atomic>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -14,11 +16,15 @@ struct Rec {
   const char* name;
   hipEvent_t a, b;
 };
-bool g_on = false;
+// Events of enabled scopes from any host thread; the mutex covers the
+// record list and the pool of reusable events.
+std::atomic<bool> g_on{false};
+std::mutex g_mu;
 std::vector<Rec> g_pending;
 std::vector<hipEvent_t> g_pool;
 
 hipEvent_t get_event() {
+  std::lock_guard<std::mutex> lock(g_mu);
   if (!g_pool.empty()) {
     hipEvent_t e = g_pool.back();
     g_pool.pop_back();
@@ -43,6 +49,7 @@ ProfScope::~ProfScope() {
   hipEvent_t b = get_event();
   if (!b) return;
   (void)hipEventRecord(b, s_);
+  std::lock_guard<std::mutex> lock(g_mu);
   g_pending.push_back(Rec{name_, a_, b});
 }
 
@@ -55,6 +62,7 @@ extern "C" {
 void nkv_profile_enable(int on) { g_on = on != 0; }
 
 int nkv_profile_read(nkv_prof_entry* out, int32_t max_entries) {
+  std::lock_guard<std::mutex> lock(g_mu);
   std::map<std::string, std::pair<double, int>> acc;
   std::vector<std::string> order;
   int rc = 0;

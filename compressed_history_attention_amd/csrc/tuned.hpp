@@ -25,7 +25,4 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
                         const void* cur_k, const void* cur_v, int64_t N_cur, void* out,
                         float* lse, char* ws, size_t ws_bytes, hipStream_t st);
 
-// true once the tuned kernels are compiled in
-bool tuned_available();
-
 }  // namespace nkv

@@ -1,14 +1,10 @@
 // Orchestration of the tuned (MFMA) attention path: workspace layout and the
 // sequence of kernels for the full-dimensional and the Fast reads.
-#include <mutex>
-
 #include "lowdim.hpp"
 #include "prof.hpp"
 #include "tuned_internal.hpp"
 
 namespace nkv {
-
-bool tuned_available() { return true; }
 
 namespace {
 
@@ -50,37 +46,6 @@ Layout make_layout(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTabl
   return L;
 }
 
-// A second stream per device for the full-dimensional half of a Fast read
-// with per-head widths: decode + flash attention run there while the
-// caller's stream runs the low-dimensional passes, and the LSE merge on the
-// caller's stream waits for both (fork and join through two events).
-// Created on first use (default priority, non-blocking), kept until the
-// process ends; a mutex covers each read's enqueue so that calls from
-// several host threads use the events one at a time.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  std::mutex mu;
-  bool ok = false;
-};
-
-SideStream* side_stream() {
-  constexpr int MAX_DEV = 64;
-  static std::mutex g;
-  static SideStream* tab[MAX_DEV] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return nullptr;
-  std::lock_guard<std::mutex> lock(g);
-  if (!tab[dev]) {
-    SideStream* ss = new SideStream;
-    ss->ok = hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) == hipSuccess &&
-             hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) == hipSuccess &&
-             hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) == hipSuccess;
-    tab[dev] = ss;
-  }
-  return tab[dev]->ok ? tab[dev] : nullptr;
-}
-
 }  // namespace
 
 size_t tuned_attend_workspace(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& full,
@@ -95,6 +60,10 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
                         const void* cur_k, const void* cur_v, int64_t N_cur, void* out,
                         float* lse, char* ws, size_t ws_bytes, hipStream_t st) {
   const Layout L = make_layout(s, kb.A, vb.A, full, low, r_low, r_low_h, Nq, N_cur);
+  if (L.total > ws_bytes) {  // the size query and this layout must agree
+    set_error("internal: tuned layout of %zu bytes exceeds the %zu given", L.total, ws_bytes);
+    return NKV_EWORKSPACE;
+  }
   const int H = s->H, W = H * s->d;
   uint16_t* kall = reinterpret_cast<uint16_t*>(ws + L.kall);
   uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
@@ -155,32 +124,9 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
         return e2;
     return NKV_OK;
   };
-  // With one width group the main pass fills the chip by itself, and running
-  // the full half beside it only moves time between the two; with several
-  // groups the low half is a chain of short passes whose preparation and
-  // last rounds leave the chip idle, which the full half then uses.
-  SideStream* ss = ng > 1 ? side_stream() : nullptr;
-  if (!ss) {
-    if ((e = full_part(false, st)) || (e = low_part())) return e;
-  } else {
-    std::lock_guard<std::mutex> lock(ss->mu);
-    if (hipEventRecord(ss->fork, st) != hipSuccess ||
-        hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) {
-      set_error("fork onto the side stream failed");
-      return NKV_EHIP;
-    }
-    const nkv_status ef = full_part(false, ss->s);
-    // join even after an error: the caller's stream must not run ahead of
-    // work already queued on the side stream
-    const bool joined = hipEventRecord(ss->join, ss->s) == hipSuccess;
-    const nkv_status el = ef ? NKV_OK : low_part();
-    if (!joined || hipStreamWaitEvent(st, ss->join, 0) != hipSuccess) {
-      set_error("join of the side stream failed");
-      return NKV_EHIP;
-    }
-    if (ef) return ef;
-    if (el) return el;
-  }
+  // everything on the caller's stream: the library creates no streams or
+  // events of its own
+  if ((e = full_part(false, st)) || (e = low_part())) return e;
   ProfScope ps("merge", st);
   return launch_lse_merge_parts(Nq, H, s->d, L.fsplit, of, lf, ol, ll, out, NKV_BF16, lse, st);
 }

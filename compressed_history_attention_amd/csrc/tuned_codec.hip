@@ -4,8 +4,13 @@
 //   1. ||mu_a||^2 per center (fp32).
 //   2. Distance GEMM  d(a, t) = ||mu_a||^2 - 2 mu_a . x_t  on bf16 MFMA (bf16
 //      products are exact in fp32); the epilogue reduces each token's
-//      column to (min distance, lowest index) and merges blocks with a
-//      64-bit atomicMin on (order-preserving distance bits << 32 | a).
+//      column over the wave's 64 centers to (min distance, lowest index)
+//      and the runner-up distance, one record per 64-center slot.  A
+//      per-token pass takes the best record and flags the token when the
+//      runner-up lies within a rigorous bound on the fp32 rounding error of
+//      the two distances; flagged tokens are assigned again in fp64 (the
+//      same ||mu||^2 - 2 mu . x form), so the argmin is the one exact
+//      arithmetic gives, ties to the lowest index.
 //   3. Projection GEMM z = E (x - mu_a): the fp32 residual (exact for bf16
 //      inputs) is split into three bf16 terms hi + mid + lo = e, so three
 //      exact-product MFMA passes with fp32 accumulation give the projection
@@ -23,7 +28,8 @@ namespace nkv {
 // ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------
-__global__ void k_center_norms(const uint16_t* __restrict__ mu, int A, int W, float* __restrict__ out) {
+__global__ void k_center_norms(const uint16_t* __restrict__ mu, int A, int W, float* __restrict__ out,
+                               uint32_t* __restrict__ max_bits) {
   const int a = blockIdx.x;
   const uint16_t* row = mu + (int64_t)a * W;
   float acc = 0.f;
@@ -45,7 +51,24 @@ __global__ void k_center_norms(const uint16_t* __restrict__ mu, int A, int W, fl
     acc = fmaf(v, v, acc);
   }
   acc = wave_sum(acc);
-  if (threadIdx.x == 0) out[a] = acc;
+  if (threadIdx.x == 0) {
+    out[a] = acc;
+    if (max_bits) atomicMax(max_bits, ordered_bits(acc));
+  }
+}
+
+// ||mu_a||^2 in fp64 (squares of bf16 values are exact), for the exact
+// re-assignment of flagged tokens
+__global__ void k_center_norms64(const uint16_t* __restrict__ mu, int W, double* __restrict__ out) {
+  const uint16_t* row = mu + (int64_t)blockIdx.x * W;
+  double acc = 0.0;
+  for (int w = threadIdx.x; w < W; w += 64) {
+    const double v = bf16_bits_to_f32(row[w]);
+    acc = fma(v, v, acc);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (threadIdx.x == 0) out[blockIdx.x] = acc;
 }
 
 __global__ void k_fill_u64(uint64_t* p, int64_t n, uint64_t v) {
@@ -53,9 +76,101 @@ __global__ void k_fill_u64(uint64_t* p, int64_t n, uint64_t v) {
   if (i < n) p[i] = v;
 }
 
-__global__ void k_unpack_idx(const uint64_t* __restrict__ keys, int64_t n, int32_t* __restrict__ idx) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) idx[i] = (int32_t)(keys[i] & 0xffffffffu);
+// Per token: the best of its slot records (lowest distance, then lowest
+// index) and the runner-up distance over all centers.  The computed
+// distance of center a differs from the exact ||mu_a||^2 - 2 mu_a . x by
+// at most g (||mu_a||^2 + 2 ||mu_a|| ||x||) + u |d_a| (g = (W + 64) u /
+// (1 - (W + 64) u), u = 2^-24: fp32 sums of W exact products, the fp32
+// norm, one rounding of the difference).  With M = max_a ||mu_a|| the
+// bound E = 2 (g + u) (M^2 + 2 M ||x||) covers both candidates; when the
+// runner-up is more than E above the best, no other center can be nearer
+// (or tie) in exact arithmetic.  Otherwise the token joins the list for
+// the fp64 assignment.  (Bounds are inflated by 1 % for the rounding of
+// the norms themselves.)
+__global__ void k_argmin_reduce(const uint64_t* __restrict__ best, const float* __restrict__ second,
+                                int nslot, int64_t N, int W, const float* __restrict__ xnorm2,
+                                const uint32_t* __restrict__ mu_max_bits, int32_t* __restrict__ idx,
+                                int32_t* __restrict__ flagged, int32_t* __restrict__ nflag) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= N) return;
+  uint64_t bk = best[t];
+  float bsec = second[t];
+  float other = INFINITY;  // best distance of every slot but the winner's
+  for (int sl = 1; sl < nslot; ++sl) {
+    const uint64_t k = best[(int64_t)sl * N + t];
+    const float sc = second[(int64_t)sl * N + t];
+    if (k < bk) {
+      other = fminf(other, from_ordered_bits(uint32_t(bk >> 32)));
+      bk = k;
+      bsec = sc;
+    } else {
+      other = fminf(other, from_ordered_bits(uint32_t(k >> 32)));
+    }
+  }
+  const float d1 = from_ordered_bits(uint32_t(bk >> 32));
+  const float d2 = fminf(other, bsec);
+  const float u = 5.9604645e-8f;  // 2^-24
+  const float kw = (float)(W + 64) * u;
+  const float g = kw / (1.f - kw);
+  const float M = sqrtf(from_ordered_bits(*mu_max_bits)) * 1.01f;
+  const float X = sqrtf(fmaxf(xnorm2[t], 0.f)) * 1.01f;
+  const float E = 2.f * (g + u) * (M * M + 2.f * M * X);
+  idx[t] = (int32_t)(bk & 0xffffffffu);
+  // (a NaN or infinite distance compares false: such tokens are re-assigned too)
+  if (!(d2 - d1 > E)) flagged[atomicAdd(nflag, 1)] = (int32_t)t;
+}
+
+// fp64 assignment of the flagged tokens: d(a) = ||mu_a||^2 - 2 mu_a . x with
+// exact bf16 products summed in fp64; lowest index on ties.  One block per
+// listed token (grid-stride over the list), wave w scanning centers
+// a = w, w + 4, ...
+__global__ __launch_bounds__(256) void k_argmin_exact(const uint16_t* __restrict__ x, int W,
+                                                      const uint16_t* __restrict__ mu, int A,
+                                                      const double* __restrict__ mu2,
+                                                      const int32_t* __restrict__ flagged,
+                                                      const int32_t* __restrict__ nflag,
+                                                      int32_t* __restrict__ idx) {
+  extern __shared__ float xs[];  // the token's row (W values, exact)
+  __shared__ double bd_s[4];
+  __shared__ int ba_s[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = *nflag;
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int64_t t = flagged[i];
+    __syncthreads();  // the previous token's reads of xs are done
+    for (int w = threadIdx.x; w < W; w += 256) xs[w] = bf16_bits_to_f32(x[t * W + w]);
+    __syncthreads();
+    double bd = INFINITY;
+    int ba = 0x7fffffff;
+    for (int a = wave; a < A; a += 4) {
+      const uint16_t* row = mu + (int64_t)a * W;
+      double acc = 0.0;
+      for (int w = lane; w < W; w += 64)
+        acc = fma((double)xs[w], (double)bf16_bits_to_f32(row[w]), acc);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      const double dist = mu2[a] - 2.0 * acc;
+      if (dist < bd) {  // a increases within the wave: strict < keeps the lowest
+        bd = dist;
+        ba = a;
+      }
+    }
+    if (lane == 0) {
+      bd_s[wave] = bd;
+      ba_s[wave] = ba;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double d0 = bd_s[0];
+      int a0 = ba_s[0];
+      for (int k = 1; k < 4; ++k)
+        if (bd_s[k] < d0 || (bd_s[k] == d0 && ba_s[k] < a0)) {
+          d0 = bd_s[k];
+          a0 = ba_s[k];
+        }
+      idx[t] = a0;
+    }
+  }
 }
 
 __device__ __forceinline__ u32x4 load8_bf16(const uint16_t* base, int64_t row, int ld, int k,
@@ -73,14 +188,17 @@ struct DistProblem {
   const uint16_t* mu;
   const uint16_t* x;
   const float* mu2;
-  uint64_t* keys;
+  uint64_t* best;   // [slot][N]: (order-preserving distance bits << 32 | a) of the slot's nearest
+  float* second;    // [slot][N]: the slot's runner-up distance
   __device__ u32x4 load_a(int, int m, int k) const { return load8_bf16(mu, m, K, k, m < M && k < K); }
   __device__ u32x4 load_b(int, int n, int k) const { return load8_bf16(x, n, K, k, n < N && k < K); }
+  // one wave = centers m0 .. m0 + 63 (slot m0 / 64) x tokens n0 .. n0 + 63
   __device__ void epilogue(int, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+    if (m0 >= M) return;  // no center in this quadrant
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      float best = INFINITY;
-      int besta = 0x7fffffff;
+      float b1 = INFINITY, s1 = INFINITY;
+      int a1 = 0x7fffffff;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -88,17 +206,29 @@ struct DistProblem {
           const int a = m0 + 32 * i + acc_row(e, lane);
           if (a < M) {
             const float dist = mu2[a] - 2.f * acc[i][j][e];
-            if (dist < best || (dist == best && a < besta)) { best = dist; besta = a; }
+            if (dist < b1 || (dist == b1 && a < a1)) {
+              s1 = b1;
+              b1 = dist;
+              a1 = a;
+            } else {
+              s1 = fminf(s1, dist);
+            }
           }
         }
       }
-      const float ob = __shfl_xor(best, 32, 64);
-      const int oa = __shfl_xor(besta, 32, 64);
-      if (ob < best || (ob == best && oa < besta)) { best = ob; besta = oa; }
+      const float b2 = __shfl_xor(b1, 32, 64), s2 = __shfl_xor(s1, 32, 64);
+      const int a2 = __shfl_xor(a1, 32, 64);
+      // runner-up of the union of both lanes' candidates
+      const float sec = fminf(fminf(s1, s2), fmaxf(b1, b2));
+      if (b2 < b1 || (b2 == b1 && a2 < a1)) {
+        b1 = b2;
+        a1 = a2;
+      }
       const int n = n0 + 32 * j + (lane & 31);
-      if (lane < 32 && n < N && besta != 0x7fffffff) {
-        const uint64_t key = ((uint64_t)ordered_bits(best) << 32) | (uint32_t)besta;
-        atomicMin(reinterpret_cast<unsigned long long*>(keys + n), (unsigned long long)key);
+      if (lane < 32 && n < N) {
+        const int64_t o = (int64_t)(m0 / 64) * N + n;
+        best[o] = ((uint64_t)ordered_bits(b1) << 32) | (uint32_t)a1;
+        second[o] = sec;
       }
     }
   }
@@ -340,28 +470,71 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
   if (j % group == 0) scales[t * (r / group) + j / group] = __half_as_ushort(sh);
 }
 
-size_t tuned_assign_workspace(int64_t N, int32_t A) {
-  return align_up(sizeof(float) * A, 256) + align_up(sizeof(uint64_t) * N, 256);
+namespace {
+// workspace of the assignment: ||mu||^2 (fp32 and fp64), slot records,
+// token norms, the flagged-token list with its count and the max norm
+struct AssignLayout {
+  size_t mu2, mu2d, best, second, xn, list, misc, total;
+};
+AssignLayout assign_layout(int64_t N, int32_t A) {
+  AssignLayout L{};
+  const int64_t nslot = ceil_div(A, 64);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.mu2 = take(sizeof(float) * A);
+  L.mu2d = take(sizeof(double) * A);
+  L.best = take(sizeof(uint64_t) * nslot * N);
+  L.second = take(sizeof(float) * nslot * N);
+  L.xn = take(sizeof(float) * N);
+  L.list = take(sizeof(int32_t) * N);
+  L.misc = take(sizeof(uint32_t) * 2);  // flagged count, max ||mu||^2 bits
+  L.total = off;
+  return L;
 }
+}  // namespace
+
+size_t tuned_assign_workspace(int64_t N, int32_t A) { return assign_layout(N, A).total; }
 
 nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void* centers,
                         int32_t A, int32_t* idx, char* ws, hipStream_t st) {
   const int W = s->H * s->d;
-  float* mu2 = reinterpret_cast<float*>(ws);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(ws + align_up(sizeof(float) * A, 256));
+  const AssignLayout L = assign_layout(N, A);
+  float* mu2 = reinterpret_cast<float*>(ws + L.mu2);
+  double* mu2d = reinterpret_cast<double*>(ws + L.mu2d);
+  uint64_t* best = reinterpret_cast<uint64_t*>(ws + L.best);
+  float* second = reinterpret_cast<float*>(ws + L.second);
+  float* xn = reinterpret_cast<float*>(ws + L.xn);
+  int32_t* list = reinterpret_cast<int32_t*>(ws + L.list);
+  uint32_t* misc = reinterpret_cast<uint32_t*>(ws + L.misc);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* mub = static_cast<const uint16_t*>(centers);
-  hipLaunchKernelGGL(k_center_norms, dim3(A), dim3(64), 0, st, mub, A, W, mu2);
+  hipLaunchKernelGGL(k_fill_u64, dim3(1), dim3(64), 0, st, reinterpret_cast<uint64_t*>(misc), 1,
+                     0ull);
   NKV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N,
-                     ~0ull);
+  hipLaunchKernelGGL(k_center_norms, dim3(A), dim3(64), 0, st, mub, A, W, mu2, misc + 1);
   NKV_LAUNCH_CHECK();
-  DistProblem dp{A, (int)N, W, mub, xb, mu2, keys};
+  hipLaunchKernelGGL(k_center_norms, dim3((unsigned)N), dim3(64), 0, st, xb, (int)N, W, xn,
+                     nullptr);
+  NKV_LAUNCH_CHECK();
+  DistProblem dp{A, (int)N, W, mub, xb, mu2, best, second};
   nkv_status e;
   // (the register-staged GEMM with 64-wide k steps: measured faster here
   // than the direct-to-LDS one, whose 32-wide steps double the barriers)
   if ((e = launch_gemm(dp, 1, st))) return e;
-  hipLaunchKernelGGL(k_unpack_idx, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, keys, N, idx);
+  hipLaunchKernelGGL(k_argmin_reduce, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, best,
+                     second, (int)ceil_div(A, 64), N, W, xn, misc + 1, idx, list,
+                     reinterpret_cast<int32_t*>(misc));
+  NKV_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_center_norms64, dim3(A), dim3(64), 0, st, mub, W, mu2d);
+  NKV_LAUNCH_CHECK();
+  // the list is usually empty: a few blocks walk whatever it holds
+  hipLaunchKernelGGL(k_argmin_exact, dim3((unsigned)std::min<int64_t>(N, 256)), dim3(256),
+                     sizeof(float) * W, st, xb, W, mub, A, mu2d, list,
+                     reinterpret_cast<const int32_t*>(misc), idx);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }

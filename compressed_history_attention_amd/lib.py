@@ -379,6 +379,7 @@ def fit_centers(shape: Shape, x, centers, iters: int, stream=None):
     counts = torch.empty(A, dtype=torch.int32, device=centers.device)
     ws = _workspace(nkv_fit_workspace_size(shape, N, A), centers.device)
     nkv_fit_centers(shape, x, centers, iters, idx if N else None, counts, ws=ws, stream=stream)
+    _keep(stream, ws, idx, counts)
     return centers, idx, counts
 
 
@@ -502,6 +503,21 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
 
 
+def _keep(stream, *tensors) -> None:
+    """Tensors allocated here come from torch's caching allocator on the
+    current stream.  When the kernels run on another ``stream``, mark them
+    used there, so that their memory is not handed out again before that
+    stream's work is done (the workspace is freed as soon as we return)."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if s.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 def encode(shape: Shape, x, centers, encoder, out=None, stream=None):
     """Encode tokens x [N, W]; returns (idx int32 [N], codes uint8 [N, r/2],
     scales int16 [N, r/group] holding fp16 bits).  ``out`` may supply the
@@ -514,6 +530,7 @@ def encode(shape: Shape, x, centers, encoder, out=None, stream=None):
                torch.empty((N, shape.r // shape.group), dtype=torch.int16, device=dev))
     ws = _workspace(nkv_encode_workspace_size(shape, N, int(centers.shape[0])), dev)
     nkv_encode(shape, x, centers, encoder, *out, ws=ws, stream=stream)
+    _keep(stream, ws, *out)
     return out
 
 
@@ -527,6 +544,7 @@ def attend_full(shape: Shape, k: Branch, v: Branch, N_hist: int, q, cur_k=None, 
         ws = _workspace(nkv_attend_workspace_size(shape, k.A, v.A, N_hist, None, 0, Nq, N_cur),
                         q.device)
     nkv_attend_full(shape, k, v, N_hist, q, cur_k, cur_v, out, lse, ws=ws, stream=stream)
+    _keep(stream, ws, out, lse)
     return out, lse
 
 
@@ -547,6 +565,7 @@ def attend_fast(shape: Shape, k: Branch, v: Branch, N_hist: int, route, r_low, q
                                                            maps[0], maps[1], Nq, N_cur), q.device)
         nkv_attend_fast_maps(shape, k, v, N_hist, route, widths, maps[0], maps[1], q, cur_k, cur_v,
                              out, lse, ws=ws, stream=stream)
+        _keep(stream, ws, out, lse)
         return out, lse
     if not isinstance(r_low, (int, np.integer)):
         if ws is None:
@@ -554,12 +573,14 @@ def attend_fast(shape: Shape, k: Branch, v: Branch, N_hist: int, route, r_low, q
                                                             Nq, N_cur), q.device)
         nkv_attend_fast_heads(shape, k, v, N_hist, route, r_low, q, cur_k, cur_v, out, lse,
                               ws=ws, stream=stream)
+        _keep(stream, ws, out, lse)
         return out, lse
     if ws is None:
         ws = _workspace(nkv_attend_workspace_size(shape, k.A, v.A, N_hist, route, r_low, Nq,
                                                   N_cur), q.device)
     nkv_attend_fast(shape, k, v, N_hist, route, r_low, q, cur_k, cur_v, out, lse, ws=ws,
                     stream=stream)
+    _keep(stream, ws, out, lse)
     return out, lse
 
 
@@ -567,4 +588,5 @@ def lse_merge(H: int, d: int, o_a, lse_a, o_b, lse_b, out_dtype=torch.float32, s
     out = torch.empty(o_a.shape, dtype=out_dtype, device=o_a.device)
     lse = torch.empty(lse_a.shape, dtype=torch.float32, device=o_a.device)
     nkv_lse_merge(H, d, o_a, lse_a, o_b, lse_b, out, lse, stream=stream)
+    _keep(stream, out, lse)
     return out, lse

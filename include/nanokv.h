@@ -16,9 +16,12 @@
  * ---------------------------------------
  *  - W = H * d.  Channel h*d + j of a [*, W] row belongs to head h.
  *  - Every array is a DEVICE pointer, row-major and contiguous, owned by the
- *    caller; the library allocates nothing and keeps no state between calls
- *    (apart from the thread-local error string).  Scratch memory is the
- *    caller's `ws` buffer, sized by the matching *_workspace_size call.
+ *    caller; the library allocates nothing, creates no streams or events
+ *    (the opt-in profiling aid below aside) and keeps no state between calls
+ *    (apart from the thread-local error string and the testing switch
+ *    nkv_force_generic).  Scratch memory is the caller's `ws` buffer, sized
+ *    by the matching *_workspace_size call.  Every kernel of a call runs on
+ *    the caller's `stream`, in order.
  *  - Token, query, center, encoder, decoder and output tensors have the
  *    element type `nkv_shape.dtype`: NKV_F32 (float) or NKV_BF16 (bfloat16
  *    bit patterns in uint16).
@@ -236,7 +239,11 @@ nkv_status nkv_attend_fast_maps(const nkv_shape* shape, const nkv_branch* k,
  *   L = log(exp(L_a) + exp(L_b)),  O = exp(L_a - L) O_a + exp(L_b - L) O_b.
  * o_a, o_b float32 [Nq, H*d]; lse_a, lse_b, lse_out float32 [Nq, H]; out
  * [Nq, H*d] of out_dtype.  A -inf partition contributes nothing; if both are
- * -inf, O = 0 and L = -inf.  out/lse_out may alias o_a/lse_a.
+ * -inf, O = 0 and L = -inf.  Any d >= 1 (four channels per step when
+ * d % 4 == 0 and the rows are 16-byte aligned, one otherwise).
+ * Aliasing: with out_dtype == NKV_F32, `out` may be the very array o_a or
+ * o_b, and lse_out may be lse_a or lse_b; any other overlap (a bf16 `out`
+ * over a part's bytes, a shifted view) returns NKV_EINVAL.
  */
 nkv_status nkv_lse_merge(int64_t Nq, int32_t H, int32_t d, const float* o_a,
                          const float* lse_a, const float* o_b,
@@ -395,11 +402,14 @@ int nkv_version(void);
  * where the tuned MFMA kernels apply; 0 (default) restores the dispatch. */
 void nkv_force_generic(int on);
 
-/* Profiling aid (not thread-safe).  While enabled, each kernel stage of the
- * tuned path is bracketed by HIP events recorded on the call's stream.
- * nkv_profile_read waits for the recorded events, writes up to max_entries
- * per-stage totals (elapsed milliseconds and number of launches) and clears
- * them; it returns the number of stages written, or -1 on a HIP error. */
+/* Profiling aid, off by default.  While enabled, each kernel stage of the
+ * tuned path is bracketed by HIP events recorded on the call's stream; these
+ * events are the only HIP objects the library ever creates (kept in a pool
+ * for reuse until the process ends).  Calls from several host threads are
+ * safe: one lock covers the record list.  nkv_profile_read waits for the
+ * recorded events, writes up to max_entries per-stage totals (elapsed
+ * milliseconds and number of launches) and clears them; it returns the
+ * number of stages written, or -1 on a HIP error. */
 typedef struct {
   char name[32];
   double ms;

@@ -92,12 +92,25 @@ def device_branch(case: Case, b: int, include_new: bool = True) -> lib.Branch:
                       to_dev(case.w.centers(b), cfg.dtype), to_dev(case.w.decoder(b), cfg.dtype))
 
 
+QBLOCK = 128  # the smallest query block of any kernel (flash's 4-wave blocks)
+
+
 def q_rows(cfg: synth.Config, n_sample: Optional[int], seed: int = 0) -> np.ndarray:
+    """Query rows compared against the oracle: all of them (n_sample None),
+    or a stratified sample that reaches every 128-row query block -- its
+    first row, its last row and max(1, n_sample // blocks) seeded random rows
+    inside it -- so every block of every kernel (128- and 256-row blocks, the
+    ragged last block) has rows under test."""
     if n_sample is None or n_sample >= cfg.Nq:
         return np.arange(cfg.Nq)
     rng = np.random.default_rng(seed)
-    rows = set(rng.choice(cfg.Nq, size=n_sample - 2, replace=False).tolist())
-    rows |= {0, cfg.Nq - 1}
+    nb = (cfg.Nq + QBLOCK - 1) // QBLOCK
+    per = max(1, n_sample // nb)
+    rows = set()
+    for b in range(nb):
+        lo, hi = b * QBLOCK, min(cfg.Nq, (b + 1) * QBLOCK)
+        rows |= {lo, hi - 1}
+        rows |= set(rng.integers(lo, hi, size=per).tolist())
     return np.array(sorted(rows))
 
 

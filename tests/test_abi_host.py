@@ -190,3 +190,85 @@ def test_fit_validation():
     assert L.nkv_fit_workspace_size(ctypes.byref(sh), -1, 4) == lib.SIZE_MAX
     assert L.nkv_fit_workspace_size(ctypes.byref(sh), 8, 0) == lib.SIZE_MAX
     assert L.nkv_fit_workspace_size(ctypes.byref(sh), 8, 4) > 0
+
+
+EHIP = 4
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="launches with fake pointers: host-only check")
+@pytest.mark.parametrize("dtype,d,r", [(1, 128, 192), (0, 16, 64), (1, 64, 128)])
+@pytest.mark.parametrize("route", [[(0, 10, 0)], [(0, 6, 1), (6, 10, 0)], [(0, 10, 1)],
+                                   [(0, 3, 1), (3, 5, 0), (5, 10, 1)]])
+@pytest.mark.parametrize("r_low", [16, 24, 48, "r"])
+def test_workspace_query_matches_dispatch(dtype, d, r, route, r_low):
+    """The size a call checks against is the one its dispatch lays out: with
+    exactly the queried bytes the call passes every workspace check and only
+    fails at its first kernel launch (no GPU here); one byte less is refused.
+    Covers routes with nothing low-dimensional and widths the tuned kernels
+    do not serve (r_low = 24, r_low = r), where the two once disagreed."""
+    L = lib.load()
+    r_low = r if r_low == "r" else r_low
+    sh = _shape(H=2, d=d, r=r, group=32, dtype=dtype)
+    segs, n = lib._segments(route)
+    need = L.nkv_attend_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, r_low, 4, 2)
+    assert need not in (0, lib.SIZE_MAX)
+    assert _attend_fast(sh, route, r_low=r_low, ws=FAKE, wsb=need - 1) == EWS
+    msg = L.nkv_last_error().decode()
+    assert f"workspace of {need} bytes needed" in msg, msg
+    assert _attend_fast(sh, route, r_low=r_low, ws=FAKE, wsb=need) == EHIP, L.nkv_last_error()
+    # the per-head call with the same width everywhere lays out the same way
+    w = (ctypes.c_int32 * 2)(r_low, r_low)
+    need_h = L.nkv_attend_heads_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, w, 4, 2)
+    assert _attend_heads(sh, [r_low, r_low], route=route, ws=FAKE, wsb=need_h - 1) == EWS
+    assert _attend_heads(sh, [r_low, r_low], route=route, ws=FAKE, wsb=need_h) == EHIP
+    # the full read needs no more than any Fast call's all-full route
+    full = L.nkv_attend_workspace_size(ctypes.byref(sh), 4, 4, 10, None, 0, 0, 4, 2)
+    if route == [(0, 10, 0)]:
+        assert full == need
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="launches with fake pointers: host-only check")
+@pytest.mark.parametrize("widths", [[16, 24], [32, 48], [24, 64]])
+def test_heads_workspace_query_matches_dispatch(widths):
+    L = lib.load()
+    sh = _shape(H=2, d=128, r=192, group=32, dtype=1)
+    route = [(0, 6, 1), (6, 10, 0)]
+    segs, n = lib._segments(route)
+    w = (ctypes.c_int32 * 2)(*widths)
+    need = L.nkv_attend_heads_workspace_size(ctypes.byref(sh), 4, 4, 10, segs, n, w, 4, 2)
+    assert _attend_heads(sh, widths, route=route, ws=FAKE, wsb=need - 1) == EWS
+    assert _attend_heads(sh, widths, route=route, ws=FAKE, wsb=need) == EHIP
+
+
+def test_merge_aliasing_rules():
+    """Only exact aliasing is accepted: an fp32 output that is a part's own
+    array, an LSE output that is a part's own LSE array."""
+    L = lib.load()
+    Nq, H, d = 4, 2, 8
+    ob = Nq * H * d * 4
+    lb = Nq * H * 4
+    base = 0x100000
+    oa, ob_, la, lb_ = base, base + 4 * ob, base + 8 * ob, base + 8 * ob + 4096
+    out, lout = base + 12 * ob, base + 16 * ob
+
+    def call(o=out, lo=lout, dt=0):
+        return L.nkv_lse_merge(Nq, H, d, oa, la, ob_, lb_, o, dt, lo, None)
+
+    # bf16 output over a part's bytes races
+    assert call(o=oa, dt=1) == EINVAL
+    # a shifted view of a part
+    assert call(o=oa + 16) == EINVAL
+    assert call(lo=la + 4) == EINVAL
+    # output over an LSE array
+    assert call(o=la) == EINVAL
+    # d not a multiple of 4 is accepted (scalar path): validation passes and
+    # only the launch fails without a GPU
+    if _no_gpu():
+        assert L.nkv_lse_merge(Nq, H, 6, oa, la, ob_, lb_, out, 0, lout, None) == EHIP
+        assert call(o=oa, lo=la) == EHIP          # exact fp32 aliasing
+        assert call(o=ob_, lo=lb_) == EHIP

@@ -2,10 +2,20 @@
 
 Bars: center indices bit-exact; INT4 codes bit-exact outside the rounding
 window (scales per the near-midpoint rule); attention outputs within
-max|err| / max|ref| <= 1e-2 and LSE within 1e-3 absolute.  Fast reads must
-also be closer to the oracle's Fast result than to its full-dimensional
-result (err <= 0.5 * gap), and on the center-scaled variants, where the two
-differ widely, within a tenth of that gap.
+max|err| / max|ref| <= 1e-2 and LSE within 1e-3 absolute.
+
+Fast reads must also show that the Fast approximation, not the full read,
+was computed (the D-rule), on both outputs of the call:
+* LSE (fp32; depends on the K side: the truncated scores):
+  max|lse_gpu - lse_fast| <= 0.1 max|lse_full - lse_fast| on every Fast case;
+* output (bf16; the V side as well): max|out_gpu - out_fast| <= f gap with
+  gap = max|out_full - out_fast|.  f = 0.1 on the center-scaled variants
+  (centers x 0.05 on the reduced cases, x 0.01 at full size: coefficients
+  carry the signal and the gap is several percent of max|ref| or more).  On the plain generator the centers dominate: at full size
+  the gap is about one bf16 step of the output (C4: gap 5.0e-4 at
+  max|ref| ~ 0.12, where a bf16 step is 4.9e-4), so rounding the output
+  alone costs up to half of it; there f = 1 (closer to Fast than to Full),
+  and f = 0.25 on the reduced plain cases (measured <= 0.15).
 """
 import dataclasses
 
@@ -56,6 +66,10 @@ SMALL = {
              n_full_tail=0, r_low=0, seed=42),
     "S12": S("C3", H=3, r=320, A=40, n_hist=500, Nq=90, N_cur=33, chunk=250, r_low=64,
              n_full_tail=120, seed=43),
+    # full-size center-scaled variants of C2 and C4 (Fast and Full far apart:
+    # with centers x 0.01 the gap is ~14 % of max|ref|, 40x a bf16 half step)
+    "C2d": S("C2", name="C2d", center_scale=0.01),
+    "C4d": S("C4", name="C4d", center_scale=0.01),
     "C0f": S("C0", mode="fast", r_low=4, n_full_tail=32),
     "C0d": S("C0", mode="fast", r_low=4, n_full_tail=32, center_scale=0.05),
 }
@@ -168,6 +182,23 @@ def _oracle_attend(case, rows, fast, route, r_low, maps=None):
     return oracle.attend_fast(q, kb, vb, route, r_low, ck, cv, cfg.H, cfg.d, cfg.tau, maps=omaps)
 
 
+def _drule(name, case, rows, out, lse, ro, rl, f_out):
+    """D-rule: the GPU result sits near the oracle's Fast result, far from
+    its full read (see the module docstring)."""
+    cfg = case.cfg
+    q, ck, cv = oracle_inputs(case, rows)
+    fo, fl = oracle_full_chunked(q, oracle_branch(case, 0), oracle_branch(case, 1), ck, cv, cfg)
+    gap = float(np.max(np.abs(fo - ro)))
+    err = float(np.max(np.abs(out - ro)))
+    fin = np.isfinite(rl)
+    gap_l = float(np.max(np.abs(fl[fin] - rl[fin])))
+    err_l = float(np.max(np.abs(lse[fin] - rl[fin])))
+    log(f"  {name}: D-rule out: gap={gap:.3e} err={err:.3e} ratio={err / gap:.3e} (<= {f_out}); "
+        f"lse: gap={gap_l:.3e} err={err_l:.3e} ratio={err_l / gap_l:.3e} (<= 0.1)")
+    assert err <= f_out * gap
+    assert err_l <= 0.1 * gap_l
+
+
 def _check_attend(name, sample=None, route=None, r_low=None, drule=None):
     cfg = _cfg(name)
     case = get_case(cfg)
@@ -180,12 +211,7 @@ def _check_attend(name, sample=None, route=None, r_low=None, drule=None):
     log(f"  {name}: rows={len(rows)} max|err|/max|ref|={rel:.3e} max|dLSE|={lerr:.3e}")
     assert rel <= OUT_TOL and lerr <= LSE_TOL
     if fast and drule is not None:
-        q, ck, cv = oracle_inputs(case, rows)
-        fo, _ = oracle_full_chunked(q, oracle_branch(case, 0), oracle_branch(case, 1), ck, cv, cfg)
-        gap = float(np.max(np.abs(fo - ro)))
-        err = float(np.max(np.abs(out - ro)))
-        log(f"  {name}: fast-vs-full gap={gap:.3e} err={err:.3e} ratio={err / gap:.3e}")
-        assert err <= drule * gap
+        _drule(name, case, rows, out, lse, ro, rl, drule)
     return rel, lerr
 
 
@@ -194,9 +220,9 @@ def test_attend_full_small(name):
     _check_attend(name)
 
 
-@pytest.mark.parametrize("name,drule", [("C0f", 0.5), ("C0d", 0.1), ("S2", 0.5), ("S3", 0.5),
-                                        ("S2d", 0.1), ("S4", 0.5), ("S5", 0.5), ("S6", 0.5),
-                                        ("S7", 0.5), ("S8", 0.5), ("S12", 0.5)])
+@pytest.mark.parametrize("name,drule", [("C0f", 0.25), ("C0d", 0.1), ("S2", 0.25), ("S3", 0.25),
+                                        ("S2d", 0.1), ("S4", 0.25), ("S5", 0.25), ("S6", 0.25),
+                                        ("S7", 0.25), ("S8", 0.25), ("S12", 0.25)])
 def test_attend_fast_small(name, drule):
     _check_attend(name, drule=drule)
 
@@ -206,7 +232,7 @@ def test_attend_fast_small(name, drule):
 # of 16 sends the whole call through the generic kernels.
 @pytest.mark.parametrize("widths", [[32, 64, 96, 128], [128, 32, 32, 80], [24, 64, 96, 40]])
 def test_attend_fast_per_head_widths(widths):
-    _check_attend("S9", r_low=widths, drule=0.5)
+    _check_attend("S9", r_low=widths, drule=0.25)
 
 
 def test_per_head_equal_widths_match_uniform():
@@ -231,11 +257,11 @@ def _anchor_route(n_chunks, chunk, recent=4, every=16):
 def test_attend_fast_anchor_routing_per_head():
     route = _anchor_route(20, 100, recent=4, every=8)
     assert sum(m == 0 for _, _, m in route) >= 3   # anchors split the low history
-    _check_attend("S10", route=route, r_low=[32, 96, 64, 128], drule=0.5)
+    _check_attend("S10", route=route, r_low=[32, 96, 64, 128], drule=0.25)
 
 
 def test_attend_fast_C3_table6_widths():
-    _check_attend("C3", sample=40, r_low=[32, 64, 96, 128] * 6, drule=0.5)
+    _check_attend("C3", sample=40, r_low=[32, 64, 96, 128] * 6, drule=1.0)
 
 
 def _adapted_maps(cfg, ld, eps=1.0, seed=5):
@@ -364,18 +390,20 @@ def test_low_read_center_range_splits_with_empty_ranges():
 
 
 def test_attend_full_C1():
-    _check_attend("C1", sample=48)
+    # every query row of the full read against the oracle
+    _check_attend("C1", sample=None)
 
 
-@pytest.mark.parametrize("name", ["C2", "C3"])
-def test_attend_fast_full_size(name):
-    _check_attend(name, sample=40, drule=0.5)
+@pytest.mark.parametrize("name,drule", [("C2", 1.0), ("C3", 1.0), ("C2d", 0.1)])
+def test_attend_fast_full_size(name, drule):
+    _check_attend(name, sample=40, drule=drule)
 
 
-def test_encode_append_attend_C4():
+@pytest.mark.parametrize("name,drule", [("C4", 1.0), ("C4d", 0.1)])
+def test_encode_append_attend_C4(name, drule):
     """Long-rollout step: encode the new chunk into the preallocated history
     on the GPU, then the Fast read over the 33-chunk history."""
-    cfg = synth.CONFIGS["C4"]
+    cfg = _cfg(name)
     case = get_case(cfg)
     shape = shape_of(cfg)
     w = case.w
@@ -406,8 +434,9 @@ def test_encode_append_attend_C4():
     out, lse = from_dev(out)[rows], from_dev(lse)[rows]
     ro, rl = _oracle_attend(case, rows, True, cfg.segments(), cfg.r_low)
     rel, lerr = attention_errors(out, lse, ro, rl)
-    log(f"  C4: max|err|/max|ref|={rel:.3e} max|dLSE|={lerr:.3e}")
+    log(f"  {name}: rows={len(rows)} max|err|/max|ref|={rel:.3e} max|dLSE|={lerr:.3e}")
     assert rel <= OUT_TOL and lerr <= LSE_TOL
+    _drule(name, case, rows, out, lse, ro, rl, drule)
 
 
 # --------------------------------------------------------------------------

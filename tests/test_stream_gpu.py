@@ -1,11 +1,10 @@
 """Stream semantics of the Fast read.
 
-With per-head widths the library runs the full-dimensional half of a Fast
-read (decode + flash attention) on a second stream of its own, forked from
-the caller's stream and joined back into it before the LSE merge.  The result
-must be complete once the caller's stream is, whichever stream that is, and
-the call must capture into a HIP graph whose replays reproduce the eager
-result.  One width for every head (one stream) is checked the same way.
+Every kernel of a call runs on the caller's stream (the library creates no
+streams or events of its own): the result must be complete once that stream
+is, whichever stream it is, and the call must capture into a HIP graph whose
+replays reproduce the eager result.  Both the per-head-width call (several
+low-dimensional passes) and the one-width call are checked.
 """
 import pytest
 import torch
