@@ -108,6 +108,7 @@ def load() -> ctypes.CDLL:
         "nkv_force_generic": (None, [ctypes.c_int]),
         "nkv_encode_workspace_size": (SZ, [SH, I64, I32]),
         "nkv_encode": (ctypes.c_int, [SH, P, I64, P, I32, P, P, P, P, P, SZ, P]),
+        "nkv_encode_noalloc": (ctypes.c_int, [SH, P, I64, P, I32, P, P, P, P, P]),
         "nkv_attend_workspace_size": (SZ, [SH, I32, I32, I64, SG, I32, I32, I64, I64]),
         "nkv_attend_full": (ctypes.c_int, [SH, BR, BR, I64, P, I64, P, P, I64, P, P, P, SZ, P]),
         "nkv_attend_fast": (ctypes.c_int, [SH, BR, BR, I64, SG, I32, I32, P, I64, P, P, I64, P,
@@ -148,7 +149,9 @@ EXPORTS = ("nkv_version", "nkv_last_error", "nkv_status_string", "nkv_force_gene
            "nkv_attend_fast_heads", "nkv_attend_maps_workspace_size", "nkv_attend_fast_maps",
            "nkv_lse_merge", "nkv_fit_workspace_size", "nkv_fit_centers", "nkv_route_segments", "nkv_storage_account",
            "nkv_layer_attend_workspace_size", "nkv_layer_attend", "nkv_layer_append_workspace_size",
-           "nkv_layer_append", "nkv_profile_enable", "nkv_profile_read")
+           "nkv_layer_append", "nkv_profile_enable", "nkv_profile_read", "nkv_encode_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # NKV_NOALLOC_SCRATCH_BYTES
 
 
 def _check(status: int):
@@ -259,6 +262,14 @@ def nkv_encode(shape: Shape, x, centers, encoder, idx, codes, scales, ws=None, s
                              int(centers.shape[0]), _ptr(encoder), _ptr(idx), _ptr(codes),
                              _ptr(scales), _ptr(ws), 0 if ws is None else ws.numel(),
                              _stream(stream)))
+
+
+def nkv_encode_noalloc(shape: Shape, x, centers, encoder, idx, codes, scales, stream=None):
+    """nkv_encode with the library's fixed device scratch: no workspace."""
+    N = int(x.shape[0]) if x is not None else 0
+    _check(load().nkv_encode_noalloc(ctypes.byref(shape.c()), _ptr(x), N, _ptr(centers),
+                                     int(centers.shape[0]), _ptr(encoder), _ptr(idx), _ptr(codes),
+                                     _ptr(scales), _stream(stream)))
 
 
 def nkv_attend_workspace_size(shape: Shape, A_k: int, A_v: int, N_hist: int, route, r_low: int,

@@ -234,6 +234,29 @@ nkv_status nkv_attend_fast_maps(const nkv_shape* shape, const nkv_branch* k,
                                 float* lse, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/* Scratch bytes of nkv_encode_noalloc's fixed device array (32 MiB). */
+#define NKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * nkv_encode without a workspace and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * results as nkv_encode (bit for bit: the same kernels run), with the
+ * scratch taken from a fixed device array of NKV_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends.
+ * Limit: calls whose nkv_encode_workspace_size exceeds that size return
+ * NKV_EUNSUPPORTED before touching the device (at W = 3072, A = 1024,
+ * r = 384 a 4680-token chunk needs 21.5 MiB and about 6900 tokens fit;
+ * split larger inputs into several calls).  Every call
+ * on one GPU shares the array: calls that overlap on one GPU (several
+ * streams or host threads) race and must be serialised by the caller.
+ * Nothing of an earlier call's contents is read.
+ */
+nkv_status nkv_encode_noalloc(const nkv_shape* shape, const void* x, int64_t N,
+                              const void* centers, int32_t A,
+                              const void* encoder, int32_t* idx,
+                              uint8_t* codes, uint16_t* scales, void* stream);
+
 /*
  * LSE merge of two partial attentions over disjoint key sets (Figure 4(d)):
  *   L = log(exp(L_a) + exp(L_b)),  O = exp(L_a - L) O_a + exp(L_b - L) O_b.
