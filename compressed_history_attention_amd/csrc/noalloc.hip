@@ -2,8 +2,8 @@
 // callers that cannot allocate device memory (code under HIP graph capture,
 // tight serving loops, harnesses that forbid hipMalloc).
 //
-// The encoder's scratch (center norms, per-slot nearest-center records, the
-// flagged-token list, projection partial sums) lives in one fixed device
+// The encoder's scratch (center norms, per-slot nearest-center records,
+// projection partial sums) lives in one fixed device
 // array of this library, `scratch`, NKV_NOALLOC_SCRATCH_BYTES long.  Every
 // GPU the library runs on holds its own copy until the process ends.  Its
 // device address is looked up once per device (hipGetSymbolAddress, with

@@ -6,11 +6,11 @@
 //      products are exact in fp32); the epilogue reduces each token's
 //      column over the wave's 64 centers to (min distance, lowest index)
 //      and the runner-up distance, one record per 64-center slot.  A
-//      per-token pass takes the best record and flags the token when the
-//      runner-up lies within a rigorous bound on the fp32 rounding error of
-//      the two distances; flagged tokens are assigned again in fp64 (the
-//      same ||mu||^2 - 2 mu . x form), so the argmin is the one exact
-//      arithmetic gives, ties to the lowest index.
+//      per-token pass takes the best record; when the runner-up lies within
+//      a rigorous bound on the fp32 rounding error of the two distances it
+//      assigns the token again in fp64 (the same ||mu||^2 - 2 mu . x form),
+//      so the argmin is the one exact arithmetic gives, ties to the lowest
+//      index.
 //   3. Projection GEMM z = E (x - mu_a): the fp32 residual (exact for bf16
 //      inputs) is split into three bf16 terms hi + mid + lo = e, so three
 //      exact-product MFMA passes with fp32 accumulation give the projection
@@ -28,149 +28,149 @@ namespace nkv {
 // ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------
-__global__ void k_center_norms(const uint16_t* __restrict__ mu, int A, int W, float* __restrict__ out,
-                               uint32_t* __restrict__ max_bits) {
-  const int a = blockIdx.x;
-  const uint16_t* row = mu + (int64_t)a * W;
-  float acc = 0.f;
-  // lane l adds elements l, l + 64, ... in that order; eight loads are
-  // issued before their FMAs (the same sums, without one round trip each)
-  int w = threadIdx.x;
-  for (; w + 7 * 64 < W; w += 8 * 64) {
-    uint16_t b[8];
+// ||mu_a||^2 per center (fp32), 16 centers per block (one per wave in four
+// rounds), 16-byte loads; each block also writes the largest of its norms,
+// so the assignment's error bound needs no atomics and no cleared counter.
+constexpr int NORM_CPB = 16;
+__global__ __launch_bounds__(256) void k_center_norms(const uint16_t* __restrict__ mu, int A, int W,
+                                                      float* __restrict__ out,
+                                                      float* __restrict__ block_max) {
+  __shared__ float smax[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float mx = 0.f;
+  for (int k = 0; k < NORM_CPB / 4; ++k) {
+    const int a = blockIdx.x * NORM_CPB + k * 4 + wave;
+    if (a >= A) break;  // wave-uniform
+    const uint16_t* row = mu + (int64_t)a * W;
+    float acc = 0.f;
+    for (int w = 8 * lane; w < W; w += 512) {  // W % 8 == 0 on this path
+      const u32x4 v = ld_u32x4(row + w);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) b[u] = row[w + 64 * u];
+      for (int u = 0; u < 4; ++u) {
+        const float lo = bf16_bits_to_f32(uint16_t(v[u] & 0xffffu));
+        const float hi = bf16_bits_to_f32(uint16_t(v[u] >> 16));
+        acc = fmaf(lo, lo, fmaf(hi, hi, acc));
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) out[a] = acc;
+    mx = fmaxf(mx, acc);
+  }
+  if (lane == 0) smax[wave] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    block_max[blockIdx.x] = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+}
+
+// Per token (one wave each): the best of its slot records (lowest distance,
+// then lowest index) and the runner-up distance over all centers.  The
+// computed distance of center a differs from the exact ||mu_a||^2 -
+// 2 mu_a . x by at most g (||mu_a||^2 + 2 ||mu_a|| ||x||) + u |d_a|
+// (g = (W + 64) u / (1 - (W + 64) u), u = 2^-24: fp32 sums of W exact
+// products, the fp32 norm, one rounding of the difference).  With
+// M = max_a ||mu_a|| the bound E = 2 (g + u) (M^2 + 2 M ||x||) covers any two
+// centers; when the runner-up is more than E above the best, no other center
+// can be nearer (or tie) in exact arithmetic.  Otherwise the wave assigns
+// the token again in fp64: d(a) = ||mu_a||^2 - 2 mu_a . x with exact bf16
+// products summed in fp64, lowest index on ties.  (M and ||x|| are inflated
+// by 1 % for their own rounding; ||x||^2 is summed here from 16-byte loads.)
+__global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restrict__ best,
+                                                       const float* __restrict__ second, int nslot,
+                                                       int64_t N, int W,
+                                                       const uint16_t* __restrict__ x,
+                                                       const uint16_t* __restrict__ mu, int A,
+                                                       const float* __restrict__ block_max,
+                                                       int nblock_max,
+                                                       int32_t* __restrict__ idx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;  // whole waves; no block barrier below
+  // ||x_t||^2 (W % 8 == 0 on this path)
+  const uint16_t* row = x + t * W;
+  float xs = 0.f;
+  for (int w = 8 * lane; w < W; w += 512) {
+    const u32x4 v = ld_u32x4(row + w);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float v = bf16_bits_to_f32(b[u]);
-      acc = fmaf(v, v, acc);
+    for (int k = 0; k < 4; ++k) {
+      const float lo = bf16_bits_to_f32(uint16_t(v[k] & 0xffffu));
+      const float hi = bf16_bits_to_f32(uint16_t(v[k] >> 16));
+      xs = fmaf(lo, lo, fmaf(hi, hi, xs));
     }
   }
-  for (; w < W; w += 64) {
-    const float v = bf16_bits_to_f32(row[w]);
-    acc = fmaf(v, v, acc);
-  }
-  acc = wave_sum(acc);
-  if (threadIdx.x == 0) {
-    out[a] = acc;
-    if (max_bits) atomicMax(max_bits, ordered_bits(acc));
-  }
-}
-
-// ||mu_a||^2 in fp64 (squares of bf16 values are exact), for the exact
-// re-assignment of flagged tokens
-__global__ void k_center_norms64(const uint16_t* __restrict__ mu, int W, double* __restrict__ out) {
-  const uint16_t* row = mu + (int64_t)blockIdx.x * W;
-  double acc = 0.0;
-  for (int w = threadIdx.x; w < W; w += 64) {
-    const double v = bf16_bits_to_f32(row[w]);
-    acc = fma(v, v, acc);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (threadIdx.x == 0) out[blockIdx.x] = acc;
-}
-
-__global__ void k_fill_u64(uint64_t* p, int64_t n, uint64_t v) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
-// Per token: the best of its slot records (lowest distance, then lowest
-// index) and the runner-up distance over all centers.  The computed
-// distance of center a differs from the exact ||mu_a||^2 - 2 mu_a . x by
-// at most g (||mu_a||^2 + 2 ||mu_a|| ||x||) + u |d_a| (g = (W + 64) u /
-// (1 - (W + 64) u), u = 2^-24: fp32 sums of W exact products, the fp32
-// norm, one rounding of the difference).  With M = max_a ||mu_a|| the
-// bound E = 2 (g + u) (M^2 + 2 M ||x||) covers both candidates; when the
-// runner-up is more than E above the best, no other center can be nearer
-// (or tie) in exact arithmetic.  Otherwise the token joins the list for
-// the fp64 assignment.  (Bounds are inflated by 1 % for the rounding of
-// the norms themselves.)
-__global__ void k_argmin_reduce(const uint64_t* __restrict__ best, const float* __restrict__ second,
-                                int nslot, int64_t N, int W, const float* __restrict__ xnorm2,
-                                const uint32_t* __restrict__ mu_max_bits, int32_t* __restrict__ idx,
-                                int32_t* __restrict__ flagged, int32_t* __restrict__ nflag) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= N) return;
-  uint64_t bk = best[t];
-  float bsec = second[t];
-  float other = INFINITY;  // best distance of every slot but the winner's
-  for (int sl = 1; sl < nslot; ++sl) {
+  xs = wave_sum(xs);
+  float m2 = 0.f;  // max ||mu||^2 from the per-block maxima
+  for (int i = lane; i < nblock_max; i += 64) m2 = fmaxf(m2, block_max[i]);
+  m2 = wave_max(m2);
+  // slot records: lane sl holds slot sl (and sl + 64, ...)
+  uint64_t bk = ~0ull;
+  float sec = INFINITY, oth = INFINITY;
+  for (int sl = lane; sl < nslot; sl += 64) {
     const uint64_t k = best[(int64_t)sl * N + t];
     const float sc = second[(int64_t)sl * N + t];
     if (k < bk) {
-      other = fminf(other, from_ordered_bits(uint32_t(bk >> 32)));
+      if (bk != ~0ull) oth = fminf(oth, from_ordered_bits(uint32_t(bk >> 32)));
       bk = k;
-      bsec = sc;
+      sec = sc;
     } else {
-      other = fminf(other, from_ordered_bits(uint32_t(k >> 32)));
+      oth = fminf(oth, from_ordered_bits(uint32_t(k >> 32)));
+    }
+  }
+  // merge across lanes: the winner's own runner-up, everybody else's best
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t k2 = __shfl_xor(bk, o, 64);
+    const float s2 = __shfl_xor(sec, o, 64), o2 = __shfl_xor(oth, o, 64);
+    const float d_me = bk == ~0ull ? INFINITY : from_ordered_bits(uint32_t(bk >> 32));
+    const float d_ot = k2 == ~0ull ? INFINITY : from_ordered_bits(uint32_t(k2 >> 32));
+    if (k2 < bk) {
+      oth = fminf(fminf(oth, o2), d_me);
+      bk = k2;
+      sec = s2;
+    } else {
+      oth = fminf(fminf(oth, o2), d_ot);
     }
   }
   const float d1 = from_ordered_bits(uint32_t(bk >> 32));
-  const float d2 = fminf(other, bsec);
+  const float d2 = fminf(oth, sec);
   const float u = 5.9604645e-8f;  // 2^-24
   const float kw = (float)(W + 64) * u;
   const float g = kw / (1.f - kw);
-  const float M = sqrtf(from_ordered_bits(*mu_max_bits)) * 1.01f;
-  const float X = sqrtf(fmaxf(xnorm2[t], 0.f)) * 1.01f;
+  const float M = sqrtf(m2) * 1.01f;
+  const float X = sqrtf(xs) * 1.01f;
   const float E = 2.f * (g + u) * (M * M + 2.f * M * X);
-  idx[t] = (int32_t)(bk & 0xffffffffu);
-  // (a NaN or infinite distance compares false: such tokens are re-assigned too)
-  if (!(d2 - d1 > E)) flagged[atomicAdd(nflag, 1)] = (int32_t)t;
-}
-
-// fp64 assignment of the flagged tokens: d(a) = ||mu_a||^2 - 2 mu_a . x with
-// exact bf16 products summed in fp64; lowest index on ties.  One block per
-// listed token (grid-stride over the list), wave w scanning centers
-// a = w, w + 4, ...
-__global__ __launch_bounds__(256) void k_argmin_exact(const uint16_t* __restrict__ x, int W,
-                                                      const uint16_t* __restrict__ mu, int A,
-                                                      const double* __restrict__ mu2,
-                                                      const int32_t* __restrict__ flagged,
-                                                      const int32_t* __restrict__ nflag,
-                                                      int32_t* __restrict__ idx) {
-  extern __shared__ float xs[];  // the token's row (W values, exact)
-  __shared__ double bd_s[4];
-  __shared__ int ba_s[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = *nflag;
-  for (int i = blockIdx.x; i < n; i += gridDim.x) {
-    const int64_t t = flagged[i];
-    __syncthreads();  // the previous token's reads of xs are done
-    for (int w = threadIdx.x; w < W; w += 256) xs[w] = bf16_bits_to_f32(x[t * W + w]);
-    __syncthreads();
+  int32_t a_out = (int32_t)(bk & 0xffffffffu);
+  // (a NaN or infinite distance compares false: such tokens are assigned again too)
+  if (!(d2 - d1 > E)) {
+    // fp64 assignment, the lane's channels w = 8 lane + 512 k .. + 7
     double bd = INFINITY;
     int ba = 0x7fffffff;
-    for (int a = wave; a < A; a += 4) {
-      const uint16_t* row = mu + (int64_t)a * W;
-      double acc = 0.0;
-      for (int w = lane; w < W; w += 64)
-        acc = fma((double)xs[w], (double)bf16_bits_to_f32(row[w]), acc);
+    for (int a = 0; a < A; ++a) {
+      const uint16_t* mrow = mu + (int64_t)a * W;
+      double mm = 0.0, dot = 0.0;
+      for (int w = 8 * lane; w < W; w += 512) {
+        const u32x4 xv = ld_u32x4(row + w), mv = ld_u32x4(mrow + w);
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      const double dist = mu2[a] - 2.0 * acc;
-      if (dist < bd) {  // a increases within the wave: strict < keeps the lowest
+        for (int k = 0; k < 8; ++k) {
+          const double xe = bf16_bits_to_f32(uint16_t(xv[k >> 1] >> (16 * (k & 1))));
+          const double me = bf16_bits_to_f32(uint16_t(mv[k >> 1] >> (16 * (k & 1))));
+          mm = fma(me, me, mm);
+          dot = fma(xe, me, dot);
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        mm += __shfl_xor(mm, o, 64);
+        dot += __shfl_xor(dot, o, 64);
+      }
+      const double dist = mm - 2.0 * dot;
+      if (dist < bd) {  // a increases: strict < keeps the lowest index
         bd = dist;
         ba = a;
       }
     }
-    if (lane == 0) {
-      bd_s[wave] = bd;
-      ba_s[wave] = ba;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double d0 = bd_s[0];
-      int a0 = ba_s[0];
-      for (int k = 1; k < 4; ++k)
-        if (bd_s[k] < d0 || (bd_s[k] == d0 && ba_s[k] < a0)) {
-          d0 = bd_s[k];
-          a0 = ba_s[k];
-        }
-      idx[t] = a0;
-    }
+    a_out = ba;
   }
+  if (lane == 0) idx[t] = a_out;
 }
 
 __device__ __forceinline__ u32x4 load8_bf16(const uint16_t* base, int64_t row, int ld, int k,
@@ -471,10 +471,10 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
 }
 
 namespace {
-// workspace of the assignment: ||mu||^2 (fp32 and fp64), slot records,
-// token norms, the flagged-token list with its count and the max norm
+// workspace of the assignment: ||mu||^2, per-block maxima of it, slot records
 struct AssignLayout {
-  size_t mu2, mu2d, best, second, xn, list, misc, total;
+  size_t mu2, bmax, best, second, total;
+  int nbmax;
 };
 AssignLayout assign_layout(int64_t N, int32_t A) {
   AssignLayout L{};
@@ -485,13 +485,11 @@ AssignLayout assign_layout(int64_t N, int32_t A) {
     off = align_up(off + bytes, 256);
     return o;
   };
+  L.nbmax = (int)ceil_div(A, NORM_CPB);
   L.mu2 = take(sizeof(float) * A);
-  L.mu2d = take(sizeof(double) * A);
+  L.bmax = take(sizeof(float) * L.nbmax);
   L.best = take(sizeof(uint64_t) * nslot * N);
   L.second = take(sizeof(float) * nslot * N);
-  L.xn = take(sizeof(float) * N);
-  L.list = take(sizeof(int32_t) * N);
-  L.misc = take(sizeof(uint32_t) * 2);  // flagged count, max ||mu||^2 bits
   L.total = off;
   return L;
 }
@@ -504,37 +502,21 @@ nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void
   const int W = s->H * s->d;
   const AssignLayout L = assign_layout(N, A);
   float* mu2 = reinterpret_cast<float*>(ws + L.mu2);
-  double* mu2d = reinterpret_cast<double*>(ws + L.mu2d);
+  float* bmax = reinterpret_cast<float*>(ws + L.bmax);
   uint64_t* best = reinterpret_cast<uint64_t*>(ws + L.best);
   float* second = reinterpret_cast<float*>(ws + L.second);
-  float* xn = reinterpret_cast<float*>(ws + L.xn);
-  int32_t* list = reinterpret_cast<int32_t*>(ws + L.list);
-  uint32_t* misc = reinterpret_cast<uint32_t*>(ws + L.misc);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* mub = static_cast<const uint16_t*>(centers);
-  hipLaunchKernelGGL(k_fill_u64, dim3(1), dim3(64), 0, st, reinterpret_cast<uint64_t*>(misc), 1,
-                     0ull);
-  NKV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_center_norms, dim3(A), dim3(64), 0, st, mub, A, W, mu2, misc + 1);
-  NKV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_center_norms, dim3((unsigned)N), dim3(64), 0, st, xb, (int)N, W, xn,
-                     nullptr);
+  hipLaunchKernelGGL(k_center_norms, dim3((unsigned)L.nbmax), dim3(256), 0, st, mub, A, W, mu2,
+                     bmax);
   NKV_LAUNCH_CHECK();
   DistProblem dp{A, (int)N, W, mub, xb, mu2, best, second};
   nkv_status e;
   // (the register-staged GEMM with 64-wide k steps: measured faster here
   // than the direct-to-LDS one, whose 32-wide steps double the barriers)
   if ((e = launch_gemm(dp, 1, st))) return e;
-  hipLaunchKernelGGL(k_argmin_reduce, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, best,
-                     second, (int)ceil_div(A, 64), N, W, xn, misc + 1, idx, list,
-                     reinterpret_cast<int32_t*>(misc));
-  NKV_LAUNCH_CHECK();
-  hipLaunchKernelGGL(k_center_norms64, dim3(A), dim3(64), 0, st, mub, W, mu2d);
-  NKV_LAUNCH_CHECK();
-  // the list is usually empty: a few blocks walk whatever it holds
-  hipLaunchKernelGGL(k_argmin_exact, dim3((unsigned)std::min<int64_t>(N, 256)), dim3(256),
-                     sizeof(float) * W, st, xb, W, mub, A, mu2d, list,
-                     reinterpret_cast<const int32_t*>(misc), idx);
+  hipLaunchKernelGGL(k_argmin_reduce, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st, best,
+                     second, (int)ceil_div(A, 64), N, W, xb, mub, A, bmax, L.nbmax, idx);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }
