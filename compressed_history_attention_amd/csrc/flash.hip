@@ -42,7 +42,8 @@ template <bool OUT_F32, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_flash(const uint16_t* __restrict__ Q, int64_t Nq, int H,
                                                   float c, const uint16_t* __restrict__ K,
                                                   const uint16_t* __restrict__ VT, int64_t Nk,
-                                                  int64_t ld, int nsplit, void* __restrict__ out,
+                                                  int64_t ld, int nsplit, int ragged_last,
+                                                  void* __restrict__ out,
                                                   float* __restrict__ lse) {
   // one array per stage and operand: the stage of every LDS access is static
   __shared__ __attribute__((aligned(1024))) char sK0[FA_KB];
@@ -61,10 +62,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_flash(const uint16_t* __res
   const int per = (nunits + 7) / 8;
   const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (u >= nunits) return;  // the whole block, before any barrier
-  const int h = (u / nqb) % H;
+  // within a split, the ragged last query block of every head comes after
+  // all full blocks, so that these shorter blocks fill the last round
   const int split = u / (nqb * H);  // key-range split (partials merged later)
+  const int rnk = u - split * nqb * H;
+  int h, qb;
+  if (ragged_last && nqb > 1 && rnk >= (nqb - 1) * H) {
+    qb = nqb - 1;
+    h = rnk - (nqb - 1) * H;
+  } else {
+    const int nq = ragged_last && nqb > 1 ? nqb - 1 : nqb;
+    qb = rnk % nq;
+    h = rnk / nq;
+  }
   const int W = H * 128;
-  const int64_t q0 = (int64_t)(u % nqb) * QB + wave * 32;
+  const int64_t q0 = (int64_t)qb * QB + wave * 32;
   const int64_t qrow = q0 + (lane & 31);
   const bool qok = qrow < Nq;
 
@@ -292,18 +304,19 @@ nkv_status launch_flash(const uint16_t* q, int64_t Nq, int H, float tau, const u
   const int nw = wide ? 8 : 4;
   const int64_t units = ceil_div(Nq, 32 * nw) * H * nsplit;
   const dim3 grid((unsigned)(ceil_div(units, 8) * 8)), block((unsigned)(64 * nw));
+  const int ragged = Nq % (32 * nw) != 0 ? 1 : 0;
   if (out_f32 && wide)
     hipLaunchKernelGGL((k_flash<true, 8>), grid, block, 0, st, q, Nq, H, c, kall, vt, Nk, ld, nsplit,
-                       out, lse);
+                       ragged, out, lse);
   else if (out_f32)
     hipLaunchKernelGGL((k_flash<true, 4>), grid, block, 0, st, q, Nq, H, c, kall, vt, Nk, ld, nsplit,
-                       out, lse);
+                       ragged, out, lse);
   else if (wide)
     hipLaunchKernelGGL((k_flash<false, 8>), grid, block, 0, st, q, Nq, H, c, kall, vt, Nk, ld,
-                       nsplit, out, lse);
+                       nsplit, ragged, out, lse);
   else
     hipLaunchKernelGGL((k_flash<false, 4>), grid, block, 0, st, q, Nq, H, c, kall, vt, Nk, ld,
-                       nsplit, out, lse);
+                       nsplit, ragged, out, lse);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }

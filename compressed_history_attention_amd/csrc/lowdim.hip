@@ -683,6 +683,7 @@ struct MainArgs {
   int H, A_k, A_v, GK, GV, NB, r_low, ra;
   int gvsplit;  // key-range splits at a^V-range boundaries
   int nqb, nsplit;  // query blocks and key-range splits (work unit = (query block, head, split))
+  int ragged_last;  // the last query block holds fewer than 256 rows
   float c;
   HeadSet hs;  // heads of the group
 };
@@ -772,8 +773,20 @@ __global__ __launch_bounds__(512, 1) void k_low_rows(const MainArgs a) {
   const int per = (nunits + 7) / 8;
   const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (u >= nunits) return;  // the whole block, before any barrier
-  const int bx = u % a.nqb, by = (u / a.nqb) % a.hs.n;
+  // Within a split, the ragged last query block of every head comes after
+  // all full blocks: each XCD runs its units in order, and the few-row
+  // blocks (fewer active waves, shorter) then fill the last round.
   const int split = u / (a.nqb * a.hs.n), nsplit = a.nsplit;
+  const int rnk = u - split * a.nqb * a.hs.n;
+  int bx, by;
+  if (a.ragged_last && a.nqb > 1 && rnk >= (a.nqb - 1) * a.hs.n) {
+    bx = a.nqb - 1;
+    by = rnk - (a.nqb - 1) * a.hs.n;
+  } else {
+    const int nq = a.ragged_last && a.nqb > 1 ? a.nqb - 1 : a.nqb;
+    bx = rnk % nq;
+    by = rnk / nq;
+  }
   const int h = a.hs.h[by];
   const int W = a.H * 128;
   const int64_t q0 = (int64_t)bx * RBW;
@@ -1481,7 +1494,8 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   ProfScope ps_main("low_main", st);
   MainArgs m{q, static_cast<const uint16_t*>(kb.centers), qt16, bound, img, tile_start,
              tile_bucket, acc, wmass, ell, Nq, H, kb.A, vb.A, P.GK, P.GV, P.NB, r_low, ra,
-             split.gv ? 1 : 0, (int)ceil_div(Nq, RBW), nsplit, c, hs};
+             split.gv ? 1 : 0, (int)ceil_div(Nq, RBW), nsplit,
+             Nq % RBW != 0 ? 1 : 0, c, hs};
   switch (rlp) {
     case 16: e = launch_main<16>(m, st); break;
     case 32: e = launch_main<32>(m, st); break;
