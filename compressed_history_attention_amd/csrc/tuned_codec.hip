@@ -75,8 +75,8 @@ __global__ __launch_bounds__(256) void k_center_norms(const uint16_t* __restrict
 // products summed in fp64, lowest index on ties.  (M and ||x|| are inflated
 // by 1 % for their own rounding; ||x||^2 is summed here from 16-byte loads.)
 __global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restrict__ best,
-                                                       const float* __restrict__ second, int nslot,
-                                                       int64_t N, int W,
+                                                       const uint64_t* __restrict__ second,
+                                                       int nslot, int64_t N, int W,
                                                        const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ mu, int A,
                                                        const float* __restrict__ block_max,
@@ -101,37 +101,31 @@ __global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restric
   float m2 = 0.f;  // max ||mu||^2 from the per-block maxima
   for (int i = lane; i < nblock_max; i += 64) m2 = fmaxf(m2, block_max[i]);
   m2 = wave_max(m2);
-  // slot records: lane sl holds slot sl (and sl + 64, ...)
-  uint64_t bk = ~0ull;
-  float sec = INFINITY, oth = INFINITY;
+  auto dist_of = [](uint64_t k) { return from_ordered_bits(uint32_t(k >> 32)); };
+  // nearest over all slots, and the nearest of everything else (every other
+  // slot's nearest, the winning slot's runner-up): lane sl holds slots sl,
+  // sl + 64, ...
+  uint64_t bk = ~0ull, sk = ~0ull;
   for (int sl = lane; sl < nslot; sl += 64) {
     const uint64_t k = best[(int64_t)sl * N + t];
-    const float sc = second[(int64_t)sl * N + t];
+    const uint64_t k2 = second[(int64_t)sl * N + t];
     if (k < bk) {
-      if (bk != ~0ull) oth = fminf(oth, from_ordered_bits(uint32_t(bk >> 32)));
+      sk = bk < k2 ? bk : k2;
       bk = k;
-      sec = sc;
     } else {
-      oth = fminf(oth, from_ordered_bits(uint32_t(k >> 32)));
+      sk = sk < k ? sk : k;
     }
   }
-  // merge across lanes: the winner's own runner-up, everybody else's best
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t k2 = __shfl_xor(bk, o, 64);
-    const float s2 = __shfl_xor(sec, o, 64), o2 = __shfl_xor(oth, o, 64);
-    const float d_me = bk == ~0ull ? INFINITY : from_ordered_bits(uint32_t(bk >> 32));
-    const float d_ot = k2 == ~0ull ? INFINITY : from_ordered_bits(uint32_t(k2 >> 32));
-    if (k2 < bk) {
-      oth = fminf(fminf(oth, o2), d_me);
-      bk = k2;
-      sec = s2;
-    } else {
-      oth = fminf(fminf(oth, o2), d_ot);
-    }
+    const uint64_t ob = __shfl_xor(bk, o, 64), os = __shfl_xor(sk, o, 64);
+    const uint64_t lose = bk < ob ? ob : bk;
+    const uint64_t s1 = sk < os ? sk : os;
+    sk = s1 < lose ? s1 : lose;
+    bk = bk < ob ? bk : ob;
   }
-  const float d1 = from_ordered_bits(uint32_t(bk >> 32));
-  const float d2 = fminf(oth, sec);
+  const float d1 = dist_of(bk);
+  const float d2 = sk == ~0ull ? INFINITY : dist_of(sk);
   const float u = 5.9604645e-8f;  // 2^-24
   const float kw = (float)(W + 64) * u;
   const float g = kw / (1.f - kw);
@@ -141,33 +135,53 @@ __global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restric
   int32_t a_out = (int32_t)(bk & 0xffffffffu);
   // (a NaN or infinite distance compares false: such tokens are assigned again too)
   if (!(d2 - d1 > E)) {
-    // fp64 assignment, the lane's channels w = 8 lane + 512 k .. + 7
+    // fp64 assignment, the lane's channels w = 8 lane + 512 k .. + 7.  The
+    // exact nearest center has a computed distance within E of d1: in each
+    // 64-center slot whose nearest is that close, the nearest is a
+    // candidate, and so is every center of the slot if its runner-up is
+    // that close too.  Candidates are met in increasing center order (ties
+    // keep the lowest index); every center when none is found (non-finite
+    // distances).
     double bd = INFINITY;
     int ba = 0x7fffffff;
-    for (int a = 0; a < A; ++a) {
-      const uint16_t* mrow = mu + (int64_t)a * W;
-      double mm = 0.0, dot = 0.0;
-      for (int w = 8 * lane; w < W; w += 512) {
-        const u32x4 xv = ld_u32x4(row + w), mv = ld_u32x4(mrow + w);
+    auto scan = [&](int a0, int a1) {
+      for (int a = a0; a < a1; ++a) {
+        const uint16_t* mrow = mu + (int64_t)a * W;
+        double mm = 0.0, dot = 0.0;
+        for (int w = 8 * lane; w < W; w += 512) {
+          const u32x4 xv = ld_u32x4(row + w), mv = ld_u32x4(mrow + w);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const double xe = bf16_bits_to_f32(uint16_t(xv[k >> 1] >> (16 * (k & 1))));
-          const double me = bf16_bits_to_f32(uint16_t(mv[k >> 1] >> (16 * (k & 1))));
-          mm = fma(me, me, mm);
-          dot = fma(xe, me, dot);
+          for (int k = 0; k < 8; ++k) {
+            const double xe = bf16_bits_to_f32(uint16_t(xv[k >> 1] >> (16 * (k & 1))));
+            const double me = bf16_bits_to_f32(uint16_t(mv[k >> 1] >> (16 * (k & 1))));
+            mm = fma(me, me, mm);
+            dot = fma(xe, me, dot);
+          }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          mm += __shfl_xor(mm, o, 64);
+          dot += __shfl_xor(dot, o, 64);
+        }
+        const double dist = mm - 2.0 * dot;
+        if (dist < bd) {  // a increases: strict < keeps the lowest index
+          bd = dist;
+          ba = a;
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        mm += __shfl_xor(mm, o, 64);
-        dot += __shfl_xor(dot, o, 64);
-      }
-      const double dist = mm - 2.0 * dot;
-      if (dist < bd) {  // a increases: strict < keeps the lowest index
-        bd = dist;
-        ba = a;
+    };
+    const float lim = d1 + E;
+    for (int sl = 0; sl < nslot; ++sl) {
+      const uint64_t kb = best[(int64_t)sl * N + t], ks = second[(int64_t)sl * N + t];
+      if (!(dist_of(kb) <= lim)) continue;
+      if (ks != ~0ull && dist_of(ks) <= lim) {
+        scan(sl * 64, min(A, sl * 64 + 64));
+      } else {
+        const int a = (int)(kb & 0xffffffffu);
+        scan(a, a + 1);
       }
     }
+    if (ba == 0x7fffffff) scan(0, A);
     a_out = ba;
   }
   if (lane == 0) idx[t] = a_out;
@@ -188,17 +202,17 @@ struct DistProblem {
   const uint16_t* mu;
   const uint16_t* x;
   const float* mu2;
-  uint64_t* best;   // [slot][N]: (order-preserving distance bits << 32 | a) of the slot's nearest
-  float* second;    // [slot][N]: the slot's runner-up distance
+  uint64_t* best;    // [slot][N]: (order-preserving distance bits << 32 | a) of the slot's nearest
+  uint64_t* second;  // [slot][N]: the same for the slot's runner-up
   __device__ u32x4 load_a(int, int m, int k) const { return load8_bf16(mu, m, K, k, m < M && k < K); }
   __device__ u32x4 load_b(int, int n, int k) const { return load8_bf16(x, n, K, k, n < N && k < K); }
-  // one wave = centers m0 .. m0 + 63 (slot m0 / 64) x tokens n0 .. n0 + 63
+  // one wave = centers m0 .. m0 + 63 (slot m0 / 64) x tokens n0 .. n0 + 63;
+  // candidates are ordered by (distance, index)
   __device__ void epilogue(int, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
     if (m0 >= M) return;  // no center in this quadrant
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      float b1 = INFINITY, s1 = INFINITY;
-      int a1 = 0x7fffffff;
+      uint64_t k1 = ~0ull, k2 = ~0ull;  // the lane's nearest and runner-up
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -206,28 +220,26 @@ struct DistProblem {
           const int a = m0 + 32 * i + acc_row(e, lane);
           if (a < M) {
             const float dist = mu2[a] - 2.f * acc[i][j][e];
-            if (dist < b1 || (dist == b1 && a < a1)) {
-              s1 = b1;
-              b1 = dist;
-              a1 = a;
-            } else {
-              s1 = fminf(s1, dist);
+            const uint64_t k = ((uint64_t)ordered_bits(dist) << 32) | (uint32_t)a;
+            if (k < k1) {
+              k2 = k1;
+              k1 = k;
+            } else if (k < k2) {
+              k2 = k;
             }
           }
         }
       }
-      const float b2 = __shfl_xor(b1, 32, 64), s2 = __shfl_xor(s1, 32, 64);
-      const int a2 = __shfl_xor(a1, 32, 64);
-      // runner-up of the union of both lanes' candidates
-      const float sec = fminf(fminf(s1, s2), fmaxf(b1, b2));
-      if (b2 < b1 || (b2 == b1 && a2 < a1)) {
-        b1 = b2;
-        a1 = a2;
-      }
+      const uint64_t o1 = __shfl_xor(k1, 32, 64), o2 = __shfl_xor(k2, 32, 64);
+      // nearest and runner-up of the union of both lanes' candidates
+      const uint64_t b = k1 < o1 ? k1 : o1;
+      const uint64_t r1 = k1 < o1 ? o1 : k1;           // the other lane's nearest
+      const uint64_t r2 = k1 < o1 ? k2 : o2;           // the winner's own runner-up
+      const uint64_t sec = r1 < r2 ? r1 : r2;
       const int n = n0 + 32 * j + (lane & 31);
       if (lane < 32 && n < N) {
         const int64_t o = (int64_t)(m0 / 64) * N + n;
-        best[o] = ((uint64_t)ordered_bits(b1) << 32) | (uint32_t)a1;
+        best[o] = b;
         second[o] = sec;
       }
     }
@@ -489,7 +501,7 @@ AssignLayout assign_layout(int64_t N, int32_t A) {
   L.mu2 = take(sizeof(float) * A);
   L.bmax = take(sizeof(float) * L.nbmax);
   L.best = take(sizeof(uint64_t) * nslot * N);
-  L.second = take(sizeof(float) * nslot * N);
+  L.second = take(sizeof(uint64_t) * nslot * N);
   L.total = off;
   return L;
 }
@@ -504,7 +516,7 @@ nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void
   float* mu2 = reinterpret_cast<float*>(ws + L.mu2);
   float* bmax = reinterpret_cast<float*>(ws + L.bmax);
   uint64_t* best = reinterpret_cast<uint64_t*>(ws + L.best);
-  float* second = reinterpret_cast<float*>(ws + L.second);
+  uint64_t* second = reinterpret_cast<uint64_t*>(ws + L.second);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* mub = static_cast<const uint16_t*>(centers);
   hipLaunchKernelGGL(k_center_norms, dim3((unsigned)L.nbmax), dim3(256), 0, st, mub, A, W, mu2,
