@@ -75,8 +75,8 @@ nkv_status tuned_attend(const nkv_shape* s, const BranchArgs& kb, const BranchAr
     nkv_status e;
     {
       ProfScope ps("decode", fs);
-      if ((e = launch_decode_tuned(kb, W, s->r, s->group, full, kall, 0, false, fs))) return e;
-      if ((e = launch_decode_tuned(vb, W, s->r, s->group, full, vt, L.nk_pad, true, fs))) return e;
+      if ((e = launch_decode_pair_tuned(kb, vb, W, s->r, s->group, full, kall, vt, L.nk_pad, fs)))
+        return e;
     }
     {
       ProfScope ps("stage_current", fs);

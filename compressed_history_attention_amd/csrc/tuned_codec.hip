@@ -19,6 +19,9 @@
 // Decoder (Figure 4(b)): x_hat = mu_a + D (code * scale) as a GEMM whose A
 // loader dequantises INT4 on the fly and whose epilogue adds the center and
 // writes bf16 rows (K) or per-head transposed columns (V).
+#include <atomic>
+#include <type_traits>
+
 #include "prof.hpp"
 #include "quant.hpp"
 #include "tuned_internal.hpp"
@@ -898,6 +901,264 @@ __global__ __launch_bounds__(256) void k_decode_stationary(BranchArgs b, RangeTa
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decoder stationary, both branches in one launch.  The unit of work is
+// (branch, 128-channel block, 32-token group); each block (8 waves, one
+// block per CU) takes an equal share of the units in that order.  For each
+// run of its units with one (branch, channel block) it loads those 128
+// decoder rows once into LDS (rows padded by 16 bytes, so the 16 rows one
+// operand read touches fall on distinct banks); then every wave takes every
+// eighth unit of the run: the 32 tokens' INT4 codes go straight into
+// registers (16 bytes per lane per 64 coefficients, one unit ahead) and are
+// dequantised there into the MFMA's B operand, against the decoder rows as A
+// operand, so one dequantised fragment feeds four MFMAs (128 channels) and
+// no decoder row is streamed per token.  The result plus the token's center
+// is rounded to bf16 and leaves through a per-wave LDS tile as 16-byte
+// stores: K rows [token][channel], V transposed [channel][token], whole
+// groups of 32 (rows or columns up to the next multiple of 32 are written).
+// Logical k order of MFMA step (j, s): lane half hl holds coefficients
+// 64 j + 32 hl + 8 s .. + 7 in both operands, so a lane's codes for a group
+// of 64 coefficients are 16 consecutive bytes (r % 64 == 0) under one scale
+// (INT4 groups of 32 or more coefficients).
+// ---------------------------------------------------------------------------
+constexpr int DP_SK = 72, DP_SV = 40;  // staging strides (bf16): K [32][72], V [64][40]
+constexpr int DP_STAGE = 64 * DP_SV;   // bf16 per wave (>= 32 * 72)
+
+struct DecodePair {
+  BranchArgs br[2];  // K, V
+  uint16_t* kout;    // [total][W]
+  uint16_t* vt;      // [W][ld]
+  int64_t ld;
+  RangeTable rows;
+  int W, gshift, G;  // group = 1 << gshift; G = token groups of 32
+  int64_t U;         // units = 2 (W / 128) G
+};
+
+template <int NJ>
+__global__ __launch_bounds__(512, 1) void k_decode_pair(const DecodePair p) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  constexpr int R = NJ * 64, RS = R + 8;
+  uint16_t* sD = reinterpret_cast<uint16_t*>(dsm);
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* sO = sD + 128 * RS + wave * DP_STAGE;
+  const int W = p.W, ncb = W / 128;
+  const int64_t total = p.rows.total;
+  const int64_t u_beg = p.U * blockIdx.x / gridDim.x, u_end = p.U * (blockIdx.x + 1) / gridDim.x;
+  // the row ranges in LDS: the token lookup then waits on LDS only, never
+  // behind the stores of the unit before (global loads and stores share one
+  // in-order counter)
+  __shared__ int64_t sBeg[NKV_MAX_SEGMENTS], sPre[NKV_MAX_SEGMENTS + 1];
+  const int nrange = p.rows.n;
+  if (tid < nrange) sBeg[tid] = p.rows.begin[tid];
+  if (tid <= nrange) sPre[tid] = p.rows.prefix[tid];
+  auto token = [&](int64_t j) __attribute__((always_inline)) {
+    int k = 0;
+    while (k + 1 < nrange && sPre[k + 1] <= j) ++k;
+    return sBeg[k] + (j - sPre[k]);
+  };
+
+  struct Pre {
+    u32x4 c[NJ];
+    uint16_t s[NJ];
+    int32_t a;
+  };
+  for (int64_t s0 = u_beg; s0 < u_end;) {
+    const int64_t seg = s0 / p.G;  // branch * ncb + channel block (block-uniform)
+    const int64_t s1 = min(u_end, (seg + 1) * p.G);
+    const int br = (int)(seg / ncb), cb = (int)(seg - (int64_t)br * ncb);
+    const BranchArgs& b = p.br[br];
+    // ---- the run's decoder rows cb*128 .. +127 into LDS ----------------------
+    __syncthreads();  // every wave is done with the previous run's rows
+    {
+      const uint16_t* D = static_cast<const uint16_t*>(b.decoder) + (int64_t)cb * 128 * R;
+      constexpr int NB = 128 * R / 8, PER = NB / 512;
+      static_assert(NB % 512 == 0, "whole rounds of 16-byte pieces");
+      // (the thread's slots from an opaque copy of its index: hoisted out of
+      // the loops, their offsets would hold registers for the whole kernel)
+      int ti = tid;
+      asm volatile("" : "+v"(ti));
+      // four 16-byte pieces per thread in flight at a time (once per run)
+#pragma unroll
+      for (int i0 = 0; i0 < PER; i0 += 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = ti + 512 * (i0 + i);
+          if (i0 + i < PER) v[i] = ld_u32x4(D + 8 * c);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = ti + 512 * (i0 + i);
+          if (i0 + i < PER) {
+            const int row = c / (R / 8), blk = c - row * (R / 8);
+            *reinterpret_cast<u32x4*>(sD + row * RS + 8 * blk) = v[i];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    // ---- this wave's units of the run -----------------------------------------
+    const uint16_t* mu = static_cast<const uint16_t*>(b.centers);
+    auto fetch = [&](int64_t u, Pre& f) __attribute__((always_inline)) {
+      const int64_t g = u - seg * p.G;
+      const int64_t m = min(g * 32 + n, total - 1);  // rows past the end repeat the last token
+      const int64_t t = token(m);
+      f.a = b.idx[t];
+      const uint8_t* crow = b.codes + t * (R / 2) + 16 * hl;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) f.c[j] = ld_u32x4(crow + 32 * j);
+      // the lane's scales: one per 32 coefficients (group >= 32); a token's
+      // row holds R / group of them
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        f.s[j] = b.scales[t * (R >> p.gshift) + ((64 * j + 32 * hl) >> p.gshift)];
+    };
+    // the unit loop, compiled once per branch (the epilogue's layout differs)
+    auto units = [&](auto brc) __attribute__((always_inline)) {
+    constexpr int BR = decltype(brc)::value;
+    // (every fetch is issued, a past-the-end unit clamped to the run's last:
+    // the same memory operations on every path keep the waits exact)
+    Pre nxt;
+    auto one = [&](int64_t u) __attribute__((always_inline)) {
+      const Pre cur = nxt;
+      // The next unit's codes are requested halfway through this unit's
+      // MFMAs (when half of this unit's codes are dead) and the centers of
+      // this unit (the lane's 16 runs of 4 channels) two code groups before
+      // the end: both land under MFMAs, without holding registers all along.
+      uint2 mv[4][4];
+      const uint16_t* mrow = mu + (int64_t)cur.a * W + cb * 128 + 4 * hl;
+      auto load_mu = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            mv[blk][gq] = *reinterpret_cast<const uint2*>(mrow + blk * 32 + gq * 8);
+      };
+      f32x16 acc[4];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) acc[blk] = zero16();
+      // the lane's decoder rows: two bases (rows n and 64 + n), each with
+      // constant offsets inside the 16-bit LDS offset field; from an opaque
+      // lane index, so they are formed here rather than held all along
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const uint16_t* arow0 = sD + (ln & 31) * RS + 32 * (ln >> 5);
+      const uint16_t* arow1 = arow0 + 64 * RS;
+      // decoder fragments of step k (k = 4 j + s): read one step ahead of
+      // their MFMAs; the fences keep the scheduler from hoisting every read
+      // of the unrolled loop (and its registers) to the top
+      auto read_a = [&](int k, bf16x8 (&af)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+          af[blk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              (blk < 2 ? arow0 : arow1) + (blk & 1) * 32 * RS + 64 * (k >> 2) + 8 * (k & 3)));
+      };
+      bf16x8 a0[4], a1[4];
+      read_a(0, a0);
+#pragma unroll
+      for (int k = 0; k < 4 * NJ; ++k) {
+        bf16x8 (&ac)[4] = (k & 1) ? a1 : a0;
+        bf16x8 (&an)[4] = (k & 1) ? a0 : a1;
+        if (k + 1 < 4 * NJ) read_a(k + 1, an);
+        if (k == 4 * (NJ / 2)) fetch(min(u + 8, s1 - 1), nxt);
+        if (k == 4 * (NJ - 2)) load_mu();
+        const int j = k >> 2, s = k & 3;
+        const float sc = fp16_bits_to_f32(cur.s[j]);
+        const float nb = -8.f * sc;
+        // INT4 two's complement -> offset binary, nibbles spread to bytes:
+        // (n' - 8) sc is exact in fp32 (fma), then one rounding to bf16
+        const uint32_t w = cur.c[j][s] ^ 0x88888888u;
+        const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+        u32x4 bv;
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          bv[h] = pack_bf16x2(fmaf((float)((lo >> (8 * h)) & 0xffu), sc, nb),
+                              fmaf((float)((hi >> (8 * h)) & 0xffu), sc, nb));
+        const bf16x8 bf = as_bf16x8(bv);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) acc[blk] = mfma_bf16(ac[blk], bf, acc[blk]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // ---- epilogue: + center, bf16, through LDS as 16-byte stores -------------
+      const int64_t g = u - seg * p.G, m0 = g * 32;
+      // accumulators + centers -> bf16 pairs first (frees the accumulators)
+      uint2 pk[4][4];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const uint2 mq = mv[blk][gq];
+          pk[blk][gq] = uint2{
+              pack_bf16x2(acc[blk][4 * gq + 0] + bf16_bits_to_f32(uint16_t(mq.x & 0xffffu)),
+                          acc[blk][4 * gq + 1] + bf16_bits_to_f32(uint16_t(mq.x >> 16))),
+              pack_bf16x2(acc[blk][4 * gq + 2] + bf16_bits_to_f32(uint16_t(mq.y & 0xffffu)),
+                          acc[blk][4 * gq + 3] + bf16_bits_to_f32(uint16_t(mq.y >> 16)))};
+        }
+      // one base per lane, every element at a constant offset from it
+      int le = lane;
+      asm volatile("" : "+v"(le));
+      uint16_t* sw = BR == 0 ? sO + (le & 31) * DP_SK + 4 * (le >> 5)
+                             : sO + 4 * (le >> 5) * DP_SV + (le & 31);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int bl = 0; bl < 2; ++bl)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int cc = bl * 32 + gq * 8;  // + 4 hl, in the base
+            const uint2 v = pk[2 * hb + bl][gq];
+            if constexpr (BR == 0) {
+              *reinterpret_cast<uint2*>(sw + cc) = v;
+            } else {
+              sw[(cc + 0) * DP_SV] = uint16_t(v.x & 0xffffu);
+              sw[(cc + 1) * DP_SV] = uint16_t(v.x >> 16);
+              sw[(cc + 2) * DP_SV] = uint16_t(v.y & 0xffffu);
+              sw[(cc + 3) * DP_SV] = uint16_t(v.y >> 16);
+            }
+          }
+        // the wave's own tile: LDS operations of a wave complete in order, so
+        // only the compiler must keep the stores above the reads
+        asm volatile("" ::: "memory");
+        // whole groups of 32 rows (the caller's buffers hold them; the rows
+        // past the end repeat the last token and are overwritten later)
+        if constexpr (BR == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = le + 64 * i, tk = c >> 3, c8 = c & 7;
+            *reinterpret_cast<u32x4*>(p.kout + (m0 + tk) * W + cb * 128 + hb * 64 + 8 * c8) =
+                *reinterpret_cast<const u32x4*>(sO + tk * DP_SK + 8 * c8);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = le + 64 * i, ch = c >> 2, t8 = 8 * (c & 3);
+            *reinterpret_cast<u32x4*>(p.vt + (int64_t)(cb * 128 + hb * 64 + ch) * p.ld + m0 + t8) =
+                *reinterpret_cast<const u32x4*>(sO + ch * DP_SV + t8);
+          }
+        }
+        asm volatile("" ::: "memory");
+      }
+    };
+    // The first unit is a copy of its own: the loop is then entered only
+    // after a unit's memory operations, as on every later trip, and the
+    // compiler's waits at its head count the previous unit's stores as
+    // still in flight instead of waiting for them.
+    const int64_t u0 = s0 + wave;
+    fetch(min(u0, s1 - 1), nxt);
+    if (u0 < s1) {
+      one(u0);
+      for (int64_t u = u0 + 8; u < s1; u += 8) one(u);
+    }
+    };
+    if (br == 0) units(std::integral_constant<int, 0>{});
+    else units(std::integral_constant<int, 1>{});
+    s0 = s1;
+  }
+}
+
 size_t decode_stationary_lds(int r) {
   const size_t o = std::max<size_t>((size_t)DS_TOK * (DS_CH + 8), (size_t)DS_CH * (DS_TOK + 8));
   return (size_t)DS_TOK * (r + 8) * 2 + o * 2;
@@ -947,6 +1208,71 @@ nkv_status launch_decode_tuned(const BranchArgs& b, int W, int r, int group,
   }
   DecodeProblem p{(int)rows.total, W, r, group, b, rows, out, ld, false};
   return launch_gemm(p, 1, st);
+}
+
+namespace {
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+}  // namespace
+
+nkv_status launch_decode_pair_tuned(const BranchArgs& kb, const BranchArgs& vb, int W, int r,
+                                    int group, const RangeTable& rows, uint16_t* kout,
+                                    uint16_t* vt, int64_t ld, hipStream_t st) {
+  if (rows.total == 0) return NKV_OK;
+  auto al = [](const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) == 0; };
+  const bool pow2 = group >= 32 && (group & (group - 1)) == 0 && r % group == 0;
+  const bool fits = r % 64 == 0 && r >= 128 && r <= 448 && W % 128 == 0 && ld % 8 == 0 && pow2 &&
+                    al(kb.codes, 16) && al(vb.codes, 16) && al(kb.decoder, 16) &&
+                    al(vb.decoder, 16) && al(kb.centers, 8) && al(vb.centers, 8) &&
+                    al(kout, 16) && al(vt, 16);
+  if (!fits) {
+    nkv_status e = launch_decode_tuned(kb, W, r, group, rows, kout, 0, false, st);
+    if (e) return e;
+    return launch_decode_tuned(vb, W, r, group, rows, vt, ld, true, st);
+  }
+  DecodePair p{};
+  p.br[0] = kb;
+  p.br[1] = vb;
+  p.kout = kout;
+  p.vt = vt;
+  p.ld = ld;
+  p.rows = rows;
+  p.W = W;
+  p.gshift = __builtin_ctz((unsigned)group);
+  p.G = (int)ceil_div(rows.total, 32);
+  p.U = 2 * (int64_t)(W / 128) * p.G;
+  const int nblk = (int)std::min<int64_t>(device_cus(), ceil_div(p.U, 8));
+  const size_t lds = ((size_t)128 * (r + 8) + 8 * DP_STAGE) * 2;
+  auto go = [&](auto kern) -> nkv_status {
+    NKV_HIP_CHECK(hipFuncSetAttribute((const void*)kern,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(512), lds, st, p);
+    NKV_LAUNCH_CHECK();
+    return NKV_OK;
+  };
+  switch (r / 64) {
+#define NKV_DP(nj) \
+  case nj: return go(k_decode_pair<nj>);
+    NKV_DP(2)
+    NKV_DP(3)
+    NKV_DP(4)
+    NKV_DP(5)
+    NKV_DP(6)
+    NKV_DP(7)
+#undef NKV_DP
+    default: break;
+  }
+  return NKV_EUNSUPPORTED;  // not reached: r / 64 in 2..7 above
 }
 
 // ---------------------------------------------------------------------------
