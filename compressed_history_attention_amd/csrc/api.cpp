@@ -444,7 +444,9 @@ size_t nkv_fit_workspace_size(const nkv_shape* shape, int64_t N, int32_t A) {
   g_err[0] = 0;
   if (check_shape(shape) || N < 0 || A < 1) return SIZE_MAX;
   const int64_t W = (int64_t)shape->H * shape->d;
-  size_t off = tuned_applies(shape, 0) ? tuned_assign_workspace(N, A) : 0;
+  const bool tuned = tuned_applies(shape, 0);
+  size_t off = tuned ? tuned_assign_workspace(N, A) : 0;
+  if (tuned) off = align_up(off + sizeof(float) * (size_t)N, 256);  // ||x||^2 per row
   off = align_up(off + sizeof(int32_t) * (size_t)N, 256);        // assignment
   off = align_up(off + sizeof(int32_t) * (size_t)N, 256);        // rows sorted by center
   off = align_up(off + sizeof(int32_t) * (3 * (size_t)A + 1), 256);  // counts, offsets, cursor
@@ -472,8 +474,11 @@ nkv_status nkv_fit_centers(const nkv_shape* shape, const void* x, int64_t N, voi
   const bool tuned = tuned_applies(shape, 0);
   char* base = static_cast<char*>(ws);
   const size_t a_bytes = tuned ? tuned_assign_workspace(N, A) : 0;
-  int32_t* lab = reinterpret_cast<int32_t*>(base + a_bytes);
-  size_t off = align_up(a_bytes + sizeof(int32_t) * (size_t)N, 256);
+  // ||x||^2 of the rows, summed once for every assignment below (tuned)
+  float* xn = reinterpret_cast<float*>(base + a_bytes);
+  const size_t l_off = tuned ? align_up(a_bytes + sizeof(float) * (size_t)N, 256) : a_bytes;
+  int32_t* lab = reinterpret_cast<int32_t*>(base + l_off);
+  size_t off = align_up(l_off + sizeof(int32_t) * (size_t)N, 256);
   int32_t* perm = reinterpret_cast<int32_t*>(base + off);
   off = align_up(off + sizeof(int32_t) * (size_t)N, 256);
   int32_t* cnt = reinterpret_cast<int32_t*>(base + off);
@@ -481,9 +486,13 @@ nkv_status nkv_fit_centers(const nkv_shape* shape, const void* x, int64_t N, voi
   int32_t* cursor = offs + A + 1;
   auto assign = [&](int32_t* out) -> nkv_status {
     if (N == 0) return NKV_OK;
-    if (tuned) return tuned_assign(shape, x, N, centers, A, out, base, s);
+    if (tuned) return tuned_assign(shape, x, N, centers, A, out, base, s, xn);
     return launch_assign_generic(shape->dtype, x, N, W, centers, A, out, s);
   };
+  if (tuned && N > 0 && (iters > 0 || idx || counts)) {
+    ProfScope ps("fit_assign", s);
+    if ((st = tuned_row_sqnorm(shape, x, N, xn, s))) return st;
+  }
   for (int it = 0; it < iters; ++it) {
     {
       ProfScope ps("fit_assign", s);

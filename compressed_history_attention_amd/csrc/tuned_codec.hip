@@ -77,19 +77,9 @@ __global__ __launch_bounds__(256) void k_center_norms(const uint16_t* __restrict
 // the token again in fp64: d(a) = ||mu_a||^2 - 2 mu_a . x with exact bf16
 // products summed in fp64, lowest index on ties.  (M and ||x|| are inflated
 // by 1 % for their own rounding; ||x||^2 is summed here from 16-byte loads.)
-__global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restrict__ best,
-                                                       const uint64_t* __restrict__ second,
-                                                       int nslot, int64_t N, int W,
-                                                       const uint16_t* __restrict__ x,
-                                                       const uint16_t* __restrict__ mu, int A,
-                                                       const float* __restrict__ block_max,
-                                                       int nblock_max,
-                                                       int32_t* __restrict__ idx) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= N) return;  // whole waves; no block barrier below
-  // ||x_t||^2 (W % 8 == 0 on this path)
-  const uint16_t* row = x + t * W;
+// ||row||^2 of one bf16 row (W % 8 == 0), summed in fp32 by one wave from
+// 16-byte loads; every lane returns the total
+__device__ __forceinline__ float row_sqnorm_wave(const uint16_t* row, int W, int lane) {
   float xs = 0.f;
   for (int w = 8 * lane; w < W; w += 512) {
     const u32x4 v = ld_u32x4(row + w);
@@ -100,7 +90,35 @@ __global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restric
       xs = fmaf(lo, lo, fmaf(hi, hi, xs));
     }
   }
-  xs = wave_sum(xs);
+  return wave_sum(xs);
+}
+
+// ||x_t||^2 per token, one wave each (rows that several assignments reuse,
+// as in center fitting, are summed once)
+__global__ __launch_bounds__(256) void k_row_sqnorm(const uint16_t* __restrict__ x, int64_t N,
+                                                    int W, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;
+  const float xs = row_sqnorm_wave(x + t * W, W, lane);
+  if (lane == 0) out[t] = xs;
+}
+
+__global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restrict__ best,
+                                                       const uint64_t* __restrict__ second,
+                                                       int nslot, int64_t N, int W,
+                                                       const uint16_t* __restrict__ x,
+                                                       const float* __restrict__ xnorm,
+                                                       const uint16_t* __restrict__ mu, int A,
+                                                       const float* __restrict__ block_max,
+                                                       int nblock_max,
+                                                       int32_t* __restrict__ idx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;  // whole waves; no block barrier below
+  // ||x_t||^2: given, or summed here (W % 8 == 0 on this path)
+  const uint16_t* row = x + t * W;
+  const float xs = xnorm ? xnorm[t] : row_sqnorm_wave(row, W, lane);
   float m2 = 0.f;  // max ||mu||^2 from the per-block maxima
   for (int i = lane; i < nblock_max; i += 64) m2 = fmaxf(m2, block_max[i]);
   m2 = wave_max(m2);
@@ -512,8 +530,17 @@ AssignLayout assign_layout(int64_t N, int32_t A) {
 
 size_t tuned_assign_workspace(int64_t N, int32_t A) { return assign_layout(N, A).total; }
 
+nkv_status tuned_row_sqnorm(const nkv_shape* s, const void* x, int64_t N, float* out,
+                            hipStream_t st) {
+  if (N <= 0) return NKV_OK;
+  hipLaunchKernelGGL(k_row_sqnorm, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), N, s->H * s->d, out);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
 nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void* centers,
-                        int32_t A, int32_t* idx, char* ws, hipStream_t st) {
+                        int32_t A, int32_t* idx, char* ws, hipStream_t st, const float* xnorm) {
   const int W = s->H * s->d;
   const AssignLayout L = assign_layout(N, A);
   float* mu2 = reinterpret_cast<float*>(ws + L.mu2);
@@ -531,7 +558,7 @@ nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void
   // than the direct-to-LDS one, whose 32-wide steps double the barriers)
   if ((e = launch_gemm(dp, 1, st))) return e;
   hipLaunchKernelGGL(k_argmin_reduce, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st, best,
-                     second, (int)ceil_div(A, 64), N, W, xb, mub, A, bmax, L.nbmax, idx);
+                     second, (int)ceil_div(A, 64), N, W, xb, xnorm, mub, A, bmax, L.nbmax, idx);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }
