@@ -267,6 +267,94 @@ struct DistProblem {
   }
 };
 
+// The same product split over K (grid z) when the tiles are too few to fill
+// the chip (few tokens or few centers): split z sums its K chunk
+// [z K, (z + 1) K) into fp32 partial dot products part[z][token][center],
+// which k_dist_reduce adds up before the slot records are formed.  Any
+// summation order keeps the rounding bound of the assignment (W + splits
+// - 1 additions, splits <= 64).
+struct DistSplitProblem {
+  static constexpr int BK = 64;
+  int M, N, K;  // M = A centers, N = tokens, K = the chunk of one split (multiple of 64)
+  int Kfull;    // W
+  const uint16_t* mu;
+  const uint16_t* x;
+  float* part;  // [splits][N][M]
+  __device__ u32x4 load_a(int z, int m, int k) const {
+    const int kk = z * K + k;
+    return load8_bf16(mu, m, Kfull, kk, m < M && kk < Kfull);
+  }
+  __device__ u32x4 load_b(int z, int n, int k) const {
+    const int kk = z * K + k;
+    return load8_bf16(x, n, Kfull, kk, n < N && kk < Kfull);
+  }
+  // lane: token n0 + 32 j + lane % 32, centers m0 + 32 i + acc_row(e): runs of
+  // four consecutive centers (e % 4), stored as one 16-byte piece when whole
+  __device__ void epilogue(int z, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
+    if (m0 >= M) return;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 32 * j + (lane & 31);
+      if (n >= N) continue;
+      float* row = part + ((int64_t)z * N + n) * M;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int a = m0 + 32 * i + acc_row(4 * g, lane);
+          if ((M & 3) == 0 && a + 4 <= M) {
+            *reinterpret_cast<f32x4*>(row + a) =
+                f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                      acc[i][j][4 * g + 3]};
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (a + u < M) row[a + u] = acc[i][j][4 * g + u];
+          }
+        }
+    }
+  }
+};
+
+// Split partials -> the slot records of DistProblem's epilogue: one wave per
+// token, lane l holding center 64 slot + l (nearest and runner-up of each
+// 64-center slot by (distance, index), as there)
+__global__ __launch_bounds__(256) void k_dist_reduce(const float* __restrict__ part, int splits,
+                                                     int64_t N, int A,
+                                                     const float* __restrict__ mu2,
+                                                     uint64_t* __restrict__ best,
+                                                     uint64_t* __restrict__ second) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;  // whole waves
+  const int nslot = (A + 63) / 64;
+  for (int sl = 0; sl < nslot; ++sl) {
+    const int a = sl * 64 + lane;
+    uint64_t k = ~0ull;
+    if (a < A) {
+      float dot = 0.f;
+      for (int z = 0; z < splits; ++z) dot += part[((int64_t)z * N + t) * A + a];
+      k = ((uint64_t)ordered_bits(mu2[a] - 2.f * dot) << 32) | (uint32_t)a;
+    }
+    uint64_t b = k;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t v = __shfl_xor(b, o, 64);
+      b = v < b ? v : b;
+    }
+    uint64_t r = k == b ? ~0ull : k;  // keys are distinct (the index is in them)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t v = __shfl_xor(r, o, 64);
+      r = v < r ? v : r;
+    }
+    if (lane == 0) {
+      best[(int64_t)sl * N + t] = b;
+      second[(int64_t)sl * N + t] = r;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // projection GEMM: rows = tokens, cols = coefficients, K = 3 W (split terms)
 // ---------------------------------------------------------------------------
@@ -506,9 +594,20 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
 namespace {
 // workspace of the assignment: ||mu||^2, per-block maxima of it, slot records
 struct AssignLayout {
-  size_t mu2, bmax, best, second, total;
-  int nbmax;
+  size_t mu2, bmax, best, second, part, total;
+  int nbmax, splits;
 };
+// K splits of the distance product: one when its 128 x 128 tiles fill the
+// chip, else enough for about two blocks per CU, at most 32 and with the
+// partials under 8 MiB (the chunk count W / 64 caps it again at launch)
+int dist_splits(int64_t N, int32_t A) {
+  const int64_t tiles = ceil_div(A, 128) * ceil_div(N, 128);
+  if (N <= 0 || tiles >= 256) return 1;
+  int64_t s = std::min<int64_t>(32, ceil_div(512, tiles));
+  s = std::min<int64_t>(s, (int64_t)(8u << 20) / (sizeof(float) * N * A));
+  return (int)std::max<int64_t>(1, s);
+}
+
 AssignLayout assign_layout(int64_t N, int32_t A) {
   AssignLayout L{};
   const int64_t nslot = ceil_div(A, 64);
@@ -523,6 +622,8 @@ AssignLayout assign_layout(int64_t N, int32_t A) {
   L.bmax = take(sizeof(float) * L.nbmax);
   L.best = take(sizeof(uint64_t) * nslot * N);
   L.second = take(sizeof(uint64_t) * nslot * N);
+  L.splits = dist_splits(N, A);
+  L.part = L.splits > 1 ? take(sizeof(float) * L.splits * N * A) : 0;
   L.total = off;
   return L;
 }
@@ -552,11 +653,23 @@ nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void
   hipLaunchKernelGGL(k_center_norms, dim3((unsigned)L.nbmax), dim3(256), 0, st, mub, A, W, mu2,
                      bmax);
   NKV_LAUNCH_CHECK();
-  DistProblem dp{A, (int)N, W, mub, xb, mu2, best, second};
   nkv_status e;
   // (the register-staged GEMM with 64-wide k steps: measured faster here
   // than the direct-to-LDS one, whose 32-wide steps double the barriers)
-  if ((e = launch_gemm(dp, 1, st))) return e;
+  const int kc = (int)std::min<int64_t>(L.splits, W / 64);
+  if (kc <= 1) {
+    DistProblem dp{A, (int)N, W, mub, xb, mu2, best, second};
+    if ((e = launch_gemm(dp, 1, st))) return e;
+  } else {
+    const int chunk = (int)ceil_div(ceil_div(W, kc), 64) * 64;
+    const int splits = (int)ceil_div(W, chunk);
+    float* part = reinterpret_cast<float*>(ws + L.part);
+    DistSplitProblem sp{A, (int)N, chunk, W, mub, xb, part};
+    if ((e = launch_gemm(sp, splits, st))) return e;
+    hipLaunchKernelGGL(k_dist_reduce, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st, part,
+                       splits, N, A, mu2, best, second);
+    NKV_LAUNCH_CHECK();
+  }
   hipLaunchKernelGGL(k_argmin_reduce, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st, best,
                      second, (int)ceil_div(A, 64), N, W, xb, xnorm, mub, A, bmax, L.nbmax, idx);
   NKV_LAUNCH_CHECK();
