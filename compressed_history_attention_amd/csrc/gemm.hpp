@@ -88,6 +88,102 @@ __global__ __launch_bounds__(256) void k_gemm(const P p) {
   p.epilogue(z, m_blk + wm, n_blk + wn, lane, acc);
 }
 
+// The same tile and LDS double buffer with the global loads two K steps
+// ahead instead of one (two register sets): step kt computes from LDS while
+// the loads of step kt + 2 are in flight and step kt + 1 waits in registers
+// for the buffer step kt - 1 freed.  For long K with global latency that one
+// step's MFMAs do not cover (P::BK == 64).
+template <class P>
+__global__ __launch_bounds__(256) void k_gemm_pf2(const P p) {
+  constexpr int BK = P::BK;
+  static_assert(BK == 64, "K step");
+  constexpr int LS = BK + 8;              // bf16 elements per LDS row
+  constexpr int LD = GEMM_BM * BK / 8 / 256;  // 8-value chunks per thread per operand
+  constexpr int TPR = BK / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][GEMM_BM * LS];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][GEMM_BN * LS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int z = blockIdx.z;
+  const int m_blk = blockIdx.y * GEMM_BM, n_blk = blockIdx.x * GEMM_BN;
+  const int ld_row0 = tid / TPR, ld_k = (tid % TPR) * 8;
+  u32x4 ra[2][LD], rb[2][LD];
+  auto fetch = [&](int set, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < LD; ++j) {
+      ra[set][j] = p.load_a(z, m_blk + ld_row0 + (256 / TPR) * j, k0 + ld_k);
+      rb[set][j] = p.load_b(z, n_blk + ld_row0 + (256 / TPR) * j, k0 + ld_k);
+    }
+  };
+  auto stash = [&](int set, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < LD; ++j) {
+      *reinterpret_cast<u32x4*>(&sA[buf][(ld_row0 + (256 / TPR) * j) * LS + ld_k]) = ra[set][j];
+      *reinterpret_cast<u32x4*>(&sB[buf][(ld_row0 + (256 / TPR) * j) * LS + ld_k]) = rb[set][j];
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int nk = (p.K + BK - 1) / BK;
+  fetch(0, 0);
+  fetch(1, min(1, nk - 1) * BK);
+  stash(0, 0);
+  __syncthreads();
+  auto mm = [&](int cur) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 16) {
+      bf16x8 fa[2], fb[2];
+      const int kk = ks + 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sA[cur][(wm + 32 * i + (lane & 31)) * LS + kk]));
+        fb[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sB[cur][(wn + 32 * i + (lane & 31)) * LS + kk]));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+    }
+  };
+  // a step with a successor: step kt + 2's loads go into the register set
+  // step kt emptied into LDS buffer cur (the final steps reload the last
+  // tile), the MFMAs read buffer cur, then step kt + 1 moves from the other
+  // register set into the other buffer
+  auto step = [&](int kt, int cur) __attribute__((always_inline)) {
+    fetch(cur, min(kt + 2, nk - 1) * BK);
+    mm(cur);
+    stash(cur ^ 1, cur ^ 1);
+    __syncthreads();
+  };
+  // two steps per trip (static register sets and buffers) in straight-line
+  // code: the same memory operations on every trip let the compiler's waits
+  // leave the newest loads in flight
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    step(kt, 0);
+    step(kt + 1, 1);
+  }
+  if (nk - kt == 2) {
+    step(kt, 0);
+    mm(1);
+  } else {
+    mm(0);
+  }
+  p.epilogue(z, m_blk + wm, n_blk + wn, lane, acc);
+}
+
+template <class P>
+inline nkv_status launch_gemm_pf2(const P& p, int batch, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0 || batch <= 0) return NKV_OK;
+  dim3 grid((unsigned)ceil_div(p.N, GEMM_BN), (unsigned)ceil_div(p.M, GEMM_BM), (unsigned)batch);
+  hipLaunchKernelGGL(k_gemm_pf2<P>, grid, dim3(256), 0, s, p);
+  NKV_LAUNCH_CHECK();
+  return NKV_OK;
+}
+
 // The same tile (128 x 128, 4 waves of 64 x 64) for problems whose operands
 // are plain bf16 rows: K % 32 == 0 and P supplies
 //   __device__ const uint16_t* a_ptr(int z, int m, int k) const;  // &A[z](m, k), 8-aligned k

@@ -35,8 +35,13 @@ namespace nkv {
 // rounds), 16-byte loads; each block also writes the largest of its norms,
 // so the assignment's error bound needs no atomics and no cleared counter.
 constexpr int NORM_CPB = 16;
+// Also ||mu_a||^2 in fp64 (out64), summed in the order the exact
+// re-assignment of k_argmin_reduce uses (lane partials over its channels
+// 8 lane + 512 k .. + 7, then the butterfly), so that pass reads it instead
+// of summing it again per token.
 __global__ __launch_bounds__(256) void k_center_norms(const uint16_t* __restrict__ mu, int A, int W,
                                                       float* __restrict__ out,
+                                                      double* __restrict__ out64,
                                                       float* __restrict__ block_max) {
   __shared__ float smax[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -46,6 +51,7 @@ __global__ __launch_bounds__(256) void k_center_norms(const uint16_t* __restrict
     if (a >= A) break;  // wave-uniform
     const uint16_t* row = mu + (int64_t)a * W;
     float acc = 0.f;
+    double acc64 = 0.0;
     for (int w = 8 * lane; w < W; w += 512) {  // W % 8 == 0 on this path
       const u32x4 v = ld_u32x4(row + w);
 #pragma unroll
@@ -53,10 +59,17 @@ __global__ __launch_bounds__(256) void k_center_norms(const uint16_t* __restrict
         const float lo = bf16_bits_to_f32(uint16_t(v[u] & 0xffffu));
         const float hi = bf16_bits_to_f32(uint16_t(v[u] >> 16));
         acc = fmaf(lo, lo, fmaf(hi, hi, acc));
+        acc64 = fma((double)lo, (double)lo, acc64);
+        acc64 = fma((double)hi, (double)hi, acc64);
       }
     }
     acc = wave_sum(acc);
-    if (lane == 0) out[a] = acc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc64 += __shfl_xor(acc64, o, 64);
+    if (lane == 0) {
+      out[a] = acc;
+      out64[a] = acc64;
+    }
     mx = fmaxf(mx, acc);
   }
   if (lane == 0) smax[wave] = mx;
@@ -110,6 +123,7 @@ __global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restric
                                                        const uint16_t* __restrict__ x,
                                                        const float* __restrict__ xnorm,
                                                        const uint16_t* __restrict__ mu, int A,
+                                                       const double* __restrict__ mu2d,
                                                        const float* __restrict__ block_max,
                                                        int nblock_max,
                                                        int32_t* __restrict__ idx) {
@@ -168,23 +182,19 @@ __global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restric
     auto scan = [&](int a0, int a1) {
       for (int a = a0; a < a1; ++a) {
         const uint16_t* mrow = mu + (int64_t)a * W;
-        double mm = 0.0, dot = 0.0;
+        double dot = 0.0;
         for (int w = 8 * lane; w < W; w += 512) {
           const u32x4 xv = ld_u32x4(row + w), mv = ld_u32x4(mrow + w);
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const double xe = bf16_bits_to_f32(uint16_t(xv[k >> 1] >> (16 * (k & 1))));
             const double me = bf16_bits_to_f32(uint16_t(mv[k >> 1] >> (16 * (k & 1))));
-            mm = fma(me, me, mm);
             dot = fma(xe, me, dot);
           }
         }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          mm += __shfl_xor(mm, o, 64);
-          dot += __shfl_xor(dot, o, 64);
-        }
-        const double dist = mm - 2.0 * dot;
+        for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+        const double dist = mu2d[a] - 2.0 * dot;  // ||mu_a||^2 in fp64, same order
         if (dist < bd) {  // a increases: strict < keeps the lowest index
           bd = dist;
           ba = a;
@@ -214,6 +224,16 @@ __device__ __forceinline__ u32x4 load8_bf16(const uint16_t* base, int64_t row, i
   return ld_u32x4(base + row * ld + k);
 }
 
+// The same as a load on every path: rows and k clamped into [0, rows) and
+// [0, ld - 8], the value zeroed after the load when out of range (a branch
+// around the load would make the compiler wait for all loads in flight)
+__device__ __forceinline__ u32x4 load8_bf16_always(const uint16_t* base, int64_t row, int rows,
+                                                   int ld, int k) {
+  const bool ok = row < rows && k < ld;
+  const u32x4 v = ld_u32x4(base + min(row, (int64_t)rows - 1) * ld + min(k, ld - 8));
+  return ok ? v : u32x4{0u, 0u, 0u, 0u};
+}
+
 // ---------------------------------------------------------------------------
 // distance GEMM with argmin epilogue: rows = centers, cols = tokens
 // ---------------------------------------------------------------------------
@@ -225,12 +245,19 @@ struct DistProblem {
   const float* mu2;
   uint64_t* best;    // [slot][N]: (order-preserving distance bits << 32 | a) of the slot's nearest
   uint64_t* second;  // [slot][N]: the same for the slot's runner-up
-  __device__ u32x4 load_a(int, int m, int k) const { return load8_bf16(mu, m, K, k, m < M && k < K); }
-  __device__ u32x4 load_b(int, int n, int k) const { return load8_bf16(x, n, K, k, n < N && k < K); }
+  __device__ u32x4 load_a(int, int m, int k) const { return load8_bf16_always(mu, m, M, K, k); }
+  __device__ u32x4 load_b(int, int n, int k) const { return load8_bf16_always(x, n, N, K, k); }
   // one wave = centers m0 .. m0 + 63 (slot m0 / 64) x tokens n0 .. n0 + 63;
   // candidates are ordered by (distance, index)
   __device__ void epilogue(int, int m0, int n0, int lane, const f32x16 (&acc)[2][2]) const {
     if (m0 >= M) return;  // no center in this quadrant
+    // the norms of the lane's 32 centers, all requested before any is used
+    // (one wait instead of one per center)
+    float nm[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) nm[i][e] = mu2[min(m0 + 32 * i + acc_row(e, lane), M - 1)];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint64_t k1 = ~0ull, k2 = ~0ull;  // the lane's nearest and runner-up
@@ -240,7 +267,7 @@ struct DistProblem {
         for (int e = 0; e < 16; ++e) {
           const int a = m0 + 32 * i + acc_row(e, lane);
           if (a < M) {
-            const float dist = mu2[a] - 2.f * acc[i][j][e];
+            const float dist = nm[i][e] - 2.f * acc[i][j][e];
             const uint64_t k = ((uint64_t)ordered_bits(dist) << 32) | (uint32_t)a;
             if (k < k1) {
               k2 = k1;
@@ -281,12 +308,10 @@ struct DistSplitProblem {
   const uint16_t* x;
   float* part;  // [splits][N][M]
   __device__ u32x4 load_a(int z, int m, int k) const {
-    const int kk = z * K + k;
-    return load8_bf16(mu, m, Kfull, kk, m < M && kk < Kfull);
+    return load8_bf16_always(mu, m, M, Kfull, z * K + k);
   }
   __device__ u32x4 load_b(int z, int n, int k) const {
-    const int kk = z * K + k;
-    return load8_bf16(x, n, Kfull, kk, n < N && kk < Kfull);
+    return load8_bf16_always(x, n, N, Kfull, z * K + k);
   }
   // lane: token n0 + 32 j + lane % 32, centers m0 + 32 i + acc_row(e): runs of
   // four consecutive centers (e % 4), stored as one 16-byte piece when whole
@@ -594,7 +619,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
 namespace {
 // workspace of the assignment: ||mu||^2, per-block maxima of it, slot records
 struct AssignLayout {
-  size_t mu2, bmax, best, second, part, total;
+  size_t mu2, mu2d, bmax, best, second, part, total;
   int nbmax, splits;
 };
 // K splits of the distance product: one when its 128 x 128 tiles fill the
@@ -619,6 +644,7 @@ AssignLayout assign_layout(int64_t N, int32_t A) {
   };
   L.nbmax = (int)ceil_div(A, NORM_CPB);
   L.mu2 = take(sizeof(float) * A);
+  L.mu2d = take(sizeof(double) * A);
   L.bmax = take(sizeof(float) * L.nbmax);
   L.best = take(sizeof(uint64_t) * nslot * N);
   L.second = take(sizeof(uint64_t) * nslot * N);
@@ -645,33 +671,36 @@ nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void
   const int W = s->H * s->d;
   const AssignLayout L = assign_layout(N, A);
   float* mu2 = reinterpret_cast<float*>(ws + L.mu2);
+  double* mu2d = reinterpret_cast<double*>(ws + L.mu2d);
   float* bmax = reinterpret_cast<float*>(ws + L.bmax);
   uint64_t* best = reinterpret_cast<uint64_t*>(ws + L.best);
   uint64_t* second = reinterpret_cast<uint64_t*>(ws + L.second);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* mub = static_cast<const uint16_t*>(centers);
   hipLaunchKernelGGL(k_center_norms, dim3((unsigned)L.nbmax), dim3(256), 0, st, mub, A, W, mu2,
-                     bmax);
+                     mu2d, bmax);
   NKV_LAUNCH_CHECK();
   nkv_status e;
-  // (the register-staged GEMM with 64-wide k steps: measured faster here
-  // than the direct-to-LDS one, whose 32-wide steps double the barriers)
+  // (register-staged GEMM with 64-wide k steps, loads two steps ahead:
+  // measured faster here than the direct-to-LDS one, whose 32-wide steps
+  // double the barriers)
   const int kc = (int)std::min<int64_t>(L.splits, W / 64);
   if (kc <= 1) {
     DistProblem dp{A, (int)N, W, mub, xb, mu2, best, second};
-    if ((e = launch_gemm(dp, 1, st))) return e;
+    if ((e = launch_gemm_pf2(dp, 1, st))) return e;
   } else {
     const int chunk = (int)ceil_div(ceil_div(W, kc), 64) * 64;
     const int splits = (int)ceil_div(W, chunk);
     float* part = reinterpret_cast<float*>(ws + L.part);
     DistSplitProblem sp{A, (int)N, chunk, W, mub, xb, part};
-    if ((e = launch_gemm(sp, splits, st))) return e;
+    if ((e = launch_gemm_pf2(sp, splits, st))) return e;
     hipLaunchKernelGGL(k_dist_reduce, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st, part,
                        splits, N, A, mu2, best, second);
     NKV_LAUNCH_CHECK();
   }
   hipLaunchKernelGGL(k_argmin_reduce, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st, best,
-                     second, (int)ceil_div(A, 64), N, W, xb, xnorm, mub, A, bmax, L.nbmax, idx);
+                     second, (int)ceil_div(A, 64), N, W, xb, xnorm, mub, A, mu2d, bmax, L.nbmax,
+                     idx);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }
