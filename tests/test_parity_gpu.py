@@ -475,6 +475,30 @@ def test_attend_edge_cases(kw, route):
         assert rel <= OUT_TOL and lerr <= LSE_TOL
 
 
+# The decoder-stationary decode (r % 64 == 0, here r = 128) writes whole
+# groups of 32 rows: one token, ragged group tails, no current chunk (the
+# padding rows then come only from the key padding), and full-routed rows in
+# several ranges of odd lengths between low ones.  (With a handful of keys
+# the LSE compares a few scores, whose bf16 key rounding alone reaches the
+# LSE tolerance: the short histories come with a 64-token current chunk.)
+@pytest.mark.parametrize("n_hist,N_cur,route", [
+    (1, 64, None),
+    (33, 64, None),
+    (95, 0, None),
+    (700, 13, [(0, 37, 0), (37, 300, 1), (300, 333, 0), (333, 640, 1), (640, 700, 0)]),
+])
+def test_decode_pair_ragged_groups_and_ranges(n_hist, N_cur, route):
+    cfg = dataclasses.replace(SMALL["S5"], name=f"dp{n_hist}_{N_cur}", n_hist=n_hist,
+                              N_cur=N_cur, Nq=70, n_full_tail=n_hist)
+    case = get_case(cfg)
+    fast = route is not None
+    out, lse, rows = _run_attend(case, None, route, fast=fast)
+    ro, rl = _oracle_attend(case, rows, fast, route, cfg.r_low)
+    rel, lerr = attention_errors(out, lse, ro, rl)
+    log(f"  decode pair n_hist={n_hist} N_cur={N_cur} fast={fast}: {rel:.3e} {lerr:.3e}")
+    assert rel <= OUT_TOL and lerr <= LSE_TOL
+
+
 def test_fast_with_full_rank_matches_full_read():
     cfg = SMALL["S2"]
     case = get_case(cfg)
