@@ -170,56 +170,75 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_flash(const uint16_t* __res
           if (tile * FA_KT + kb * 32 + fa_key_of_row(acc_row(e, lane)) >= Nk) s[kb][e] = -INFINITY;
     }
     // ---- online softmax (base 2, lazy rescale) ----------------------------
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c;
-    if (mt > m_run + 8.f) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
-      l_part *= alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-      m_run = mt;
-    }
+    // The running maximum only moves when a score exceeds it by more than 2^8.
+    // Instead of the tile maximum before the exponentials, the tile's p are
+    // formed from the running maximum and the wave checks the lanes' sums: a
+    // sum of at most 256 means no p above 256, so nothing moves.  Otherwise
+    // (or when the sum is not finite: the first tile meets an empty maximum)
+    // the tile maximum is taken and, where it moves, O and l are rescaled
+    // and the p formed again.
     // P for 16 keys (step j: key block j/2, half j%2), packed to bf16: the
     // elements 8 (j%2) .. +7 of the lane are the keys 16 j + 8 (lane/32) + 0..7
-    auto probs = [&](int j) __attribute__((always_inline)) {
+    auto probs = [&](int j, float& ss) __attribute__((always_inline)) {
       const int kb = j >> 1, half = j & 1;
       u32x4 pk;
+      float sum = 0.f;
 #pragma unroll
       for (int uu = 0; uu < 4; ++uu) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * uu], c, -m_run));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * uu + 1], c, -m_run));
-        l_part += p0 + p1;
+        sum += p0 + p1;
         pk[uu] = pack_bf16x2(p0, p1);
       }
+      ss = sum;
       return as_bf16x8(pk);
     };
-    // ---- O^T += V^T P^T: V fragments one 16-key step ahead, each step's
-    // MFMAs overlapping the exponentials of the next ----------------------
-    bf16x8 p = probs(0);
+    // all four steps' p first, then one check for the tile (a rescale must
+    // come before the tile's first P V MFMA: rescaling accumulators that
+    // MFMAs have already written costs registers the kernel does not have)
+    float s0s, s1s, s2s, s3s;
+    bf16x8 p0 = probs(0, s0s), p1 = probs(1, s1s), p2 = probs(2, s2s), p3 = probs(3, s3s);
+    {
+      const float ss = (s0s + s1s) + (s2s + s3s);
+      if (__ballot(!(ss <= 256.f))) {  // wave-uniform: the maximum needs both lane halves
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c;
+        if (mt > m_run + 8.f) {  // per row, the same in both lane halves
+          const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+          l_part *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+          m_run = mt;
+          p0 = probs(0, s0s);
+          p1 = probs(1, s1s);
+          p2 = probs(2, s2s);
+          p3 = probs(3, s3s);
+        }
+      }
+      l_part += (s0s + s1s) + (s2s + s3s);
+    }
+    // ---- O^T += V^T P^T: V fragments one 16-key step ahead ----------------
     __builtin_amdgcn_sched_barrier(0);
     read_v4(1, vb);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(va[db], p, o[db]);
-    p = probs(1);
+    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(va[db], p0, o[db]);
     __builtin_amdgcn_sched_barrier(0);
     read_v4(2, va);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(vb[db], p, o[db]);
-    p = probs(2);
+    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(vb[db], p1, o[db]);
     __builtin_amdgcn_sched_barrier(0);
     read_v4(3, vb);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(va[db], p, o[db]);
-    p = probs(3);
+    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(va[db], p2, o[db]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(vb[db], p, o[db]);
+    for (int db = 0; db < 4; ++db) o[db] = mfma_bf16(vb[db], p3, o[db]);
     // tile + 1 has landed (this wave's share) and every wave is done with
     // this stage before it is loaded again
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
