@@ -182,15 +182,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_flash(const uint16_t* __res
     auto probs = [&](int j, float& ss) __attribute__((always_inline)) {
       const int kb = j >> 1, half = j & 1;
       u32x4 pk;
-      float sum = 0.f;
+      float pair[4];
 #pragma unroll
       for (int uu = 0; uu < 4; ++uu) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * uu], c, -m_run));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * half + 2 * uu + 1], c, -m_run));
-        sum += p0 + p1;
+        pair[uu] = p0 + p1;
         pk[uu] = pack_bf16x2(p0, p1);
       }
-      ss = sum;
+      // a tree from the first pair on: seven adds for eight values (a sum
+      // started from 0.f keeps an add the compiler may not drop, as 0 + -0 is +0)
+      ss = (pair[0] + pair[1]) + (pair[2] + pair[3]);
       return as_bf16x8(pk);
     };
     // all four steps' p first, then one check for the tile (a rescale must
