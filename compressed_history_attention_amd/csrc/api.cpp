@@ -490,7 +490,7 @@ nkv_status nkv_fit_centers(const nkv_shape* shape, const void* x, int64_t N, voi
     return launch_assign_generic(shape->dtype, x, N, W, centers, A, out, s);
   };
   if (tuned && N > 0 && (iters > 0 || idx || counts)) {
-    ProfScope ps("fit_assign", s);
+    ProfScope ps("fit_rownorm", s);
     if ((st = tuned_row_sqnorm(shape, x, N, xn, s))) return st;
   }
   for (int it = 0; it < iters; ++it) {

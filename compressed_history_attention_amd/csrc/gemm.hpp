@@ -93,8 +93,50 @@ __global__ __launch_bounds__(256) void k_gemm(const P p) {
 // the loads of step kt + 2 are in flight and step kt + 1 waits in registers
 // for the buffer step kt - 1 freed.  For long K with global latency that one
 // step's MFMAs do not cover (P::BK == 64).
+// Block order of a 1-D grid for a short M (the centers) and a long N (the
+// tokens).  N tiles slowest would stream all of B once per M tile.  Here
+// the hardware deals consecutive blocks to the 8 XCDs in turn (block b runs
+// on XCD b % 8), and with G > 0 the M tiles form mt / G groups of G, each
+// group served by 8 / (mt / G) XCDs that split the N tiles between them:
+// an XCD runs its N tiles in order, the G blocks of one N tile together, so
+// the N tile's B rows are fetched into its L2 once for G products and its
+// G M tiles of A rows stay resident; B is read 8 / G times in all.  G = 0:
+// M tiles fastest in plain order.
+struct TileOrder {
+  int mt, nt;   // M and N tiles
+  int G;        // M tiles per group, or 0
+  int ng, xpg;  // groups; XCDs per group (ng * xpg = 8)
+  int blocks;   // grid size (grouped: whole rounds of every XCD, some empty)
+  __device__ bool map(int b, int& m_t, int& n_t) const {
+    if (G == 0) {
+      m_t = b % mt;
+      n_t = b / mt;
+      return true;
+    }
+    const int x = b & 7, i = b >> 3;
+    n_t = (i / G) * xpg + x / ng;
+    m_t = (x % ng) * G + i % G;
+    return n_t < nt;
+  }
+};
+
+// the grouping for mt x nt tiles: the largest G <= gmax that divides mt
+// with mt / G dividing 8, else plain order
+inline TileOrder make_tile_order(int64_t mt, int64_t nt, int gmax) {
+  TileOrder o{(int)mt, (int)nt, 0, 1, 8, (int)(mt * nt)};
+  for (int64_t G = std::min<int64_t>(gmax, mt); G >= 2; --G)
+    if (mt % G == 0 && 8 % (mt / G) == 0) {
+      o.G = (int)G;
+      o.ng = (int)(mt / G);
+      o.xpg = 8 / o.ng;
+      o.blocks = (int)(8 * ((nt + o.xpg - 1) / o.xpg) * G);
+      break;
+    }
+  return o;
+}
+
 template <class P>
-__global__ __launch_bounds__(256) void k_gemm_pf2(const P p) {
+__global__ __launch_bounds__(256) void k_gemm_pf2(const P p, const TileOrder o) {
   constexpr int BK = P::BK;
   static_assert(BK == 64, "K step");
   constexpr int LS = BK + 8;              // bf16 elements per LDS row
@@ -104,7 +146,9 @@ __global__ __launch_bounds__(256) void k_gemm_pf2(const P p) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][GEMM_BN * LS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int z = blockIdx.z;
-  const int m_blk = blockIdx.y * GEMM_BM, n_blk = blockIdx.x * GEMM_BN;
+  int m_t, n_t;
+  if (!o.map((int)blockIdx.x, m_t, n_t)) return;  // the whole block, before any barrier
+  const int m_blk = m_t * GEMM_BM, n_blk = n_t * GEMM_BN;
   const int ld_row0 = tid / TPR, ld_k = (tid % TPR) * 8;
   u32x4 ra[2][LD], rb[2][LD];
   auto fetch = [&](int set, int k0) __attribute__((always_inline)) {
@@ -175,11 +219,15 @@ __global__ __launch_bounds__(256) void k_gemm_pf2(const P p) {
   p.epilogue(z, m_blk + wm, n_blk + wn, lane, acc);
 }
 
+// gmax: the largest M-tile group of the block order (0 or 1: plain order)
 template <class P>
-inline nkv_status launch_gemm_pf2(const P& p, int batch, hipStream_t s) {
+inline nkv_status launch_gemm_pf2(const P& p, int batch, hipStream_t s, int gmax) {
   if (p.M <= 0 || p.N <= 0 || batch <= 0) return NKV_OK;
-  dim3 grid((unsigned)ceil_div(p.N, GEMM_BN), (unsigned)ceil_div(p.M, GEMM_BM), (unsigned)batch);
-  hipLaunchKernelGGL(k_gemm_pf2<P>, grid, dim3(256), 0, s, p);
+  const int64_t mt = ceil_div(p.M, GEMM_BM), nt = ceil_div(p.N, GEMM_BN);
+  if (mt * nt > (int64_t)1 << 30) return NKV_EUNSUPPORTED;  // a grid of whole XCD rounds stays < 2^31
+  const TileOrder o = make_tile_order(mt, nt, gmax);
+  dim3 grid((unsigned)o.blocks, 1, (unsigned)batch);
+  hipLaunchKernelGGL(k_gemm_pf2<P>, grid, dim3(256), 0, s, p, o);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }

@@ -4,13 +4,13 @@
 //   1. ||mu_a||^2 per center (fp32).
 //   2. Distance GEMM  d(a, t) = ||mu_a||^2 - 2 mu_a . x_t  on bf16 MFMA (bf16
 //      products are exact in fp32); the epilogue reduces each token's
-//      column over the wave's 64 centers to (min distance, lowest index)
-//      and the runner-up distance, one record per 64-center slot.  A
-//      per-token pass takes the best record; when the runner-up lies within
-//      a rigorous bound on the fp32 rounding error of the two distances it
-//      assigns the token again in fp64 (the same ||mu||^2 - 2 mu . x form),
-//      so the argmin is the one exact arithmetic gives, ties to the lowest
-//      index.
+//      column over the wave's 64 centers to its three nearest by
+//      (distance, index), one record each per 64-center slot.  A per-token
+//      pass takes the best record; when the runner-up lies within a
+//      rigorous bound on the fp32 rounding error of the two distances it
+//      assigns the token again in fp64 (the same ||mu||^2 - 2 mu . x form)
+//      over the candidate centers the slot records leave, so the argmin is
+//      the one exact arithmetic gives, ties to the lowest index.
 //   3. Projection GEMM z = E (x - mu_a): the fp32 residual (exact for bf16
 //      inputs) is split into three bf16 terms hi + mid + lo = e, so three
 //      exact-product MFMA passes with fp32 accumulation give the projection
@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256) void k_row_sqnorm(const uint16_t* __restrict__
 
 __global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restrict__ best,
                                                        const uint64_t* __restrict__ second,
+                                                       const uint64_t* __restrict__ third,
                                                        int nslot, int64_t N, int W,
                                                        const uint16_t* __restrict__ x,
                                                        const float* __restrict__ xnorm,
@@ -173,10 +174,11 @@ __global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restric
     // fp64 assignment, the lane's channels w = 8 lane + 512 k .. + 7.  The
     // exact nearest center has a computed distance within E of d1: in each
     // 64-center slot whose nearest is that close, the nearest is a
-    // candidate, and so is every center of the slot if its runner-up is
-    // that close too.  Candidates are met in increasing center order (ties
-    // keep the lowest index); every center when none is found (non-finite
-    // distances).
+    // candidate, so is its runner-up if that close too, and so is every
+    // center of the slot if its third is that close as well (the others are
+    // no closer than the third).  Candidates are met in increasing center
+    // order (ties keep the lowest index); every center when none is found
+    // (non-finite distances).
     double bd = INFINITY;
     int ba = 0x7fffffff;
     auto scan = [&](int a0, int a1) {
@@ -203,12 +205,20 @@ __global__ __launch_bounds__(256) void k_argmin_reduce(const uint64_t* __restric
     };
     const float lim = d1 + E;
     for (int sl = 0; sl < nslot; ++sl) {
-      const uint64_t kb = best[(int64_t)sl * N + t], ks = second[(int64_t)sl * N + t];
+      const int64_t o = (int64_t)sl * N + t;
+      const uint64_t kb = best[o], ks = second[o];
       if (!(dist_of(kb) <= lim)) continue;
+      const int a = (int)(kb & 0xffffffffu);
       if (ks != ~0ull && dist_of(ks) <= lim) {
-        scan(sl * 64, min(A, sl * 64 + 64));
+        const uint64_t k3 = third[o];
+        if (k3 != ~0ull && dist_of(k3) <= lim) {
+          scan(sl * 64, min(A, sl * 64 + 64));
+        } else {
+          const int a2 = (int)(ks & 0xffffffffu);
+          scan(min(a, a2), min(a, a2) + 1);
+          scan(max(a, a2), max(a, a2) + 1);
+        }
       } else {
-        const int a = (int)(kb & 0xffffffffu);
         scan(a, a + 1);
       }
     }
@@ -245,6 +255,7 @@ struct DistProblem {
   const float* mu2;
   uint64_t* best;    // [slot][N]: (order-preserving distance bits << 32 | a) of the slot's nearest
   uint64_t* second;  // [slot][N]: the same for the slot's runner-up
+  uint64_t* third;   // [slot][N]: and for its third
   __device__ u32x4 load_a(int, int m, int k) const { return load8_bf16_always(mu, m, M, K, k); }
   __device__ u32x4 load_b(int, int n, int k) const { return load8_bf16_always(x, n, N, K, k); }
   // one wave = centers m0 .. m0 + 63 (slot m0 / 64) x tokens n0 .. n0 + 63;
@@ -260,7 +271,9 @@ struct DistProblem {
       for (int e = 0; e < 16; ++e) nm[i][e] = mu2[min(m0 + 32 * i + acc_row(e, lane), M - 1)];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      uint64_t k1 = ~0ull, k2 = ~0ull;  // the lane's nearest and runner-up
+      // the lane's three nearest, k1 < k2 < k3 (keys are distinct: the
+      // index is in them)
+      uint64_t k1 = ~0ull, k2 = ~0ull, k3 = ~0ull;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -270,25 +283,35 @@ struct DistProblem {
             const float dist = nm[i][e] - 2.f * acc[i][j][e];
             const uint64_t k = ((uint64_t)ordered_bits(dist) << 32) | (uint32_t)a;
             if (k < k1) {
+              k3 = k2;
               k2 = k1;
               k1 = k;
             } else if (k < k2) {
+              k3 = k2;
               k2 = k;
+            } else if (k < k3) {
+              k3 = k;
             }
           }
         }
       }
-      const uint64_t o1 = __shfl_xor(k1, 32, 64), o2 = __shfl_xor(k2, 32, 64);
-      // nearest and runner-up of the union of both lanes' candidates
-      const uint64_t b = k1 < o1 ? k1 : o1;
-      const uint64_t r1 = k1 < o1 ? o1 : k1;           // the other lane's nearest
-      const uint64_t r2 = k1 < o1 ? k2 : o2;           // the winner's own runner-up
-      const uint64_t sec = r1 < r2 ? r1 : r2;
+      const uint64_t o1 = __shfl_xor(k1, 32, 64), o2 = __shfl_xor(k2, 32, 64),
+                     o3 = __shfl_xor(k3, 32, 64);
+      // the three nearest of both lanes' (sorted) triples: the smaller first
+      // key wins; the rest merge the winner's (k2, k3) with the loser's
+      // (o1, o2)
+      const bool mine = k1 < o1;
+      const uint64_t b = mine ? k1 : o1;
+      const uint64_t w2 = mine ? k2 : o2, w3 = mine ? k3 : o3;  // the winner's other two
+      const uint64_t l1 = mine ? o1 : k1, l2 = mine ? o2 : k2;  // the loser's first two
+      const uint64_t sec = w2 < l1 ? w2 : l1;
+      const uint64_t thd = w2 < l1 ? (w3 < l1 ? w3 : l1) : (w2 < l2 ? w2 : l2);
       const int n = n0 + 32 * j + (lane & 31);
       if (lane < 32 && n < N) {
         const int64_t o = (int64_t)(m0 / 64) * N + n;
         best[o] = b;
         second[o] = sec;
+        third[o] = thd;
       }
     }
   }
@@ -342,13 +365,14 @@ struct DistSplitProblem {
 };
 
 // Split partials -> the slot records of DistProblem's epilogue: one wave per
-// token, lane l holding center 64 slot + l (nearest and runner-up of each
-// 64-center slot by (distance, index), as there)
+// token, lane l holding center 64 slot + l (nearest, runner-up and third of
+// each 64-center slot by (distance, index), as there)
 __global__ __launch_bounds__(256) void k_dist_reduce(const float* __restrict__ part, int splits,
                                                      int64_t N, int A,
                                                      const float* __restrict__ mu2,
                                                      uint64_t* __restrict__ best,
-                                                     uint64_t* __restrict__ second) {
+                                                     uint64_t* __restrict__ second,
+                                                     uint64_t* __restrict__ third) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= N) return;  // whole waves
@@ -373,9 +397,16 @@ __global__ __launch_bounds__(256) void k_dist_reduce(const float* __restrict__ p
       const uint64_t v = __shfl_xor(r, o, 64);
       r = v < r ? v : r;
     }
+    uint64_t q = (k == b || k == r) ? ~0ull : k;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t v = __shfl_xor(q, o, 64);
+      q = v < q ? v : q;
+    }
     if (lane == 0) {
       best[(int64_t)sl * N + t] = b;
       second[(int64_t)sl * N + t] = r;
+      third[(int64_t)sl * N + t] = q;
     }
   }
 }
@@ -629,7 +660,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
 namespace {
 // workspace of the assignment: ||mu||^2, per-block maxima of it, slot records
 struct AssignLayout {
-  size_t mu2, mu2d, bmax, best, second, part, total;
+  size_t mu2, mu2d, bmax, best, second, third, part, total;
   int nbmax, splits;
 };
 // K splits of the distance product: one when its 128 x 128 tiles fill the
@@ -658,6 +689,7 @@ AssignLayout assign_layout(int64_t N, int32_t A) {
   L.bmax = take(sizeof(float) * L.nbmax);
   L.best = take(sizeof(uint64_t) * nslot * N);
   L.second = take(sizeof(uint64_t) * nslot * N);
+  L.third = take(sizeof(uint64_t) * nslot * N);
   L.splits = dist_splits(N, A);
   L.part = L.splits > 1 ? take(sizeof(float) * L.splits * N * A) : 0;
   L.total = off;
@@ -685,6 +717,7 @@ nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void
   float* bmax = reinterpret_cast<float*>(ws + L.bmax);
   uint64_t* best = reinterpret_cast<uint64_t*>(ws + L.best);
   uint64_t* second = reinterpret_cast<uint64_t*>(ws + L.second);
+  uint64_t* third = reinterpret_cast<uint64_t*>(ws + L.third);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* mub = static_cast<const uint16_t*>(centers);
   hipLaunchKernelGGL(k_center_norms, dim3((unsigned)L.nbmax), dim3(256), 0, st, mub, A, W, mu2,
@@ -694,23 +727,26 @@ nkv_status tuned_assign(const nkv_shape* s, const void* x, int64_t N, const void
   // (register-staged GEMM with 64-wide k steps, loads two steps ahead:
   // measured faster here than the direct-to-LDS one, whose 32-wide steps
   // double the barriers)
+  // block order: groups of up to DIST_GROUP center tiles per XCD group
+  // (their center rows, 768 KiB per tile at W = 3072, stay in its L2)
+  constexpr int DIST_GROUP = 4;
   const int kc = (int)std::min<int64_t>(L.splits, W / 64);
   if (kc <= 1) {
-    DistProblem dp{A, (int)N, W, mub, xb, mu2, best, second};
-    if ((e = launch_gemm_pf2(dp, 1, st))) return e;
+    DistProblem dp{A, (int)N, W, mub, xb, mu2, best, second, third};
+    if ((e = launch_gemm_pf2(dp, 1, st, DIST_GROUP))) return e;
   } else {
     const int chunk = (int)ceil_div(ceil_div(W, kc), 64) * 64;
     const int splits = (int)ceil_div(W, chunk);
     float* part = reinterpret_cast<float*>(ws + L.part);
     DistSplitProblem sp{A, (int)N, chunk, W, mub, xb, part};
-    if ((e = launch_gemm_pf2(sp, splits, st))) return e;
+    if ((e = launch_gemm_pf2(sp, splits, st, DIST_GROUP))) return e;
     hipLaunchKernelGGL(k_dist_reduce, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st, part,
-                       splits, N, A, mu2, best, second);
+                       splits, N, A, mu2, best, second, third);
     NKV_LAUNCH_CHECK();
   }
   hipLaunchKernelGGL(k_argmin_reduce, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st, best,
-                     second, (int)ceil_div(A, 64), N, W, xb, xnorm, mub, A, mu2d, bmax, L.nbmax,
-                     idx);
+                     second, third, (int)ceil_div(A, 64), N, W, xb, xnorm, mub, A, mu2d, bmax,
+                     L.nbmax, idx);
   NKV_LAUNCH_CHECK();
   return NKV_OK;
 }

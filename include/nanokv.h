@@ -246,7 +246,7 @@ nkv_status nkv_attend_fast_maps(const nkv_shape* shape, const nkv_branch* k,
  * the library holds on every GPU it runs on until the process ends.
  * Limit: calls whose nkv_encode_workspace_size exceeds that size return
  * NKV_EUNSUPPORTED before touching the device (at W = 3072, A = 1024,
- * r = 384 a 4680-token chunk needs 21.7 MiB and about 6900 tokens fit;
+ * r = 384 a 4680-token chunk needs 22.3 MiB and about 6700 tokens fit;
  * split larger inputs into several calls).  Every call
  * on one GPU shares the array: calls that overlap on one GPU (several
  * streams or host threads) race and must be serialised by the caller.

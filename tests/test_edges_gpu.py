@@ -134,21 +134,27 @@ def _bf16_away_from_zero(x, floor=2.0 ** -6):
     return synth.f64_to_bf16_bits(x)
 
 
-def _near_tie_set(W, A, N, seed):
-    """Centers in pairs: center 2j+1 is center 2j with one channel moved by one
-    bf16 step (pairs with j % 4 == 3 are exact duplicates); tokens sit near
-    the even center of a pair, so the two distances differ by ~3e-3 against
-    fp32 rounding errors of ~1e-2 in distances near ||mu||^2 ~ 64 W."""
+def _near_tie_set(W, A, N, seed, group=2):
+    """Centers in groups of `group`: center g j + k (k >= 1) is center g j with
+    one channel moved by one bf16 step (groups with j % 4 == 3: exact
+    duplicates); tokens sit near the first center of a group, so the group's
+    distances differ by ~3e-3 against fp32 rounding errors of ~1e-2 in
+    distances near ||mu||^2 ~ 64 W.  Pairs leave a 64-center slot's third
+    nearest far away (two candidates per slot); triples bring the third
+    within the bound too (the whole slot is searched).  Centers past the
+    last whole group are independent draws."""
     rng = np.random.default_rng(seed)
-    even = _bf16_away_from_zero(8.0 * rng.standard_normal((A // 2, W)))
-    odd = even.copy()
-    ch = rng.integers(0, W, size=A // 2)
-    for j in range(A // 2):
-        if j % 4 != 3:
-            odd[j, ch[j]] = np.uint16(int(odd[j, ch[j]]) + (1 if rng.random() < 0.5 else -1))
-    mu = np.empty((A, W), np.uint16)
-    mu[0::2], mu[1::2] = even, odd
-    a = rng.integers(0, A // 2, size=N) * 2
+    ng = A // group
+    base = _bf16_away_from_zero(8.0 * rng.standard_normal((A, W)))
+    mu = base.copy()
+    for j in range(ng):
+        for k in range(1, group):
+            mu[group * j + k] = mu[group * j]
+            if j % 4 != 3:
+                c = rng.integers(0, W)
+                mu[group * j + k, c] = np.uint16(int(mu[group * j, c]) +
+                                                 (1 if rng.random() < 0.5 else -1))
+    a = rng.integers(0, ng, size=N) * group
     x = synth.bf16_bits_to_f64(mu[a]) + 0.05 * rng.standard_normal((N, W))
     return mu, _bf16_away_from_zero(x)
 
@@ -168,13 +174,14 @@ def _exact_argmin(x_bits, mu_bits, rows):
 # (A, N): 600 tokens x 64 centers make too few 128 x 128 tiles for the chip,
 # so the tuned distance product is split over K; 16384 x 256 fill it and take
 # the unsplit product with its own epilogue
+@pytest.mark.parametrize("group", [2, 3], ids=["pairs", "triples"])
 @pytest.mark.parametrize("size", [(64, 600), (256, 16384)], ids=["split-k", "one-pass"])
 @pytest.mark.parametrize("generic", [False, True])
-def test_assign_near_ties_and_duplicates(generic, size):
+def test_assign_near_ties_and_duplicates(generic, size, group):
     H, d, r = 2, 128, 64
     A, N = size
     W = H * d
-    mu, x = _near_tie_set(W, A, N, seed=7)
+    mu, x = _near_tie_set(W, A, N, seed=7, group=group)
     enc = synth.f64_to_bf16_bits(np.linalg.qr(np.random.default_rng(8).standard_normal((W, r)))[0].T
                                  .copy())
     ref = oracle.encode(x, mu, enc, 32, "bf16")
