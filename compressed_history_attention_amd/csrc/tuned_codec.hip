@@ -659,6 +659,20 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
 
 namespace {
 // workspace of the assignment: ||mu||^2, per-block maxima of it, slot records
+// compute units of the current device (cached per device)
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 struct AssignLayout {
   size_t mu2, mu2d, bmax, best, second, third, part, total;
   int nbmax, splits;
@@ -1424,21 +1438,6 @@ nkv_status launch_decode_tuned(const BranchArgs& b, int W, int r, int group,
   DecodeProblem p{(int)rows.total, W, r, group, b, rows, out, ld, false};
   return launch_gemm(p, 1, st);
 }
-
-namespace {
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v <= 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cache[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
-}  // namespace
 
 nkv_status launch_decode_pair_tuned(const BranchArgs& kb, const BranchArgs& vb, int W, int r,
                                     int group, const RangeTable& rows, uint16_t* kout,

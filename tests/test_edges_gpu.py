@@ -214,6 +214,29 @@ def test_assign_near_ties_and_duplicates(generic, size, group):
     log(f"  {rep}")
 
 
+@pytest.mark.parametrize("group", [2, 3], ids=["pairs", "triples"])
+def test_assign_near_ties_many_tiles(group):
+    """2048 centers x 32768 tokens: 16 x 256 tiles of 128 x 128, so the
+    distance product's block order forms four groups of four center tiles,
+    each served by two XCDs (the C4-sized fitting has two groups of four)."""
+    H, d, r = 2, 128, 64
+    A, N = 2048, 32768
+    W = H * d
+    mu, x = _near_tie_set(W, A, N, seed=11, group=group)
+    enc = synth.f64_to_bf16_bits(np.linalg.qr(np.random.default_rng(8).standard_normal((W, r)))[0].T
+                                 .copy())
+    ref = oracle.encode(x, mu, enc, 32, "bf16")
+    shape = lib.Shape(H, d, r, 32, "bf16")
+    idx, codes, sc = lib.encode(shape, to_dev(x, "bf16"), to_dev(mu, "bf16"), to_dev(enc, "bf16"))
+    torch.cuda.synchronize()
+    gidx = idx.cpu().numpy()
+    bad = np.flatnonzero(gidx != ref["idx"])
+    log(f"many-tile near-tie set ({group} per group): {len(bad)} index differences of {N}")
+    assert len(bad) == 0, f"indices differ at {bad[:10]}"
+    rep = check_encode(gidx, codes.cpu().numpy(), sc.cpu().numpy(), ref, 32)
+    log(f"  {rep}")
+
+
 # --------------------------------------------------------------------------
 # low-dimensional rows recomputed exactly (score bound too loose)
 # --------------------------------------------------------------------------
