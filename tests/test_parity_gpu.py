@@ -353,6 +353,36 @@ def test_low_read_with_few_tokens_ignores_stale_workspace():
         assert rel <= OUT_TOL and lerr <= LSE_TOL
 
 
+def test_fast_read_at_the_center_limit():
+    """4096 centers per branch (the most the attention entry points take):
+    the encoder's nearest center over 64 slots, and a Fast read whose 64 x 64
+    center-range buckets mostly hold one or two of the 6000 low-routed
+    tokens (nearly every tile ragged), on a NaN-filled workspace."""
+    cfg = S("C3", H=2, r=128, A=4096, n_hist=6000, Nq=130, N_cur=40, chunk=3000, r_low=64,
+            n_full_tail=700, seed=45)
+    w = synth.workload(cfg)
+    for b in range(2):
+        x = w.history_chunk(b, 0)[0]
+        rep, _ = _encode_and_check(cfg, x, b, w)
+        log(f"encode at 4096 centers, branch {b}: {rep}")
+    case = get_case(cfg)
+    shape = shape_of(cfg)
+    kb, vb = device_branch(case, 0), device_branch(case, 1)
+    q = to_dev(case.w.queries(), cfg.dtype)
+    ck, cv = to_dev(case.w.current(0), cfg.dtype), to_dev(case.w.current(1), cfg.dtype)
+    route = cfg.segments()
+    n = lib.nkv_attend_workspace_size(shape, cfg.A, cfg.A, cfg.n_attend, route, cfg.r_low,
+                                      cfg.Nq, cfg.N_cur)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    out, lse = lib.attend_fast(shape, kb, vb, cfg.n_attend, route, cfg.r_low, q, ck, cv, ws=ws)
+    torch.cuda.synchronize()
+    rows = q_rows(cfg, None)
+    ro, rl = _oracle_attend(case, rows, True, route, cfg.r_low)
+    rel, lerr = attention_errors(from_dev(out), from_dev(lse), ro, rl)
+    log(f"Fast read at 4096 centers: rel={rel:.3e} dLSE={lerr:.3e}")
+    assert rel <= OUT_TOL and lerr <= LSE_TOL
+
+
 def test_low_read_center_range_splits_with_empty_ranges():
     """Splits of the main pass at V-center-range boundaries: 960 far-away V
     centers that no token uses put every token in the first of 16 ranges,
