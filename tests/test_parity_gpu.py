@@ -484,6 +484,7 @@ def _edge(name, **kw):
     (dict(n_hist=0, N_cur=0), None),                          # nothing: O = 0, LSE = -inf
     (dict(N_cur=0, n_full_tail=0), None),                     # all history low-dimensional
     (dict(Nq=1), None),                                       # one query
+    (dict(H=1), None),                                        # one head
     (dict(), [(i * 150, (i + 1) * 150, i % 2) for i in range(10)]),  # interleaved routing
 ])
 def test_attend_edge_cases(kw, route):
