@@ -94,6 +94,7 @@ struct Plan {
   TileGeom g;
   // byte offsets inside the low-path workspace
   size_t racc, rell;  // split coefficient sums reduced to bf16 hi/lo planes, and their ell
+  size_t rmass;       // split center masses reduced to planes (one a^V range only), or 0
   size_t dkt, mvt, qt32, qt16, bound, tmax, present, misc, flags, cnt, base, tile_start, bcount,
       tile_bucket, perm, img, acc, wmass, ell, total;
 };
@@ -150,6 +151,9 @@ Plan make_plan(const nkv_shape* s, int32_t A_k, int32_t A_v, const RangeTable& l
   P.ell = take(sizeof(float) * prows);
   P.racc = take(sizeof(float) * P.rows * P.ra);   // rows of 2 x ra bf16
   P.rell = take(sizeof(float) * P.rows);
+  // with a single a^V range the key-range splits leave fp32 mass partials
+  // (several ranges split at range boundaries and write planes directly)
+  P.rmass = P.GV == 1 ? take(sizeof(uint16_t) * 2 * CR * s->H * ceil_div(Nq, 128) * 128) : 0;
   P.total = off;
   return P;
 }
@@ -1168,18 +1172,54 @@ nkv_status launch_main(const MainArgs& m, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// Split center masses of a single a^V range (A_v <= 64) summed into the bf16
+// hi/lo planes the restoration reads (the main kernel's plane layout, whole
+// rows of WS = 64 columns: zero past A_v): thread i takes 4 centers of a row.
+__device__ __forceinline__ void reduce_mass_one(int64_t i, const float* __restrict__ wmass,
+                                                int64_t Nq, int nh, int nsplit, int A_v, int WS,
+                                                uint16_t* __restrict__ planes) {
+  const int per = WS / 4;
+  if (i >= Nq * nh * per) return;
+  const int64_t row = i / per;  // (query, head of the group)
+  const int c = (int)(i - row * per) * 4;
+  const int64_t m = row / nh;
+  const int zb = (int)(row - m * nh);
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* src = wmass + ((int64_t)sp * Nq * nh + row) * A_v + c;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (c + u < A_v) v[u] += src[u];
+  }
+  float l[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) l[u] = v[u] - (float)(__bf16)v[u];
+  const int64_t nmt = (Nq + 127) / 128;
+  *reinterpret_cast<uint2*>(planes + mass_pos(m, zb, c, nmt, WS)) =
+      uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  *reinterpret_cast<uint2*>(planes + mass_pos(m, zb, WS + c, nmt, WS)) =
+      uint2{pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3])};
+}
+
 // Split coefficient sums -> one bf16 hi/lo plane row each (and ell summed),
 // in split order: rows = (query, head of the group); one thread per four
 // plane columns of a row (r_low % 16 == 0; zeros in [r_low, ra)).
-// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_reduce_acc(const float* __restrict__ acc,
                                                     const float* __restrict__ ell, int64_t rows,
                                                     int nsplit, int r_low, int ra,
                                                     uint16_t* __restrict__ racc,
-                                                    float* __restrict__ rell) {
+                                                    float* __restrict__ rell,
+                                                    const float* __restrict__ wmass, int64_t Nq,
+                                                    int nh, int A_v, int WS,
+                                                    uint16_t* __restrict__ planes) {
+  // threads [0, rows * ra / 4): coefficient sums; then, with `planes`, the
+  // center masses of a single a^V range: [rows * ra / 4, + rows * WS / 4)
   const int per = ra / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows * per) return;
+  if (i >= rows * per) {
+    if (planes) reduce_mass_one(i - rows * per, wmass, Nq, nh, nsplit, A_v, WS, planes);
+    return;
+  }
   const int64_t row = i / per;
   const int c = (int)(i - row * per) * 4;
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -1514,18 +1554,28 @@ nkv_status launch_low(const nkv_shape* s, const BranchArgs& kb, const BranchArgs
   ProfScope ps_restore("low_restore", st);
   const float* acc_r = acc;
   const float* ell_r = ell;
+  const float* wmass_r = wmass;
+  bool planes = nsplit == 1 || split.gv;
   if (nsplit > 1) {
+    // split coefficient sums, and (a single a^V range: key-range splits)
+    // the fp32 center-mass partials, reduced to planes in one launch
     const int64_t rows_g = Nq * hs.n;
-    hipLaunchKernelGGL(k_reduce_acc, dim3((unsigned)ceil_div(rows_g * (ra / 4), 256)), dim3(256),
-                       0, st, acc, ell, rows_g, nsplit, r_low, ra,
-                       reinterpret_cast<uint16_t*>(at(P.racc)),
-                       reinterpret_cast<float*>(at(P.rell)));
+    uint16_t* mplanes = !planes && P.rmass ? reinterpret_cast<uint16_t*>(at(P.rmass)) : nullptr;
+    const int64_t n = rows_g * (ra / 4) + (mplanes ? rows_g * (P.GV * CR / 4) : 0);
+    hipLaunchKernelGGL(k_reduce_acc, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, acc, ell,
+                       rows_g, nsplit, r_low, ra, reinterpret_cast<uint16_t*>(at(P.racc)),
+                       reinterpret_cast<float*>(at(P.rell)), wmass, Nq, hs.n, vb.A, P.GV * CR,
+                       mplanes);
     NKV_LAUNCH_CHECK();
     acc_r = reinterpret_cast<const float*>(at(P.racc));
     ell_r = reinterpret_cast<const float*>(at(P.rell));
+    if (mplanes) {
+      wmass_r = reinterpret_cast<const float*>(mplanes);
+      planes = true;
+    }
   }
   RestoreProblem rp{(int)Nq, 128, 2 * ra + 2 * P.av, H, mp.ld, r_low, ra, vb.A, P.av, nsplit,
-                    P.GV * CR, (nsplit == 1 || split.gv) ? 1 : 0, acc_r, wmass,
+                    P.GV * CR, planes ? 1 : 0, acc_r, wmass_r,
                     static_cast<const uint16_t*>(mp.omap), mvt, ell_r, bound, o_low, lse_low, hs};
   if ((e = rp.dma_ok() ? launch_gemm_dma(rp, hs.n, st) : launch_gemm(rp, hs.n, st))) return e;
   }

@@ -383,6 +383,35 @@ def test_fast_read_at_the_center_limit():
     assert rel <= OUT_TOL and lerr <= LSE_TOL
 
 
+def test_low_read_key_splits_of_a_single_center_range():
+    """64 V centers make a single a^V range, so the main pass splits the
+    low-routed keys into key ranges (here five) whose fp32 center masses are
+    summed into bf16 planes before the restoration; NaN-filled workspace."""
+    cfg = S("C3", H=2, r=128, A=64, n_hist=3000, Nq=100, N_cur=30, chunk=1000, r_low=64,
+            n_full_tail=200, seed=46)
+    case = get_case(cfg)
+    shape = shape_of(cfg)
+    kb, vb = device_branch(case, 0), device_branch(case, 1)
+    q = to_dev(case.w.queries(), cfg.dtype)
+    ck, cv = to_dev(case.w.current(0), cfg.dtype), to_dev(case.w.current(1), cfg.dtype)
+    route = cfg.segments()
+    rows = q_rows(cfg, None)
+    for widths in (64, [64, 32]):
+        if isinstance(widths, int):
+            n = lib.nkv_attend_workspace_size(shape, cfg.A, cfg.A, cfg.n_attend, route, widths,
+                                              cfg.Nq, cfg.N_cur)
+        else:
+            n = lib.nkv_attend_heads_workspace_size(shape, cfg.A, cfg.A, cfg.n_attend, route,
+                                                    widths, cfg.Nq, cfg.N_cur)
+        ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+        out, lse = lib.attend_fast(shape, kb, vb, cfg.n_attend, route, widths, q, ck, cv, ws=ws)
+        torch.cuda.synchronize()
+        ro, rl = _oracle_attend(case, rows, True, route, widths)
+        rel, lerr = attention_errors(from_dev(out), from_dev(lse), ro, rl)
+        log(f"single a^V range, key splits, widths={widths}: rel={rel:.3e} dLSE={lerr:.3e}")
+        assert rel <= OUT_TOL and lerr <= LSE_TOL
+
+
 def test_low_read_center_range_splits_with_empty_ranges():
     """Splits of the main pass at V-center-range boundaries: 960 far-away V
     centers that no token uses put every token in the first of 16 ranges,
