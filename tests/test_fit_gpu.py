@@ -62,6 +62,24 @@ def test_fit_tuned_from_label_rows():
         _check(cfg, x, mu0, iters)
 
 
+def test_fit_tuned_random_row_start():
+    """Centers started from random rows, as a k-means++-free start does:
+    several rows of one generating cluster become near-duplicate centers,
+    so many tokens sit within the assignment's rounding bound of two or
+    three of them and are assigned again exactly; results still bit-exact."""
+    cfg = synth.small_config("C3", H=4, r=128, A=64, n_hist=3000, chunk=3000)
+    w = synth.workload(cfg)
+    x, labels, _ = w.history_chunk(0, 0)
+    rng = np.random.default_rng(5)
+    sel = rng.choice(x.shape[0], cfg.A, replace=False)
+    mu0 = x[sel]
+    multi = int((np.bincount(labels[sel], minlength=cfg.A) >= 2).sum())
+    log(f"random-row start: {multi} generating clusters hold two or more starting centers")
+    assert multi > 0
+    for iters in (1, 3):
+        _check(cfg, x, mu0, iters)
+
+
 def test_fit_tuned_perturbed_centers_with_empty_cluster():
     cfg = synth.small_config("C3", H=4, r=128, A=64, n_hist=2000, chunk=2000)
     w = synth.workload(cfg)
